@@ -1,0 +1,166 @@
+"""fp64 oracle of the MXFP8 format: E4M3 elements, one E8M0 scale per block
+of 32 consecutive elements along the contraction axis.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+MoK flash §02 folds MXFP8 quantisation into the dispatch, grouped GEMM and
+SwiGLU datapath; the page names the format only.  The element and scale
+encodings and the scale rule follow the OCP Microscaling Formats (MX) v1.0
+specification (a public standard):
+  * E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field
+    0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; the largest finite
+    magnitude is 1.75 * 2^8 = 448; there is no infinity.
+  * E8M0 scale: an unsigned biased exponent, value 2^(code-127); 255 is NaN.
+  * Block scale: shared_exp = floor(log2(max |v|)) - 8 (8 = the largest
+    E4M3 exponent), clamped to [-127, 127]; each element is v / 2^shared_exp
+    rounded to nearest-even E4M3, with magnitudes beyond 448 clamped to 448.
+    A block of zeros takes scale code 0 and zero elements.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8
+
+
+def e4m3_value(code):
+    """Decode one E4M3 code (0..255) to fp64 by the field definitions."""
+    code = int(code)
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (-6)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+def e4m3_table():
+    """fp64 values of all 256 codes (NaN at 0x7F and 0xFF)."""
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+_POS = None
+
+
+def _positive_codes():
+    """(values, codes) of the 127 finite non-negative codes, increasing."""
+    global _POS
+    if _POS is None:
+        codes = np.arange(0, 127, dtype=np.int64)          # 0x00 .. 0x7E
+        vals = np.array([e4m3_value(c) for c in codes])
+        assert np.all(np.diff(vals) > 0)
+        _POS = (vals, codes)
+    return _POS
+
+
+def e4m3_encode(v):
+    """Round fp64 values to E4M3 codes: nearest, ties to the even code
+    (the even mantissa), magnitudes above 448 clamped to 448."""
+    v = np.asarray(v, dtype=np.float64)
+    vals, codes = _positive_codes()
+    mag = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(vals, mag, side="left")           # vals[hi] >= mag
+    hi = np.clip(hi, 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo = mag - vals[lo]
+    d_hi = vals[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    pick_hi |= (hi == lo)
+    out = np.where(pick_hi, codes[hi], codes[lo])
+    neg = np.signbit(v) & (out != 0)
+    return (out | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def e8m0_value(code):
+    code = np.asarray(code, dtype=np.int64)
+    return np.where(code == 255, np.nan, np.ldexp(1.0, code - 127))
+
+
+def block_scale_code(amax):
+    """E8M0 code of the shared scale for blocks with the given max |v|."""
+    amax = np.asarray(amax, dtype=np.float64)
+    out = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    # floor(log2(amax)) exactly, from frexp: amax = m * 2^e with m in [0.5, 1)
+    _, e = np.frexp(amax[nz])
+    shared = (e - 1) - E4M3_EMAX
+    out[nz] = np.clip(shared, -127, 127) + 127
+    return out.astype(np.uint8)
+
+
+def quantize(v):
+    """Quantise along the last axis in blocks of 32.
+
+    Returns (codes uint8 [..., K], scales uint8 [..., K/32]).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % BLOCK:
+        raise ValueError("last axis must be a multiple of 32")
+    blocks = v.reshape(v.shape[:-1] + (K // BLOCK, BLOCK))
+    amax = np.max(np.abs(blocks), axis=-1)
+    sc = block_scale_code(amax)
+    scale = e8m0_value(sc)[..., None]
+    codes = e4m3_encode(blocks / scale)
+    return codes.reshape(v.shape), sc
+
+
+def dequantize(codes, scales):
+    """fp64 values of codes [..., K] with scales [..., K/32] (exact)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    K = codes.shape[-1]
+    table = e4m3_table()
+    vals = table[codes.astype(np.int64)]
+    sc = e8m0_value(np.asarray(scales)).repeat(BLOCK, axis=-1)
+    return (vals.reshape(codes.shape) * sc.reshape(codes.shape[:-1] + (K,)))
+
+
+def fake_quant(v):
+    """quantize then dequantize, in fp64."""
+    return dequantize(*quantize(v))
+
+
+def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
+    """The forward with the expert GEMMs in MXFP8.
+
+    MoK flash §02 folds quantisation into dispatch, the grouped GEMM and
+    SwiGLU.  Quantised here: each gathered token row along d (the dispatch),
+    W1/W3 along d and W2 along I (blocks along the contraction axis of each
+    GEMM), and H along I after SwiGLU.  Routing and the weighted combine stay
+    in high precision.  Every product of dequantised operands is exact in
+    fp64 before summation.
+    """
+    from . import moe as M
+    T = np.shape(x)[0]
+    E = np.shape(w1)[0]
+    if logits is None:
+        logits = M.router_logits(x, wr, None)
+    idx, gate = M.route(logits, k, score, renorm, bias)
+    counts, offsets, perm, inv, src = M.layout(idx, E)
+    xq = fake_quant(np.asarray(x, dtype=np.float64))   # per token along d
+    xp = xq[src]
+    I = np.shape(w1)[1]
+    d = np.shape(w1)[2]
+    R = perm.shape[0]
+    H = np.zeros((R, I))
+    Yp = np.zeros((R, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        w1q = fake_quant(w1[e])          # [I, d], blocks along d
+        w3q = fake_quant(w3[e])
+        w2q = fake_quant(w2[e])          # [d, I], blocks along I
+        A = xp[lo:hi] @ w1q.T
+        B = xp[lo:hi] @ w3q.T
+        h = M.silu(A) * B
+        H[lo:hi] = h
+        Yp[lo:hi] = fake_quant(h) @ w2q.T
+    y = M.combine(Yp, gate, inv, T, k)
+    return dict(logits=logits, topk_idx=idx, gate=gate, counts=counts,
+                offsets=offsets, perm=perm, inv=inv, src=src, H=H, Yp=Yp,
+                y=y)
