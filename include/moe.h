@@ -1,0 +1,232 @@
+/*
+ * moe.h -- C ABI of libmoe.so, one GPU's share of a fused Mixture-of-Experts
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the news page "Cursor's MoK achieves
+ * 2.37x performance boost on NVIDIA GB300 NVL72" (KuCoin news flash; cited
+ * below as "MoK flash" with its article section):
+ *   section 01 (the communication tax of MoE): route tokens, count how many
+ *     tokens each expert has, decide where each lands with one expert's rows
+ *     kept together for the grouped GEMM, wait until data is complete, send
+ *     results back to each token's original position (dispatch / combine);
+ *     training adds the two exchanges in the reverse direction.
+ *   section 02 (how to compute while sending tokens): pull dispatch (the
+ *     receiver reads each token given only where it lives), push combine,
+ *     pull reverse-combine and push reverse-dispatch in the backward; one
+ *     megakernel whose communication side tells the compute side through
+ *     GPU-local counters when a batch of tokens is complete; the batch size
+ *     handed to the experts as a tunable; GPU-resident control with no CPU
+ *     step per round; MXFP8 quantisation folded into the dispatch, grouped
+ *     GEMM and SwiGLU datapath.
+ *   section 03: the measured unit is the whole layer -- schedule, dispatch,
+ *     expert FFN, combine and the final weighted merge.
+ * On one GPU the source of every token is local, so dispatch is an on-device
+ * row gather and combine a weighted row merge.
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers to caller-owned, contiguous,
+ *     row-major buffers; struct arguments (moe_desc, moe_weights, moe_saved)
+ *     are HOST pointers read during the call only.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising.  No call reads device data
+ *     back to the host, allocates device memory, or keeps state between calls.
+ *   - Host-side validation failures return a negative moe_status and enqueue
+ *     nothing.  A failed launch returns MOE_ERR_HIP.  Failures found on the
+ *     device (an expert index out of range, a wait that exceeded its bound)
+ *     are written to the optional device status word (moe_saved.status, an
+ *     int32 the caller zeroes); outputs are then undefined.
+ *   - Calls sharing one workspace must not overlap in time.
+ *
+ * Shapes: T tokens, d hidden size, E experts on this GPU, k experts per token,
+ * I expert intermediate size, R = T*k routed rows.  An assignment is numbered
+ * a = t*k + j (token t, slot j).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef MOE_API
+#define MOE_API __attribute__((visibility("default")))
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad shape, k > E, ...           */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid but not implemented (e.g. d % 64 != 0) */
+  MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required    */
+  MOE_ERR_HIP = -4,           /* a HIP launch failed                           */
+  MOE_ERR_TIMEOUT = -5,       /* device: a bounded wait expired                */
+  MOE_ERR_INVALID_ROUTE = -6  /* device: an expert index outside [0, E)        */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,    /* IEEE binary32                                           */
+  MOE_BF16 = 1,   /* bfloat16                                                */
+  MOE_MXFP8 = 2   /* OCP MX: E4M3 codes (uint8) + one E8M0 scale (uint8) per
+                     32 consecutive elements along the contraction axis      */
+} moe_dtype;
+
+typedef enum moe_score {
+  MOE_SCORE_SOFTMAX = 0,
+  MOE_SCORE_SIGMOID = 1
+} moe_score;
+
+/* Layer description.  Read on the host during each call. */
+typedef struct moe_desc {
+  int32_t T, d, E, k, I;
+  int32_t act_dtype;     /* MOE_F32 or MOE_BF16: X, Wr, Y, dY, dX          */
+  int32_t expert_dtype;  /* MOE_F32 (needs act F32), MOE_BF16 or MOE_MXFP8 */
+  int32_t score;         /* moe_score                                       */
+  int32_t renorm;        /* 1: gates renormalised over the chosen k          */
+  int32_t fused;         /* 1: one persistent launch driven by device-side
+                            ready counters; 0: one launch per step          */
+  int32_t stage_rows;    /* rows per ready counter (the minibatch handed to
+                            the expert GEMM): 0 = auto, else 128 or 256     */
+  int32_t n_workgroups;  /* persistent grid size, 0 = auto (all CUs)       */
+  uint32_t flags;        /* MOE_FLAG_* below                                */
+} moe_desc;
+
+/* Flags. */
+#define MOE_FLAG_DIRECT_PULL 0x1u  /* fused bf16 forward: the up-projection
+                                      reads token rows from X through the
+                                      layout instead of a staged copy       */
+#define MOE_FLAG_SPIN_LIMIT_TINY 0x100u /* test only: bounded waits give up
+                                      after a few polls (exercises the
+                                      MOE_ERR_TIMEOUT path)                 */
+
+/* Expert weights, in output-major order (row n of a matrix is output
+ * feature n, contiguous along the contraction axis):
+ *   w1, w3: [E, I, d]   gate and up projections
+ *   w2    : [E, d, I]   down projection
+ * Element type desc->expert_dtype.  For MOE_MXFP8 the arrays hold E4M3 codes
+ * and the *_scale arrays hold E8M0 codes: w1_scale/w3_scale [E, I, d/32],
+ * w2_scale [E, d, I/32]; NULL otherwise. */
+typedef struct moe_weights {
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const uint8_t* w1_scale;
+  const uint8_t* w3_scale;
+  const uint8_t* w2_scale;
+} moe_weights;
+
+/* Optional device buffers.  moe_forward writes each non-NULL one;
+ * moe_backward reads topk_idx, gate, offsets, perm, inv, a, b and h
+ * (all required there).
+ *   logits   float [T, E]   router logits (bias not included)
+ *   topk_idx int32 [T, k]   chosen experts, largest logit first
+ *   gate     float [T, k]   gates of the chosen experts
+ *   counts   int32 [E]      rows per expert
+ *   offsets  int32 [E+1]    exclusive prefix sum of counts
+ *   perm     int32 [R]      perm[r] = assignment on row r (rows grouped by
+ *                           expert, increasing assignment inside a group)
+ *   inv      int32 [R]      inv[a]  = row of assignment a
+ *   a, b     act   [R, I]   pre-activations x W1^T and x W3^T (bf16 only)
+ *   h        act   [R, I]   silu(a) * b
+ *   status   int32 [1]      device status word (see conventions)       */
+typedef struct moe_saved {
+  float* logits;
+  int32_t* topk_idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  void* a;
+  void* b;
+  void* h;
+  int32_t* status;
+} moe_saved;
+
+/* Bytes of workspace the calls below need for `desc` (covers moe_forward,
+ * moe_backward, moe_layout and moe_gather).  Returns MOE_ERR_INVALID_ARG for
+ * an invalid descriptor.  Host only. */
+MOE_API int moe_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* Router top-k and gates (MoK flash §01: the router re-decides every step
+ * which experts each token goes to; the score function and normalisation
+ * follow desc->score / desc->renorm).
+ *   logits   float [T, E]  input
+ *   bias     float [E] or NULL, added to the logits (in fp32) before both
+ *            selection and gates
+ *   topk_idx int32 [T, k]  output: the k largest biased logits, largest
+ *            first, exact ties to the lower expert index
+ *   gate     float [T, k]  output
+ * No workspace.  Needs 1 <= k <= min(E, 16), E <= 1024. */
+MOE_API int moe_route(const moe_desc* desc, const float* logits, const float* bias,
+              int32_t* topk_idx, float* gate, void* stream);
+
+/* Per-expert counting and layout (MoK flash §01: count each expert's tokens
+ * first, then place them so one expert's rows are contiguous).
+ *   topk_idx int32 [T, k]  input, distinct experts per token
+ *   counts   int32 [E], offsets int32 [E+1], perm int32 [R], inv int32 [R]:
+ *            outputs as in moe_saved (a stable counting sort by expert)
+ * An index outside [0, E) sets MOE_ERR_INVALID_ROUTE in `status` (may be
+ * NULL) and leaves the outputs undefined. */
+MOE_API int moe_layout(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts,
+               int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pull dispatch as a row gather (MoK flash §02: the receiver pulls each
+ * token given only its source position and lays rows out itself).
+ *   x   act [T, d] input;  perm int32 [R] from moe_layout;
+ *   xp  act [R, d] output, xp[r] = x[perm[r] / k].
+ * For desc->expert_dtype == MOE_MXFP8 the gather also quantises (MoK flash
+ * §02, quantisation folded into the dispatch): xp receives E4M3 codes
+ * uint8 [R, d] and xp_scale E8M0 codes uint8 [R, d/32]; else xp_scale is
+ * ignored. */
+MOE_API int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm,
+               void* xp, uint8_t* xp_scale, void* stream);
+
+/* MXFP8 quantisation of a [rows, K] bf16 matrix along K in blocks of 32
+ * (the standalone quantise step that the fused path folds away; also used
+ * to prepare MXFP8 weights).  codes uint8 [rows, K], scales uint8
+ * [rows, K/32].  K % 32 == 0. */
+MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K,
+                       uint8_t* codes, uint8_t* scales, void* stream);
+
+/* The whole forward layer (MoK flash §03: schedule, dispatch, expert FFN,
+ * combine and the final weighted merge).
+ *   x     act [T, d];  wr act [E, d] (row e scores expert e);
+ *   bias  float [E] or NULL (added to the logits);
+ *   w     expert weights (see moe_weights);
+ *   y     act [T, d] output: y[t] = sum_j gate[t,j] * FFN_{idx[t,j]}(x[t]),
+ *         FFN_e(v) = (silu(v W1_e^T) * (v W3_e^T)) W2_e^T;
+ *   saved optional outputs (may be NULL).
+ * With desc->fused = 1 the layer is one persistent launch (after a small
+ * clearing launch): routing, counting, layout, gather, the two grouped
+ * GEMMs and the combine are tasks taken from a device-side queue in
+ * dependency order; a GEMM tile starts as soon as the ready counter of its
+ * rows shows them staged (MoK flash §02). */
+MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
+                const float* bias, const moe_weights* w, void* y,
+                const moe_saved* saved, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Backward of the expert path with the routing frozen (MoK flash §01/§02:
+ * pull reverse-combine, expert dgrad and wgrad, push reverse-dispatch).
+ * bf16 only.
+ *   dy    act [T, d] upstream gradient;  x act [T, d] the forward input;
+ *   saved the forward's topk_idx, gate, offsets, perm, inv, a, b, h;
+ *   dx    act [T, d] output, gradient through the experts only;
+ *   dw1, dw3 act [E, I, d], dw2 act [E, d, I] outputs (overwritten; zero
+ *         for experts without rows);
+ *   dgate float [T, k] output, dL/dgate. */
+MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
+                 const moe_weights* w, const moe_saved* saved, void* dx,
+                 void* dw1, void* dw3, void* dw2, float* dgate,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+MOE_API const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

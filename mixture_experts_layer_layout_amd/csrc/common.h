@@ -1,0 +1,129 @@
+// common.h -- shared device helpers for the gfx950 MoE kernels: element
+// conversions, MFMA wrappers, bounded device-side waits and signals.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bits
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;  // every kernel runs 4 waves of 64
+
+// ---------------------------------------------------------------- numbers
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+
+// float -> bfloat16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// ---------------------------------------------------------------- MFMA
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).  Each lane supplies 8
+// consecutive-k values of one A row and of one B column; lanes 0-31 and
+// 32-63 cover the two halves of k.  Output register r of lane l holds
+// row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- waits
+// A bounded wait on a device counter.  Thread 0 of the workgroup polls with
+// agent-scope acquire loads; the whole workgroup then proceeds or, when the
+// bound expires or another workgroup has aborted, records MOE_ERR_TIMEOUT
+// and returns false.  `abort` is a workspace word every wait also watches,
+// so one expired wait drains the whole grid instead of hanging it.
+struct WaitCtx {
+  int* abort;
+  int32_t* status;
+  long long spin_limit;
+};
+
+__device__ __forceinline__ int load_acquire(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void set_status(int32_t* status, int code) {
+  if (status) atomicCAS((int*)status, 0, code);
+}
+
+// Returns true when *ctr >= target; false on timeout/abort.  Block-uniform.
+__device__ __forceinline__ bool wait_geq(const int* ctr, int target, const WaitCtx& w,
+                                         int* lds_flag) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    long long spins = 0;
+    while (load_acquire(ctr) < target) {
+      if (load_relaxed(w.abort)) { ok = 0; break; }
+      if (++spins > w.spin_limit) {
+        set_status(w.status, MOE_ERR_TIMEOUT);
+        __hip_atomic_store(w.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    *lds_flag = ok;
+  }
+  __syncthreads();
+  int ok = *lds_flag;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+  return ok != 0;
+}
+
+// Makes every prior global store of the workgroup visible at agent scope,
+// then adds `v` to *ctr.  Block-uniform call.
+__device__ __forceinline__ void signal_add(int* ctr, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- misc
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace moe

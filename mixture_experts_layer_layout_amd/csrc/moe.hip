@@ -1,0 +1,507 @@
+// moe.hip -- kernels and C-ABI entry points of libmoe.so (gfx950).
+//
+// The forward runs either as one persistent kernel (desc->fused = 1) whose
+// workgroups take tasks from a ticket queue in dependency order and wait on
+// the device counters of their inputs, or as one kernel per step on the
+// caller's stream.  Both call the same task functions (tasks_fwd.h,
+// tasks_bwd.h).  Tickets are handed out in increasing order and every task
+// waits only on tasks with lower tickets, which were claimed by workgroups
+// already running; so the queue drains whatever the grid size, and every
+// wait is additionally bounded (MOE_ERR_TIMEOUT) so a fault cannot hang it.
+#include <hip/hip_runtime.h>
+
+#include <string.h>
+#include <type_traits>
+
+#include "plan.h"
+#include "tasks_fwd.h"
+#include "tasks_bwd.h"
+#include "mxfp8.h"
+
+namespace moe {
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int make_plan(const moe_desc* D, Plan* p) {
+  if (!D || !p) return MOE_ERR_INVALID_ARG;
+  memset(p, 0, sizeof(*p));
+  const int T = D->T, d = D->d, E = D->E, k = D->k, I = D->I;
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || k > kMaxK || k > E) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * k > (int64_t)1 << 30) return MOE_ERR_INVALID_ARG;
+  if (D->score != MOE_SCORE_SOFTMAX && D->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  const bool f32 = D->act_dtype == MOE_F32;
+  if (f32) {
+    if (D->expert_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (d % 64 || I % 32) return MOE_ERR_UNSUPPORTED;
+  } else if (D->act_dtype == MOE_BF16) {
+    if (D->expert_dtype != MOE_BF16 && D->expert_dtype != MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+    if (d % 256 || I % 128) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (D->stage_rows != 0 && D->stage_rows != 128 && D->stage_rows != 256) return MOE_ERR_UNSUPPORTED;
+  p->T = T; p->d = d; p->E = E; p->k = k; p->I = I; p->R = T * k;
+  p->f32 = f32;
+  p->mxfp8 = D->expert_dtype == MOE_MXFP8;
+  p->act_es = f32 ? 4 : 2;
+  p->nb = cdiv(T, kTokBlock);
+  p->S = (!f32 && d % 1024 == 0 && d >= 2048) ? 4 : 1;
+  if (f32) {
+    p->BM = TileF32::BM;
+    p->nN1 = I / 32;
+    p->nN2 = d / 64;
+  } else {
+    p->BM = D->stage_rows ? D->stage_rows : 128;
+    p->nN1 = I / (TileB128::BN / 2);
+    p->nN2 = d / TileB128::BN;
+  }
+  p->nC = cdiv(T, kCombTok);
+  p->max_tiles = p->R / p->BM + (E < p->R ? E : p->R) + 1;
+  p->nNdh = I / 256;
+  p->nNdx = d / 256;
+  p->nPart = 2 * (p->nNdh > 0 ? p->nNdh : 1);
+
+  const size_t R = (size_t)p->R, es = p->act_es;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  p->n_ctr = C_HEADER + p->nb + 3 * (size_t)p->max_tiles + 2 * (size_t)E + 16;
+  p->o_ctr = take(p->n_ctr * 4);
+  p->o_lpart = take((size_t)p->S * T * E * 4);
+  p->o_topk = take(R * 4);
+  p->o_gate = take(R * 4);
+  p->o_bmask = take((size_t)p->nb * E * 8);
+  p->o_bcnt = take((size_t)p->nb * E * 4);
+  p->o_bbase = take((size_t)p->nb * E * 4);
+  p->o_counts = take((size_t)E * 4);
+  p->o_offsets = take((size_t)(E + 1) * 4);
+  p->o_tile_e = take((size_t)p->max_tiles * 4);
+  p->o_tile_r0 = take((size_t)p->max_tiles * 4);
+  p->o_tile_n = take((size_t)p->max_tiles * 4);
+  p->o_perm = take(R * 4);
+  p->o_inv = take(R * 4);
+  p->o_src = take(R * 4);
+  p->o_grow = take(R * 4);
+  p->o_h = take(R * I * es);
+  p->o_hs = take(R * (I / 32));
+  p->o_big1 = take(R * d * es);
+  p->o_big2 = take(R * d * es);
+  if (!f32) {
+    p->o_da = take(R * I * 2);
+    p->o_db = take(R * I * 2);
+    p->o_dgp = take((size_t)p->nPart * R * 4);
+  }
+  p->total = o;
+  return MOE_OK;
+}
+
+template <class T>
+static inline T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+static Sync make_sync(const Plan& p, void* ws, int32_t* status, uint32_t flags) {
+  int* c = at<int>(ws, p.o_ctr);
+  Sync s;
+  s.queue = c + C_QUEUE;
+  s.abort = c + C_ABORT;
+  s.r2_done = c + C_R2;
+  s.scan_done = c + C_SCAN;
+  s.g2_done = c + C_G2;
+  s.n_mtiles = c + C_NMT;
+  s.aux3 = c + C_AUX3;
+  int* q = c + C_HEADER;
+  s.r1_cnt = q; q += p.nb;
+  s.ready = q; q += p.max_tiles;
+  s.h_cnt = q; q += p.max_tiles;
+  s.aux0 = q; q += p.max_tiles;
+  s.aux1 = q; q += p.E;
+  s.aux2 = q; q += p.E;
+  s.status = status;
+  s.spin_limit = (flags & MOE_FLAG_SPIN_LIMIT_TINY) ? 64 : (1ll << 22);
+  return s;
+}
+
+static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved* sv) {
+  Fwd F;
+  memset(&F, 0, sizeof(F));
+  F.T = p.T; F.d = p.d; F.E = p.E; F.k = p.k; F.I = p.I; F.R = p.R;
+  F.nb = p.nb; F.S = p.S; F.BM = p.BM; F.nN1 = p.nN1; F.nN2 = p.nN2; F.nC = p.nC;
+  F.max_tiles = p.max_tiles;
+  F.score = D->score; F.renorm = D->renorm ? 1 : 0;
+  F.direct = (D->flags & MOE_FLAG_DIRECT_PULL) && !p.f32 && !p.mxfp8 ? 1 : 0;
+  F.lpart = at<float>(ws, p.o_lpart);
+  F.logits = sv ? sv->logits : nullptr;
+  F.topk = (sv && sv->topk_idx) ? sv->topk_idx : at<int>(ws, p.o_topk);
+  F.gate = (sv && sv->gate) ? sv->gate : at<float>(ws, p.o_gate);
+  F.bmask = at<unsigned long long>(ws, p.o_bmask);
+  F.bcnt = at<int>(ws, p.o_bcnt);
+  F.bbase = at<int>(ws, p.o_bbase);
+  F.counts = (sv && sv->counts) ? sv->counts : at<int>(ws, p.o_counts);
+  F.offsets = (sv && sv->offsets) ? sv->offsets : at<int>(ws, p.o_offsets);
+  F.tile_e = at<int>(ws, p.o_tile_e);
+  F.tile_r0 = at<int>(ws, p.o_tile_r0);
+  F.tile_n = at<int>(ws, p.o_tile_n);
+  F.perm = (sv && sv->perm) ? sv->perm : at<int>(ws, p.o_perm);
+  F.inv = (sv && sv->inv) ? sv->inv : at<int>(ws, p.o_inv);
+  F.src = at<int>(ws, p.o_src);
+  F.grow = nullptr;
+  F.xp = at<char>(ws, p.o_big1);
+  F.a = sv ? sv->a : nullptr;
+  F.b = sv ? sv->b : nullptr;
+  F.h = (sv && sv->h) ? sv->h : at<char>(ws, p.o_h);
+  F.yp = at<char>(ws, p.o_big2);
+  F.s = make_sync(p, ws, sv ? sv->status : nullptr, D->flags);
+  return F;
+}
+
+// ------------------------------------------------------------------ kernels
+__global__ void k_zero(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Spreads consecutive logical tiles over one XCD: hardware dispatches
+// workgroup b to XCD b % 8, so logical tile ranges stay in one L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = n / 8, rem = n % 8, x = b % 8, s = b / 8;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + s;
+}
+
+template <class Act>
+__global__ void __launch_bounds__(256) k_router_partial(Fwd F) { router_partial<Act>(F, blockIdx.x); }
+
+template <bool MASKS>
+__global__ void __launch_bounds__(256) k_router_topk(Fwd F) {
+  __shared__ unsigned long long smask[kMaxE];
+  router_topk<MASKS>(F, blockIdx.x, smask);
+}
+
+__global__ void __launch_bounds__(256) k_build_masks(Fwd F) {
+  __shared__ unsigned long long smask[kMaxE];
+  build_masks(F, blockIdx.x, smask);
+}
+
+__global__ void __launch_bounds__(256) k_scan(Fwd F) {
+  __shared__ int sh[2 * kMaxE + 16];
+  layout_scan(F, sh);
+}
+
+template <class Act, bool COPY>
+__global__ void __launch_bounds__(256) k_gather(Fwd F) {
+  __shared__ int ssrc[256];
+  const int tile = blockIdx.x;
+  if (tile >= *F.s.n_mtiles) return;
+  gather_tile<Act, COPY>(F, tile, ssrc);
+}
+
+template <class Act, class TL>
+__device__ __forceinline__ void run_g1(const Fwd& F, int tile, int nt, char* smem) {
+  if constexpr (std::is_same<Act, float>::value)
+    g1_tile_f32(F, tile, nt, (float*)smem);
+  else
+    g1_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
+}
+template <class Act, class TL>
+__device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* smem) {
+  if constexpr (std::is_same<Act, float>::value)
+    g2_tile_f32(F, tile, nt, (float*)smem);
+  else
+    g2_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
+}
+
+template <class Act, class TL>
+__global__ void __launch_bounds__(256, 1) k_g1(Fwd F) {
+  extern __shared__ __align__(16) char smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = id / F.nN1, nt = id % F.nN1;
+  if (tile >= *F.s.n_mtiles) return;
+  run_g1<Act, TL>(F, tile, nt, smem);
+}
+
+template <class Act, class TL>
+__global__ void __launch_bounds__(256, 1) k_g2(Fwd F) {
+  extern __shared__ __align__(16) char smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = id / F.nN2, nt = id % F.nN2;
+  if (tile >= *F.s.n_mtiles) return;
+  run_g2<Act, TL>(F, tile, nt, smem);
+}
+
+template <class Act>
+__global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F, blockIdx.x); }
+
+// The persistent forward.
+template <class Act, class TL>
+__global__ void __launch_bounds__(256, 1) k_fused_fwd(Fwd F) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_t, s_flag;
+  const WaitCtx W = wctx(F.s);
+  const int n_r1 = F.nb * F.S;
+  for (;;) {
+    __syncthreads();
+    if (threadIdx.x == 0) s_t = atomicAdd(F.s.queue, 1);
+    __syncthreads();
+    int t = s_t;
+    if (t < n_r1) {
+      router_partial<Act>(F, t);
+      signal_add(&F.s.r1_cnt[t / F.S], 1);
+      continue;
+    }
+    t -= n_r1;
+    if (t < F.nb) {
+      if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, (unsigned long long*)smem);
+      signal_add(F.s.r2_done, 1);
+      continue;
+    }
+    t -= F.nb;
+    if (t == 0) {
+      if (wait_geq(F.s.r2_done, F.nb, W, &s_flag)) layout_scan(F, (int*)smem);
+      signal_add(F.s.scan_done, 1);
+      continue;
+    }
+    t -= 1;
+    if (!wait_geq(F.s.scan_done, 1, W, &s_flag)) break;
+    const int nmt = *(volatile int*)F.s.n_mtiles;
+    if (t < nmt) {
+      if (F.direct)
+        gather_tile<Act, false>(F, t, (int*)smem);
+      else
+        gather_tile<Act, true>(F, t, (int*)smem);
+      continue;
+    }
+    t -= nmt;
+    if (t < nmt * F.nN1) {
+      const int tile = t / F.nN1, nt = t % F.nN1;
+      if (wait_geq(&F.s.ready[tile], 1, W, &s_flag)) run_g1<Act, TL>(F, tile, nt, smem);
+      signal_add(&F.s.h_cnt[tile], 1);
+      continue;
+    }
+    t -= nmt * F.nN1;
+    if (t < nmt * F.nN2) {
+      const int tile = t / F.nN2, nt = t % F.nN2;
+      if (wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) run_g2<Act, TL>(F, tile, nt, smem);
+      signal_add(F.s.g2_done, 1);
+      continue;
+    }
+    t -= nmt * F.nN2;
+    if (t < F.nC) {
+      if (wait_geq(F.s.g2_done, nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
+      continue;
+    }
+    break;
+  }
+}
+
+// Standalone pull gather: xp[r] = x[perm[r] / k].
+template <class Act>
+__global__ void __launch_bounds__(256) k_gather_perm(const Act* __restrict__ x, const int* __restrict__ perm,
+                                                     Act* __restrict__ xp, int R, int d, int k) {
+  const int lane = threadIdx.x & 63;
+  const int nvec = d * (int)sizeof(Act) / 16;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4) {
+    const uint4* s = (const uint4*)x + (size_t)(perm[r] / k) * nvec;
+    uint4* dst = (uint4*)xp + (size_t)r * nvec;
+    for (int v = lane; v < nvec; v += 64) dst[v] = s[v];
+  }
+}
+
+// ------------------------------------------------------------------ host
+static int g_num_cus = 0;
+
+static int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_num_cus = n;
+  }
+  return g_num_cus;
+}
+
+template <class K>
+static bool set_smem(K kernel, size_t bytes) {
+  if (bytes <= 65536) return true;
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) ==
+         hipSuccess;
+}
+
+static int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <class Act, class TL>
+static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStream_t st) {
+  constexpr bool isf = std::is_same<Act, float>::value;
+  // the persistent kernel's LDS serves every task: GEMM stages, routing
+  // masks (kMaxE u64), the layout scan (2 kMaxE + 16 ints), gather rows
+  size_t smem = isf ? TileF32::smem_bytes : TL::smem_bytes;
+  const size_t other[3] = {kMaxE * 8, (2 * kMaxE + 16) * 4, 256 * 4};
+  for (size_t o : other) smem = smem > o ? smem : o;
+  const size_t gsmem = isf ? TileF32::smem_bytes : TL::smem_bytes;
+  hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, F.s.queue, (int)p.n_ctr);
+  if (p.T == 0) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
+    return launch_status();
+  }
+  if (D->fused) {
+    if (!set_smem(k_fused_fwd<Act, TL>, smem)) return MOE_ERR_HIP;
+    const int n_wg = D->n_workgroups > 0 ? D->n_workgroups : num_cus();
+    if (n_wg <= 0) return MOE_ERR_HIP;
+    hipLaunchKernelGGL((k_fused_fwd<Act, TL>), dim3(n_wg), dim3(256), smem, st, F);
+    return launch_status();
+  }
+  hipLaunchKernelGGL(k_router_partial<Act>, dim3(p.nb * p.S), dim3(256), 0, st, F);
+  hipLaunchKernelGGL(k_router_topk<true>, dim3(p.nb), dim3(256), 0, st, F);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
+  if (F.direct)
+    hipLaunchKernelGGL((k_gather<Act, false>), dim3(p.max_tiles), dim3(256), 0, st, F);
+  else
+    hipLaunchKernelGGL((k_gather<Act, true>), dim3(p.max_tiles), dim3(256), 0, st, F);
+  if (!set_smem(k_g1<Act, TL>, gsmem) || !set_smem(k_g2<Act, TL>, gsmem)) return MOE_ERR_HIP;
+  hipLaunchKernelGGL((k_g1<Act, TL>), dim3(p.max_tiles * p.nN1), dim3(256), gsmem, st, F);
+  hipLaunchKernelGGL((k_g2<Act, TL>), dim3(p.max_tiles * p.nN2), dim3(256), gsmem, st, F);
+  hipLaunchKernelGGL(k_combine<Act>, dim3(p.nC), dim3(256), 0, st, F);
+  return launch_status();
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_workspace_size(const moe_desc* desc, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  *bytes = p.total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_desc* desc, const float* logits, const float* bias, int32_t* topk_idx, float* gate,
+              void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.T > 0 && (!logits || !topk_idx || !gate)) return MOE_ERR_INVALID_ARG;
+  if (p.T == 0) return MOE_OK;
+  Fwd F;
+  memset(&F, 0, sizeof(F));
+  F.T = p.T; F.E = p.E; F.k = p.k; F.S = 1;
+  F.score = desc->score; F.renorm = desc->renorm ? 1 : 0;
+  F.lpart = (float*)logits;
+  F.bias = bias;
+  F.topk = topk_idx;
+  F.gate = gate;
+  hipLaunchKernelGGL(k_router_topk<false>, dim3(p.nb), dim3(256), 0, (hipStream_t)stream, F);
+  return launch_status();
+}
+
+int moe_layout(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+               int32_t* inv, int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (!counts || !offsets || (p.R > 0 && (!topk_idx || !perm || !inv))) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  moe_saved sv;
+  memset(&sv, 0, sizeof(sv));
+  sv.topk_idx = (int32_t*)topk_idx;
+  sv.counts = counts;
+  sv.offsets = offsets;
+  sv.perm = perm;
+  sv.inv = inv;
+  sv.status = status;
+  Fwd F = make_fwd(p, desc, workspace, &sv);
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, F.s.queue, (int)p.n_ctr);
+  if (p.nb > 0) hipLaunchKernelGGL(k_build_masks, dim3(p.nb), dim3(256), 0, st, F);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
+  if (p.R > 0) {
+    if (p.f32)
+      hipLaunchKernelGGL((k_gather<float, false>), dim3(p.max_tiles), dim3(256), 0, st, F);
+    else
+      hipLaunchKernelGGL((k_gather<bf16_t, false>), dim3(p.max_tiles), dim3(256), 0, st, F);
+  }
+  return launch_status();
+}
+
+int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm, void* xp, uint8_t* xp_scale,
+               void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.R == 0) return MOE_OK;
+  if (!x || !perm || !xp) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const int grid = cdiv(p.R, 4) < 4096 ? cdiv(p.R, 4) : 4096;
+  if (p.mxfp8) {
+    if (!xp_scale) return MOE_ERR_INVALID_ARG;
+    return mxfp8_gather_perm((const bf16_t*)x, perm, (uint8_t*)xp, xp_scale, p.R, p.d, p.k, st);
+  }
+  if (p.f32)
+    hipLaunchKernelGGL(k_gather_perm<float>, dim3(grid), dim3(256), 0, st, (const float*)x, perm, (float*)xp, p.R,
+                       p.d, p.k);
+  else
+    hipLaunchKernelGGL(k_gather_perm<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)x, perm, (bf16_t*)xp,
+                       p.R, p.d, p.k);
+  return launch_status();
+}
+
+int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  return mxfp8_quantize_rows((const bf16_t*)src, rows, K, codes, scales, (hipStream_t)stream);
+}
+
+int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float* bias, const moe_weights* w,
+                void* y, const moe_saved* saved, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (!w || (p.T > 0 && (!x || !wr || !y || !w->w1 || !w->w3 || !w->w2))) return MOE_ERR_INVALID_ARG;
+  if (p.mxfp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  if (p.f32 && saved && (saved->a || saved->b)) {
+    // fp32 layer: a/b are written as fp32 (act dtype)
+  }
+  Fwd F = make_fwd(p, desc, workspace, saved);
+  F.x = x; F.wr = wr; F.bias = bias; F.w1 = w->w1; F.w3 = w->w3; F.w2 = w->w2; F.y = y;
+  hipStream_t st = (hipStream_t)stream;
+  if (p.mxfp8) return mxfp8_forward(p, desc, F, w, st);
+  if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st);
+  if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st);
+  return forward_impl<bf16_t, TileB128>(p, desc, F, st);
+}
+
+int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_weights* w, const moe_saved* saved,
+                 void* dx, void* dw1, void* dw3, void* dw2, float* dgate, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.f32 || p.mxfp8) return MOE_ERR_UNSUPPORTED;
+  if (!w || !saved) return MOE_ERR_INVALID_ARG;
+  if (!saved->offsets || !saved->gate) return MOE_ERR_INVALID_ARG;
+  if (p.T > 0 && (!dy || !x || !dx || !dw1 || !dw3 || !dw2 || !dgate || !w->w1 || !w->w3 || !w->w2 ||
+                  !saved->topk_idx || !saved->perm || !saved->inv || !saved->a || !saved->b || !saved->h))
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  return backward_impl(p, desc, dy, x, w, saved, dx, dw1, dw3, dw2, dgate, workspace, (hipStream_t)stream);
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or type combination not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_TIMEOUT: return "MOE_ERR_TIMEOUT: a device-side wait exceeded its bound";
+    case MOE_ERR_INVALID_ROUTE: return "MOE_ERR_INVALID_ROUTE: expert index out of range or repeated";
+    default: return "unknown moe_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// plan.h -- host-side validation of a layer description and the carving of
+// one caller-owned workspace into the buffers the kernels use.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+struct Plan {
+  int T, d, E, k, I, R;
+  int nb;          // token blocks of 64
+  int S;           // router k-slices
+  int BM;          // rows per row tile (= rows per ready counter)
+  int nN1, nN2;    // column tiles of the up / down projection
+  int nC;          // combine tasks
+  int max_tiles;   // upper bound on row tiles: R/BM + min(E, R)
+  int act_es;      // bytes per activation element
+  bool f32, mxfp8;
+  // backward
+  int nNdh;        // column tiles of the dH GEMM (over I)
+  int nNdx;        // column tiles of the dX GEMM (over d)
+  int nPart;       // dgate partial sums per row
+  // workspace carving (byte offsets)
+  size_t o_ctr, n_ctr;
+  size_t o_lpart, o_topk, o_gate, o_bmask, o_bcnt, o_bbase, o_counts, o_offsets;
+  size_t o_tile_e, o_tile_r0, o_tile_n, o_perm, o_inv, o_src, o_grow;
+  size_t o_h, o_big1, o_big2, o_da, o_db, o_dgp, o_hs;
+  size_t total;
+};
+
+// Counter region, in ints.
+enum CtrSlot {
+  C_QUEUE = 0, C_ABORT, C_R2, C_SCAN, C_G2, C_NMT, C_AUX3, C_HEADER = 16
+};
+
+int make_plan(const moe_desc* d, Plan* p);
+
+}  // namespace moe

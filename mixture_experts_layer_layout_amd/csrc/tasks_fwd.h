@@ -1,0 +1,540 @@
+// tasks_fwd.h -- the forward layer as tasks.  Each task is one workgroup's
+// unit of work; the same functions run as separate kernels (one task per
+// workgroup, the stream orders the steps) or inside the persistent kernel
+// (tasks taken from a device-side ticket queue in dependency order, each
+// waiting on the device counters its inputs raise).
+//
+// Steps (MoK flash = the page "Cursor's MoK achieves 2.37x performance boost
+// on NVIDIA GB300 NVL72", by article section):
+//   router_partial  router GEMM, one k-slice of 64 tokens x E experts
+//   router_topk     sum of slices, top-k, gates, per-block expert bitmasks
+//                   (§01: the router re-decides each token's experts)
+//   layout_scan     per-expert counts, offsets, per-(block, expert) bases and
+//                   the list of row tiles (§01: count first, then place, one
+//                   expert's rows contiguous)
+//   gather          each row tile derives its own source tokens from the
+//                   masks and pulls the rows into expert order, then raises
+//                   its ready counter (§02: pull dispatch; the communication
+//                   side tells the compute side through GPU-local counters)
+//   g1              up projection + SwiGLU for one (row tile, column tile)
+//   g2              down projection for one (row tile, column tile)
+//   combine         weighted merge back into token order (§01, §03)
+#pragma once
+
+#include "common.h"
+#include "gemm_bf16.h"
+#include "gemm_f32.h"
+
+namespace moe {
+
+constexpr int kTokBlock = 64;  // tokens per routing block (one mask bit each)
+constexpr int kCombTok = 8;    // tokens per combine task
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+
+typedef Tile<128, 256> TileB128;
+typedef Tile<256, 256> TileB256;
+
+struct Sync {
+  int* queue;
+  int* abort;
+  int* r2_done;
+  int* scan_done;
+  int* g2_done;
+  int* n_mtiles;
+  int* r1_cnt;   // [nb]
+  int* ready;    // [max_tiles]
+  int* h_cnt;    // [max_tiles]
+  int* aux0;     // backward: [max_tiles]
+  int* aux1;     // backward: [E]
+  int* aux2;     // backward: [E]
+  int* aux3;     // backward: scalar
+  int32_t* status;
+  long long spin_limit;
+};
+
+struct Fwd {
+  int T, d, E, k, I, R, nb, S, BM, nN1, nN2, nC, max_tiles;
+  int score, renorm, direct;
+  const void* x;
+  const void* wr;
+  const float* bias;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  void* y;
+  float* lpart;      // [S, T, E]
+  float* logits;     // [T, E] or null
+  int* topk;         // [T, k]
+  float* gate;       // [T, k]
+  unsigned long long* bmask;  // [nb, E]
+  int* bcnt;         // [nb, E]
+  int* bbase;        // [nb, E]
+  int* counts;       // [E]
+  int* offsets;      // [E+1]
+  int* tile_e;       // [max_tiles]
+  int* tile_r0;
+  int* tile_n;
+  int* perm;         // [R]
+  int* inv;          // [R]
+  int* src;          // [R]
+  float* grow;       // [R] gate of each row, or null
+  void* xp;          // [R, d]
+  void* a;           // [R, I] or null
+  void* b;           // [R, I] or null
+  void* h;           // [R, I]
+  void* yp;          // [R, d]
+  Sync s;
+};
+
+__device__ __forceinline__ WaitCtx wctx(const Sync& s) { return WaitCtx{s.abort, s.status, s.spin_limit}; }
+
+// ---------------------------------------------------------------- router
+// logits slice s of token block b: lpart[s][t][e] = sum over k in slice s.
+template <class Act>
+__device__ void router_partial(const Fwd& F, int task);
+
+template <>
+__device__ void router_partial<bf16_t>(const Fwd& F, int task) {
+  const int b = task / F.S, s = task % F.S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int dk = F.d / F.S, k0 = s * dk;
+  const int nEB = cdiv(F.E, 32);
+  const bf16_t* X = (const bf16_t*)F.x;
+  const bf16_t* Wr = (const bf16_t*)F.wr;
+  const int koff = (lane >> 5) * 8;
+  for (int it = wave; it < 2 * nEB; it += 4) {
+    const int rb = it & 1, eb = it >> 1;
+    const int row = b * kTokBlock + rb * 32 + (lane & 31);
+    const int e = eb * 32 + (lane & 31);
+    const bool rv = row < F.T, ev = e < F.E;
+    const bf16_t* xa = X + (size_t)(rv ? row : 0) * F.d + k0 + koff;
+    const bf16_t* wb = Wr + (size_t)(ev ? e : 0) * F.d + k0 + koff;
+    f32x16_t acc;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int kk = 0; kk < dk; kk += 64) {
+      bf16x8_t av[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint4 ta = rv ? *(const uint4*)(xa + kk + 16 * u) : make_uint4(0, 0, 0, 0);
+        uint4 tb = ev ? *(const uint4*)(wb + kk + 16 * u) : make_uint4(0, 0, 0, 0);
+        av[u] = *(bf16x8_t*)&ta;
+        bv[u] = *(bf16x8_t*)&tb;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc = mfma32x32x16(av[u], bv[u], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int orow = b * kTokBlock + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (orow < F.T && ev) F.lpart[((size_t)s * F.T + orow) * F.E + e] = acc[r];
+    }
+  }
+}
+
+template <>
+__device__ void router_partial<float>(const Fwd& F, int task) {
+  const int b = task / F.S, s = task % F.S;
+  const int dk = F.d / F.S, k0 = s * dk;
+  const float* X = (const float*)F.x;
+  const float* Wr = (const float*)F.wr;
+  for (int p = threadIdx.x; p < kTokBlock * F.E; p += kThreads) {
+    const int row = b * kTokBlock + p / F.E, e = p % F.E;
+    if (row >= F.T) continue;
+    float acc = 0.0f;
+    for (int kk = 0; kk < dk; ++kk) acc = fmaf(X[(size_t)row * F.d + k0 + kk], Wr[(size_t)e * F.d + k0 + kk], acc);
+    F.lpart[((size_t)s * F.T + row) * F.E + e] = acc;
+  }
+}
+
+// Top-k of one token, one wave.  vals[q] holds expert lane + 64 q.
+// Largest value first; equal values go to the lower expert index.
+__device__ __forceinline__ void wave_topk_gates(const float* vals, int QN, int E, int k, int score,
+                                                int renorm, int& sel_e, float& sel_g) {
+  const int lane = threadIdx.x & 63;
+  uint32_t taken = 0;
+  float sv = -INFINITY;
+  sel_e = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < kMaxE / 64; ++q) {
+      const int e = lane + 64 * q;
+      if (q < QN && e < E && !((taken >> q) & 1u)) {
+        const float v = vals[q];
+        if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) { sel_e = bi; sv = bv; }
+  }
+  const bool mine = lane < k;
+  float g;
+  if (score == MOE_SCORE_SOFTMAX) {
+    const float m = __shfl(sv, 0);  // the largest logit
+    if (renorm) {
+      const float ex = mine ? expf(sv - m) : 0.0f;
+      g = ex / wave_sum(ex);
+    } else {
+      float part = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxE / 64; ++q)
+        if (q < QN && lane + 64 * q < E) part += expf(vals[q] - m);
+      g = (mine ? expf(sv - m) : 0.0f) / wave_sum(part);
+    }
+  } else {
+    const float sg = mine ? 1.0f / (1.0f + expf(-sv)) : 0.0f;
+    g = renorm ? sg / wave_sum(sg) : sg;
+  }
+  sel_g = g;
+}
+
+// Sums the slices, adds the bias, selects, writes idx/gates and the block's
+// expert bitmasks.  With S == 1 and lpart == the caller's logits this is
+// also the standalone route step.
+template <bool MASKS>
+__device__ void router_topk(const Fwd& F, int b, unsigned long long* smask) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (MASKS) {
+    for (int e = threadIdx.x; e < F.E; e += kThreads) smask[e] = 0ull;
+    __syncthreads();
+  }
+  const int QN = cdiv(F.E, 64);
+  for (int tt = wave; tt < kTokBlock; tt += 4) {
+    const int t = b * kTokBlock + tt;
+    if (t >= F.T) break;
+    float vals[kMaxE / 64];
+#pragma unroll
+    for (int q = 0; q < kMaxE / 64; ++q) {
+      const int e = lane + 64 * q;
+      float v = -INFINITY;
+      if (q < QN && e < F.E) {
+        v = 0.0f;
+        for (int s = 0; s < F.S; ++s) v += F.lpart[((size_t)s * F.T + t) * F.E + e];
+        if (F.logits) F.logits[(size_t)t * F.E + e] = v;
+        if (F.bias) v += F.bias[e];
+      }
+      vals[q] = v;
+    }
+    int se;
+    float sg;
+    wave_topk_gates(vals, QN, F.E, F.k, F.score, F.renorm, se, sg);
+    if (lane < F.k) {
+      F.topk[(size_t)t * F.k + lane] = se;
+      F.gate[(size_t)t * F.k + lane] = sg;
+      if (MASKS) atomicOr(&smask[se], 1ull << tt);
+    }
+  }
+  if (MASKS) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < F.E; e += kThreads) {
+      const unsigned long long m = smask[e];
+      F.bmask[(size_t)b * F.E + e] = m;
+      F.bcnt[(size_t)b * F.E + e] = __popcll(m);
+    }
+  }
+}
+
+// Expert bitmasks of one token block from given indices (the layout entry
+// point).  Out-of-range or repeated experts set MOE_ERR_INVALID_ROUTE.
+__device__ void build_masks(const Fwd& F, int b, unsigned long long* smask) {
+  for (int e = threadIdx.x; e < F.E; e += kThreads) smask[e] = 0ull;
+  __syncthreads();
+  for (int p = threadIdx.x; p < kTokBlock * F.k; p += kThreads) {
+    const int tt = p / F.k, t = b * kTokBlock + tt;
+    if (t >= F.T) continue;
+    const int e = F.topk[(size_t)t * F.k + p % F.k];
+    if (e < 0 || e >= F.E) {
+      set_status(F.s.status, MOE_ERR_INVALID_ROUTE);
+      continue;
+    }
+    const unsigned long long bit = 1ull << tt;
+    if (atomicOr(&smask[e], bit) & bit) set_status(F.s.status, MOE_ERR_INVALID_ROUTE);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < F.E; e += kThreads) {
+    const unsigned long long m = smask[e];
+    F.bmask[(size_t)b * F.E + e] = m;
+    F.bcnt[(size_t)b * F.E + e] = __popcll(m);
+  }
+}
+
+// ---------------------------------------------------------------- layout
+// Exclusive scan of n <= 1024 ints in LDS (in place), returns the total.
+__device__ int block_exclusive_scan(int* v, int n, int* tmp /* >= 8 ints */) {
+  const int per = cdiv(n, kThreads);
+  const int lo = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (lo + i < n) local += v[lo + i];
+  // inclusive scan of `local` across the block
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = local;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int wbase = 0, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) wbase += tmp[w];
+    total += tmp[w];
+  }
+  int run = wbase + x - local;
+  for (int i = 0; i < per; ++i)
+    if (lo + i < n) {
+      const int c = v[lo + i];
+      v[lo + i] = run;
+      run += c;
+    }
+  __syncthreads();
+  return total;
+}
+
+// One workgroup: counts, offsets, bases, tile list.
+__device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
+  int* scnt = sh;
+  int* stile = sh + kMaxE;
+  int* tmp = sh + 2 * kMaxE;
+  __syncthreads();
+  for (int e = threadIdx.x; e < F.E; e += kThreads) {
+    int tot = 0;
+    for (int b = 0; b < F.nb; ++b) tot += F.bcnt[(size_t)b * F.E + e];
+    scnt[e] = tot;
+    stile[e] = cdiv(tot, F.BM);
+    F.counts[e] = tot;
+  }
+  __syncthreads();
+  const int R = block_exclusive_scan(scnt, F.E, tmp);
+  const int ntiles = block_exclusive_scan(stile, F.E, tmp);
+  for (int e = threadIdx.x; e < F.E; e += kThreads) {
+    const int off = scnt[e];
+    F.offsets[e] = off;
+    int run = off;
+    for (int b = 0; b < F.nb; ++b) {
+      F.bbase[(size_t)b * F.E + e] = run;
+      run += F.bcnt[(size_t)b * F.E + e];
+    }
+    const int cnt = run - off;
+    for (int mt = 0, id = stile[e]; mt * F.BM < cnt; ++mt, ++id) {
+      F.tile_e[id] = e;
+      F.tile_r0[id] = off + mt * F.BM;
+      F.tile_n[id] = min(F.BM, cnt - mt * F.BM);
+    }
+  }
+  if (threadIdx.x == 0) {
+    F.offsets[F.E] = R;
+    *F.s.n_mtiles = ntiles;
+  }
+}
+
+// Position of the rank-th set bit (0-based) of m.
+__device__ __forceinline__ int select_bit(unsigned long long m, int rank) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const unsigned long long low = m & ((1ull << w) - 1ull);
+    const int c = __popcll(low);
+    if (rank >= c) {
+      rank -= c;
+      m >>= w;
+      pos += w;
+    } else {
+      m = low;
+    }
+  }
+  return pos;
+}
+
+// Source assignment of row r of expert e (rows in increasing assignment
+// order): the block whose base is the last one <= r, then the matching set
+// bit of that block's mask, then the slot of e among the token's experts.
+__device__ __forceinline__ int row_source(const Fwd& F, int e, int r) {
+  int lo = 0, hi = F.nb;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (F.bbase[(size_t)mid * F.E + e] <= r) lo = mid + 1; else hi = mid;
+  }
+  const int b = lo - 1;
+  const int rank = r - F.bbase[(size_t)b * F.E + e];
+  const int t = b * kTokBlock + select_bit(F.bmask[(size_t)b * F.E + e], rank);
+  int j = 0;
+  for (int jj = 0; jj < F.k; ++jj)
+    if (F.topk[(size_t)t * F.k + jj] == e) j = jj;
+  return t * F.k + j;
+}
+
+// Rows of one tile: writes perm, inv, src (and the per-row gate), then (if
+// COPY) pulls the token rows into expert order.  Raises ready[tile].
+template <class Act, bool COPY>
+__device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
+  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int r = r0 + i;
+    const int a = row_source(F, e, r);
+    const int t = a / F.k;
+    F.perm[r] = a;
+    F.inv[a] = r;
+    F.src[r] = t;
+    if (F.grow) F.grow[r] = F.gate[a];
+    ssrc[i] = t;
+  }
+  __syncthreads();
+  if (COPY) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nvec = F.d * (int)sizeof(Act) / 16;
+    const uint4* X = (const uint4*)F.x;
+    uint4* XP = (uint4*)F.xp;
+    for (int i = wave; i < n; i += 4) {
+      const uint4* s = X + (size_t)ssrc[i] * nvec;
+      uint4* dst = XP + (size_t)(r0 + i) * nvec;
+      for (int v = lane; v < nvec; v += 64) dst[v] = s[v];
+    }
+  }
+  signal_add(&F.s.ready[tile], 1);
+}
+
+// ---------------------------------------------------------------- GEMMs
+template <class TL>
+__device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
+  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const int d = F.d, I = F.I;
+  const bf16_t* W1 = (const bf16_t*)F.w1 + (size_t)e * I * d;
+  const bf16_t* W3 = (const bf16_t*)F.w3 + (size_t)e * I * d;
+  const int c0 = nt * (TL::BN / 2);
+  KRows<TL::BM> la;
+  KRows<TL::BN> lb;
+  if (F.direct) {
+    const bf16_t* X = (const bf16_t*)F.x;
+    la.init([&](int r) -> const bf16_t* { return r < n ? X + (size_t)F.src[r0 + r] * d : nullptr; });
+  } else {
+    const bf16_t* XP = (const bf16_t*)F.xp;
+    la.init([&](int r) -> const bf16_t* { return r < n ? XP + (size_t)(r0 + r) * d : nullptr; });
+  }
+  lb.init([&](int nr) -> const bf16_t* {
+    int which, col;
+    swiglu_brow<TL>(nr, which, col);
+    return (which ? W3 : W1) + (size_t)(c0 + col) * d;
+  });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(d / 64, smem, acc, [&](int kt) { la.load(kt); }, [&](int kt) { lb.load(kt); },
+                    [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  bf16_t* H = (bf16_t*)F.h;
+  bf16_t* A = (bf16_t*)F.a;
+  bf16_t* B = (bf16_t*)F.b;
+  tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float bv) {
+    if (row < n) {
+      const size_t o = (size_t)(r0 + row) * I + c0 + col;
+      H[o] = f32_to_bf16(silu_f(av) * bv);
+      if (A) A[o] = f32_to_bf16(av);
+      if (B) B[o] = f32_to_bf16(bv);
+    }
+  });
+}
+
+template <class TL>
+__device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
+  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const int d = F.d, I = F.I;
+  const bf16_t* W2 = (const bf16_t*)F.w2 + (size_t)e * d * I;
+  const bf16_t* H = (const bf16_t*)F.h;
+  const int c0 = nt * TL::BN;
+  KRows<TL::BM> la;
+  KRows<TL::BN> lb;
+  la.init([&](int r) -> const bf16_t* { return r < n ? H + (size_t)(r0 + r) * I : nullptr; });
+  lb.init([&](int nr) -> const bf16_t* { return W2 + (size_t)(c0 + nr) * I; });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(I / 64, smem, acc, [&](int kt) { la.load(kt); }, [&](int kt) { lb.load(kt); },
+                    [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  bf16_t* YP = (bf16_t*)F.yp;
+  tile_visit<TL>(acc, [&](int row, int col, float v) {
+    if (row < n) YP[(size_t)(r0 + row) * d + c0 + col] = f32_to_bf16(v);
+  });
+}
+
+__device__ void g1_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
+  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const int d = F.d, I = F.I;
+  const float* W1 = (const float*)F.w1 + (size_t)e * I * d;
+  const float* W3 = (const float*)F.w3 + (size_t)e * I * d;
+  const float* XP = (const float*)F.xp;
+  const int c0 = nt * 32;
+  float acc[2][4];
+  tile_f32(d, smem, acc,
+           [&](int r) -> const float* { return r < n ? XP + (size_t)(r0 + r) * d : nullptr; },
+           [&](int nr) -> const float* { return (nr < 32 ? W1 : W3) + (size_t)(c0 + (nr & 31)) * d; });
+  float* H = (float*)F.h;
+  float* A = (float*)F.a;
+  float* B = (float*)F.b;
+  tile_f32_visit_pairs(acc, [&](int row, int col, float av, float bv) {
+    if (row < n) {
+      const size_t o = (size_t)(r0 + row) * I + c0 + col;
+      H[o] = silu_f(av) * bv;
+      if (A) A[o] = av;
+      if (B) B[o] = bv;
+    }
+  });
+}
+
+__device__ void g2_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
+  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const int d = F.d, I = F.I;
+  const float* W2 = (const float*)F.w2 + (size_t)e * d * I;
+  const float* H = (const float*)F.h;
+  const int c0 = nt * 64;
+  float acc[2][4];
+  tile_f32(I, smem, acc,
+           [&](int r) -> const float* { return r < n ? H + (size_t)(r0 + r) * I : nullptr; },
+           [&](int nr) -> const float* { return W2 + (size_t)(c0 + nr) * I; });
+  float* YP = (float*)F.yp;
+  tile_f32_visit(acc, [&](int row, int col, float v) {
+    if (row < n) YP[(size_t)(r0 + row) * d + c0 + col] = v;
+  });
+}
+
+// ---------------------------------------------------------------- combine
+// y[t] = sum_j gate[t,j] * yp[inv[t*k+j]], fp32 accumulation in slot order.
+template <class Act>
+__device__ void combine_tokens(const Fwd& F, int cb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int EPV = 16 / sizeof(Act);  // elements per 16-byte vector
+  const int nvec = F.d / EPV;
+  for (int tt = wave; tt < kCombTok; tt += 4) {
+    const int t = cb * kCombTok + tt;
+    if (t >= F.T) break;
+    int rows[kMaxK];
+    float g[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      rows[j] = j < F.k ? F.inv[(size_t)t * F.k + j] : 0;
+      g[j] = j < F.k ? F.gate[(size_t)t * F.k + j] : 0.0f;
+    }
+    for (int v = lane; v < nvec; v += 64) {
+      float acc[EPV];
+#pragma unroll
+      for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= F.k) break;
+        const uint4 u = ((const uint4*)F.yp)[(size_t)rows[j] * nvec + v];
+        const Act* p = (const Act*)&u;
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) acc[q] = fmaf(g[j], Elem<Act>::to_f32(p[q]), acc[q]);
+      }
+      uint4 o;
+      Act* po = (Act*)&o;
+      for (int q = 0; q < EPV; ++q) po[q] = Elem<Act>::from_f32(acc[q]);
+      ((uint4*)F.y)[(size_t)t * nvec + v] = o;
+    }
+  }
+}
+
+}  // namespace moe
