@@ -186,13 +186,22 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", experts=True,
         w3 = torch.empty((w.E, w.I, w.d), dtype=wdt, device=dev)
         w2 = torch.empty((w.E, w.d, w.I), dtype=wdt, device=dev)
         for e in range(w.E):
-            w1[e] = _normal((w.I, w.d), w1_s, _gen(dev, seed, "w1", e), dev, wdt)
-            w3[e] = _normal((w.I, w.d), w1_s, _gen(dev, seed, "w3", e), dev, wdt)
-            w2[e] = _normal((w.d, w.I), w2_s, _gen(dev, seed, "w2", e), dev, wdt)
+            w1[e], w3[e], w2[e] = expert_weights(w, seed, e, dev)
         out["w1"], out["w3"], out["w2"] = w1, w3, w2
     if with_dy or (with_dy is None and w.backward):
         out["dy"] = _normal((w.T, w.d), 1.0, _gen(dev, seed, "dy"), dev, act)
     return out
+
+
+def expert_weights(w: Workload, seed: int, e: int, device="cpu"):
+    """(w1[e], w3[e], w2[e]) exactly as ``make_inputs`` draws them, for one
+    expert on its own."""
+    dev = torch.device(device)
+    wdt = torch.float32 if w.experts == "f32" else torch.bfloat16
+    _, _, w1_s, w2_s = w.scales()
+    return (_normal((w.I, w.d), w1_s, _gen(dev, seed, "w1", e), dev, wdt),
+            _normal((w.I, w.d), w1_s, _gen(dev, seed, "w3", e), dev, wdt),
+            _normal((w.d, w.I), w2_s, _gen(dev, seed, "w2", e), dev, wdt))
 
 
 def random_logits(T, E, seed, device="cpu", ties=False):

@@ -306,12 +306,16 @@ def token_output(x_t, experts, gates, w1, w3, w2):
     return y
 
 
-def expert_backward(x_rows, dy_rows, g_rows, w1_e, w3_e, w2_e):
+def expert_backward(x_rows, dy_rows, g_rows, w1_e, w3_e, w2_e, saved=None):
     """Backward of one expert over its rows (in segment order).
 
+    ``saved`` = (A, B, H) of this expert's forward, recomputed when None.
     Returns dW1_e, dW3_e, dW2_e, the per-row dXp and the per-row dgate.
     """
-    A, B, H, _ = expert_ffn(x_rows, w1_e, w3_e, w2_e)
+    if saved is None:
+        A, B, H, _ = expert_ffn(x_rows, w1_e, w3_e, w2_e)
+    else:
+        A, B, H = saved
     G = _f64(dy_rows)
     g = _f64(g_rows)
     dHu = G @ _f64(w2_e)
