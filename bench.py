@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix-core peak, TFLOP/s
 
-DEFAULT_WORKLOAD = "dsv3-bf16"
+DEFAULT_WORKLOAD = "dsv3-fwdbwd-zipf"
 METRIC = "MoE layer tokens/s fwd+bwd on 1 MI355X; grouped-GEMM MFMA util %; gather GB/s"
 
 

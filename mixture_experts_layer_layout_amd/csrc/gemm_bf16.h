@@ -74,21 +74,25 @@ struct KRows {
 //   kptr(k) -> pointer to the stored row holding absolute k at the tile's
 //              first row, or nullptr when k lies outside the operand
 //   kscale(k) -> factor applied to that stored row (1 for none)
+//   half_off  -> extra element offset for the second half of the tile's
+//                rows (two column ranges of one stored row, e.g. the dA and
+//                dB halves of [dA | dB]); 0 when the rows are contiguous
 template <int ROWS>
 struct KCols {
   static constexpr int NB = ROWS / 8;
   uint4 v[8];
   template <class P, class S>
-  __device__ __forceinline__ void load(int kt, P kptr, S kscale) {
+  __device__ __forceinline__ void load(int kt, P kptr, S kscale, int half_off = 0) {
     const int kb = threadIdx.x & 7, nb = threadIdx.x >> 3;
     if (nb >= NB) return;
+    const int coff = nb * 8 + (nb >= NB / 2 ? half_off : 0);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int k = kt * 64 + kb * 8 + kk;
       const bf16_t* p = kptr(k);
       uint4 x = make_uint4(0, 0, 0, 0);
       if (p) {
-        x = *(const uint4*)(p + nb * 8);
+        x = *(const uint4*)(p + coff);
         const float s = kscale(k);
         if (s != 1.0f) {
           uint32_t* w = (uint32_t*)&x;

@@ -57,10 +57,17 @@ int make_plan(const moe_desc* D, Plan* p) {
     p->nN2 = d / TileB128::BN;
   }
   p->nC = cdiv(T, kCombTok);
-  p->max_tiles = p->R / p->BM + (E < p->R ? E : p->R) + 1;
+  // row tiles of the forward (BM rows) and of the backward (TileDH::BM rows)
+  const int min_bm = p->BM < TileDH::BM ? p->BM : TileDH::BM;
+  p->max_tiles = p->R / min_bm + (E < p->R ? E : p->R) + 1;
+  p->bwd_ok = !f32 && !p->mxfp8 && d % 256 == 0 && I % 256 == 0;
   p->nNdh = I / 256;
   p->nNdx = d / 256;
-  p->nPart = 2 * (p->nNdh > 0 ? p->nNdh : 1);
+  p->nW2m = d / 128;
+  p->nW2n = I / 256;
+  p->nW13m = I / 64;
+  p->nW13n = d / 256;
+  p->nRP = cdiv(p->R, kRowPrep);
 
   const size_t R = (size_t)p->R, es = p->act_es;
   size_t o = 0;
@@ -82,14 +89,15 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_inv = take(R * 4);
   p->o_src = take(R * 4);
   p->o_grow = take(R * 4);
+  p->o_etile = take((size_t)(E + 1) * 4);
+  p->o_eorder = take((size_t)E * 4);
   p->o_h = take(R * I * es);
   p->o_hs = take(R * (I / 32));
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
-  if (!f32) {
-    p->o_da = take(R * I * 2);
-    p->o_db = take(R * I * 2);
-    p->o_dgp = take((size_t)p->nPart * R * 4);
+  if (p->bwd_ok) {
+    p->o_dab = take(R * 2 * I * 2);
+    p->o_dgp = take((size_t)p->nNdh * R * 4);
   }
   p->total = o;
   return MOE_OK;
@@ -170,8 +178,8 @@ __global__ void __launch_bounds__(256) k_router_partial(Fwd F) { router_partial<
 
 template <bool MASKS>
 __global__ void __launch_bounds__(256) k_router_topk(Fwd F) {
-  __shared__ unsigned long long smask[kMaxE];
-  router_topk<MASKS>(F, blockIdx.x, smask);
+  extern __shared__ __align__(16) char smem[];
+  router_topk<MASKS>(F, blockIdx.x, smem);
 }
 
 __global__ void __launch_bounds__(256) k_build_masks(Fwd F) {
@@ -247,7 +255,7 @@ __global__ void __launch_bounds__(256, 1) k_fused_fwd(Fwd F) {
     }
     t -= n_r1;
     if (t < F.nb) {
-      if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, (unsigned long long*)smem);
+      if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
       signal_add(F.s.r2_done, 1);
       continue;
     }
@@ -303,6 +311,103 @@ __global__ void __launch_bounds__(256) k_gather_perm(const Act* __restrict__ x, 
   }
 }
 
+// ------------------------------------------------------------------ backward
+__global__ void __launch_bounds__(256) k_bwd_setup(Bwd B) {
+  __shared__ int sh[2 * kMaxE + 16];
+  bwd_setup(B, sh);
+}
+
+__global__ void __launch_bounds__(256) k_bwd_rowprep(Bwd B) { bwd_rowprep(B, blockIdx.x); }
+
+__global__ void __launch_bounds__(256, 1) k_bwd_dh(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = id / B.nNdh, nt = id % B.nNdh;
+  if (tile >= *B.s.n_mtiles) return;
+  bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
+}
+
+__global__ void __launch_bounds__(256, 1) k_bwd_dxp(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = id / B.nNdx, nt = id % B.nNdx;
+  if (tile >= *B.s.n_mtiles) return;
+  bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
+}
+
+__global__ void __launch_bounds__(256, 1) k_bwd_dw2(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  bwd_dw2_tile(B, xcd_remap(blockIdx.x, gridDim.x), (bf16_t*)smem);
+}
+
+__global__ void __launch_bounds__(256, 1) k_bwd_dw13(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  bwd_dw13_tile(B, xcd_remap(blockIdx.x, gridDim.x), (bf16_t*)smem);
+}
+
+__global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockIdx.x); }
+
+// The persistent backward: the same tasks in ticket order.
+__global__ void __launch_bounds__(256, 1) k_fused_bwd(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_t, s_flag;
+  const WaitCtx W = wctx(B.s);
+  const int nper2 = B.nW2m * B.nW2n, nper13 = B.nW13m * B.nW13n;
+  const int nW2 = B.E * nper2, nW13 = B.E * nper13;
+  for (;;) {
+    __syncthreads();
+    if (threadIdx.x == 0) s_t = atomicAdd(B.s.queue, 1);
+    __syncthreads();
+    int t = s_t;
+    if (t == 0) {
+      bwd_setup(B, (int*)smem);
+      signal_add(B.s.scan_done, 1);
+      continue;
+    }
+    t -= 1;
+    if (t < B.nRP) {
+      bwd_rowprep(B, t);
+      signal_add(B.s.scan_done, 1);
+      continue;
+    }
+    t -= B.nRP;
+    if (!wait_geq(B.s.scan_done, 1 + B.nRP, W, &s_flag)) break;
+    const int nmt = *(volatile int*)B.s.n_mtiles;
+    if (t < nmt * B.nNdh) {
+      const int tile = t / B.nNdh, nt = t % B.nNdh;
+      bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
+      signal_add(&B.s.h_cnt[tile], 1);
+      signal_add(&B.s.aux1[B.tile_e[tile]], 1);
+      continue;
+    }
+    t -= nmt * B.nNdh;
+    if (t < nW2) {
+      bwd_dw2_tile(B, t, (bf16_t*)smem);
+      continue;
+    }
+    t -= nW2;
+    if (t < nmt * B.nNdx) {
+      const int tile = t / B.nNdx, nt = t % B.nNdx;
+      if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
+      signal_add(B.s.g2_done, 1);
+      continue;
+    }
+    t -= nmt * B.nNdx;
+    if (t < nW13) {
+      const int e = B.eorder[t / nper13];
+      const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
+      if (wait_geq(&B.s.aux1[e], need, W, &s_flag)) bwd_dw13_tile(B, t, (bf16_t*)smem);
+      continue;
+    }
+    t -= nW13;
+    if (t < B.nC) {
+      if (wait_geq(B.s.g2_done, nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
+      continue;
+    }
+    break;
+  }
+}
+
 // ------------------------------------------------------------------ host
 static int g_num_cus = 0;
 
@@ -334,7 +439,7 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   // the persistent kernel's LDS serves every task: GEMM stages, routing
   // masks (kMaxE u64), the layout scan (2 kMaxE + 16 ints), gather rows
   size_t smem = isf ? TileF32::smem_bytes : TL::smem_bytes;
-  const size_t other[3] = {kMaxE * 8, (2 * kMaxE + 16) * 4, 256 * 4};
+  const size_t other[3] = {kTopkSmem, (2 * kMaxE + 16) * 4, 256 * 4};
   for (size_t o : other) smem = smem > o ? smem : o;
   const size_t gsmem = isf ? TileF32::smem_bytes : TL::smem_bytes;
   hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, F.s.queue, (int)p.n_ctr);
@@ -350,7 +455,8 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
     return launch_status();
   }
   hipLaunchKernelGGL(k_router_partial<Act>, dim3(p.nb * p.S), dim3(256), 0, st, F);
-  hipLaunchKernelGGL(k_router_topk<true>, dim3(p.nb), dim3(256), 0, st, F);
+  if (!set_smem(k_router_topk<true>, kTopkSmem)) return MOE_ERR_HIP;
+  hipLaunchKernelGGL(k_router_topk<true>, dim3(p.nb), dim3(256), kTopkSmem, st, F);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
   if (F.direct)
     hipLaunchKernelGGL((k_gather<Act, false>), dim3(p.max_tiles), dim3(256), 0, st, F);
@@ -360,6 +466,47 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   hipLaunchKernelGGL((k_g1<Act, TL>), dim3(p.max_tiles * p.nN1), dim3(256), gsmem, st, F);
   hipLaunchKernelGGL((k_g2<Act, TL>), dim3(p.max_tiles * p.nN2), dim3(256), gsmem, st, F);
   hipLaunchKernelGGL(k_combine<Act>, dim3(p.nC), dim3(256), 0, st, F);
+  return launch_status();
+}
+
+static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const void* x, const moe_weights* w,
+                         const moe_saved* sv, void* dx, void* dw1, void* dw3, void* dw2, float* dgate, void* ws,
+                         hipStream_t st) {
+  Bwd B;
+  memset(&B, 0, sizeof(B));
+  B.T = p.T; B.d = p.d; B.E = p.E; B.k = p.k; B.I = p.I; B.R = p.R; B.BM = TileDH::BM;
+  B.nNdh = p.nNdh; B.nNdx = p.nNdx; B.nW2m = p.nW2m; B.nW2n = p.nW2n; B.nW13m = p.nW13m; B.nW13n = p.nW13n;
+  B.nRP = p.nRP; B.nC = p.nC;
+  B.dy = (const bf16_t*)dy; B.x = (const bf16_t*)x;
+  B.w1 = (const bf16_t*)w->w1; B.w3 = (const bf16_t*)w->w3; B.w2 = (const bf16_t*)w->w2;
+  B.gate = sv->gate; B.offsets = sv->offsets; B.perm = sv->perm; B.inv = sv->inv;
+  B.a = (const bf16_t*)sv->a; B.b = (const bf16_t*)sv->b; B.h = (const bf16_t*)sv->h;
+  B.dx = (bf16_t*)dx; B.dw1 = (bf16_t*)dw1; B.dw3 = (bf16_t*)dw3; B.dw2 = (bf16_t*)dw2; B.dgate = dgate;
+  B.tile_e = at<int>(ws, p.o_tile_e); B.tile_r0 = at<int>(ws, p.o_tile_r0); B.tile_n = at<int>(ws, p.o_tile_n);
+  B.etile = at<int>(ws, p.o_etile); B.eorder = at<int>(ws, p.o_eorder);
+  B.src = at<int>(ws, p.o_src); B.grow = at<float>(ws, p.o_grow);
+  B.dab = at<bf16_t>(ws, p.o_dab); B.dxp = at<bf16_t>(ws, p.o_big2); B.dgp = at<float>(ws, p.o_dgp);
+  B.s = make_sync(p, ws, sv->status, D->flags);
+  hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, B.s.queue, (int)p.n_ctr);
+  const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes;
+  if (D->fused) {
+    const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
+    if (!set_smem(k_fused_bwd, smem)) return MOE_ERR_HIP;
+    const int n_wg = D->n_workgroups > 0 ? D->n_workgroups : num_cus();
+    if (n_wg <= 0) return MOE_ERR_HIP;
+    hipLaunchKernelGGL(k_fused_bwd, dim3(n_wg), dim3(256), smem, st, B);
+    return launch_status();
+  }
+  if (!set_smem(k_bwd_dh, sm_dh) || !set_smem(k_bwd_dxp, sm_dh) || !set_smem(k_bwd_dw2, sm_dw) ||
+      !set_smem(k_bwd_dw13, sm_dw))
+    return MOE_ERR_HIP;
+  hipLaunchKernelGGL(k_bwd_setup, dim3(1), dim3(256), 0, st, B);
+  if (p.nRP > 0) hipLaunchKernelGGL(k_bwd_rowprep, dim3(p.nRP), dim3(256), 0, st, B);
+  if (p.R > 0) hipLaunchKernelGGL(k_bwd_dh, dim3(p.max_tiles * p.nNdh), dim3(256), sm_dh, st, B);
+  hipLaunchKernelGGL(k_bwd_dw2, dim3(p.E * p.nW2m * p.nW2n), dim3(256), sm_dw, st, B);
+  if (p.R > 0) hipLaunchKernelGGL(k_bwd_dxp, dim3(p.max_tiles * p.nNdx), dim3(256), sm_dh, st, B);
+  hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * p.nW13n), dim3(256), sm_dw, st, B);
+  if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
   return launch_status();
 }
 
@@ -393,7 +540,8 @@ int moe_route(const moe_desc* desc, const float* logits, const float* bias, int3
   F.bias = bias;
   F.topk = topk_idx;
   F.gate = gate;
-  hipLaunchKernelGGL(k_router_topk<false>, dim3(p.nb), dim3(256), 0, (hipStream_t)stream, F);
+  if (!set_smem(k_router_topk<false>, kTopkSmem)) return MOE_ERR_HIP;
+  hipLaunchKernelGGL(k_router_topk<false>, dim3(p.nb), dim3(256), kTopkSmem, (hipStream_t)stream, F);
   return launch_status();
 }
 
@@ -481,11 +629,11 @@ int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
-  if (p.f32 || p.mxfp8) return MOE_ERR_UNSUPPORTED;
+  if (!p.bwd_ok) return MOE_ERR_UNSUPPORTED;
   if (!w || !saved) return MOE_ERR_INVALID_ARG;
-  if (!saved->offsets || !saved->gate) return MOE_ERR_INVALID_ARG;
-  if (p.T > 0 && (!dy || !x || !dx || !dw1 || !dw3 || !dw2 || !dgate || !w->w1 || !w->w3 || !w->w2 ||
-                  !saved->topk_idx || !saved->perm || !saved->inv || !saved->a || !saved->b || !saved->h))
+  if (!saved->offsets || !dw1 || !dw3 || !dw2 || !w->w1 || !w->w3 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (p.T > 0 && (!dy || !x || !dx || !dgate || !saved->gate || !saved->perm || !saved->inv || !saved->a ||
+                  !saved->b || !saved->h))
     return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   return backward_impl(p, desc, dy, x, w, saved, dx, dw1, dw3, dw2, dgate, workspace, (hipStream_t)stream);

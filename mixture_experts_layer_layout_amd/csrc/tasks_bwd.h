@@ -1,4 +1,33 @@
-// tasks_bwd.h -- the backward of the expert path as tasks.
+// tasks_bwd.h -- the backward of the expert path (routing frozen) as tasks,
+// run either as one kernel per step or inside one persistent kernel whose
+// workgroups take tickets in dependency order (like the forward).
+//
+// MoK flash (the page "Cursor's MoK achieves 2.37x performance boost on
+// NVIDIA GB300 NVL72"), §01: training adds two exchanges in the opposite
+// direction; §02: the backward pulls the reverse-combine and pushes the
+// reverse-dispatch.  On one GPU both are row moves through the layout:
+//   pull reverse-combine  the dH GEMM reads dY rows through the layout
+//                         (G[r] = dY[src[r]], never staged)
+//   expert dgrad/wgrad    dHu = G W2_e;  dgate_r = <dHu_r, H_r>;
+//                         dH = g_r dHu;  SwiGLU backward
+//                         dA = dH * B * s(A) (1 + A (1 - s(A))),
+//                         dB = dH * silu(A);
+//                         dW2_e = (g G)_e^T H_e;
+//                         dXp = dA W1_e + dB W3_e;
+//                         dW1_e = dA_e^T Xp_e, dW3_e = dB_e^T Xp_e
+//                         (Xp[r] = X[src[r]] read through the layout)
+//   push reverse-dispatch dX[t] = sum_j dXp[inv[t k + j]]  (a fixed-order
+//                         gather-sum, so the result is deterministic)
+// Tasks, in ticket order, and what each waits for:
+//   setup      row tiles and expert order from the saved offsets
+//   rowprep    src[r] = perm[r] / k and g[r] = gate[perm[r]]
+//   dh         (row tile, I tile): dHu, dgate partial, dA | dB   [setup]
+//   dw2        (expert, d tile, I tile)                          [setup]
+//   dxp        (row tile, d tile), K = 2I over [dA | dB]         [dh of the row tile]
+//   dw13       (expert, I tile, d tile): dW1 and dW3 together    [dh of the expert]
+//   dx         8 tokens: dX and dgate                            [every dxp]
+// Weight-gradient tiles are taken in order of decreasing expert load so the
+// longest tiles start first.
 #pragma once
 
 #include "plan.h"
@@ -6,10 +35,275 @@
 
 namespace moe {
 
-static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const void* x, const moe_weights* w,
-                         const moe_saved* sv, void* dx, void* dw1, void* dw3, void* dw2, float* dgate, void* ws,
-                         hipStream_t st) {
-  return MOE_ERR_UNSUPPORTED;
+typedef Tile<128, 256> TileDH;  // row tiles: dh, dxp
+typedef Tile<128, 256> TileDW;  // weight-gradient tiles: dw2, dw13
+constexpr int kRowPrep = 1024;  // rows per rowprep task
+
+struct Bwd {
+  int T, d, E, k, I, R, BM;
+  int nNdh, nNdx, nW2m, nW2n, nW13m, nW13n, nRP, nC;
+  const bf16_t* dy;
+  const bf16_t* x;
+  const bf16_t* w1;
+  const bf16_t* w3;
+  const bf16_t* w2;
+  const float* gate;     // [T, k]
+  const int* offsets;    // [E+1]
+  const int* perm;       // [R]
+  const int* inv;        // [R]
+  const bf16_t* a;       // [R, I]
+  const bf16_t* b;       // [R, I]
+  const bf16_t* h;       // [R, I]
+  bf16_t* dx;            // [T, d]
+  bf16_t* dw1;           // [E, I, d]
+  bf16_t* dw3;           // [E, I, d]
+  bf16_t* dw2;           // [E, d, I]
+  float* dgate;          // [T, k]
+  int* tile_e;           // [max_tiles]
+  int* tile_r0;
+  int* tile_n;
+  int* etile;            // [E+1] first row tile of each expert
+  int* eorder;           // [E] experts by decreasing row count
+  int* src;              // [R]
+  float* grow;           // [R]
+  bf16_t* dab;           // [R, 2I]  dA | dB
+  bf16_t* dxp;           // [R, d]
+  float* dgp;            // [nNdh, R] dgate partial sums
+  Sync s;
+};
+
+// ---------------------------------------------------------------- setup
+__device__ void bwd_setup(const Bwd& B, int* sh /* >= 2*kMaxE + 16 ints */) {
+  int* scnt = sh;
+  int* stile = sh + kMaxE;
+  int* tmp = sh + 2 * kMaxE;
+  __syncthreads();
+  for (int e = threadIdx.x; e < B.E; e += kThreads) {
+    const int c = B.offsets[e + 1] - B.offsets[e];
+    scnt[e] = c;
+    stile[e] = cdiv(c, B.BM);
+  }
+  __syncthreads();
+  const int ntiles = block_exclusive_scan(stile, B.E, tmp);
+  for (int e = threadIdx.x; e < B.E; e += kThreads) {
+    const int c = scnt[e], off = B.offsets[e];
+    B.etile[e] = stile[e];
+    for (int mt = 0, id = stile[e]; mt * B.BM < c; ++mt, ++id) {
+      B.tile_e[id] = e;
+      B.tile_r0[id] = off + mt * B.BM;
+      B.tile_n[id] = min(B.BM, c - mt * B.BM);
+    }
+    // rank by (count descending, expert ascending)
+    int rank = 0;
+    for (int f = 0; f < B.E; ++f) {
+      const int cf = scnt[f];
+      rank += (cf > c) || (cf == c && f < e);
+    }
+    B.eorder[rank] = e;
+  }
+  if (threadIdx.x == 0) {
+    B.etile[B.E] = ntiles;
+    *B.s.n_mtiles = ntiles;
+  }
+}
+
+__device__ void bwd_rowprep(const Bwd& B, int task) {
+  const int r_end = min(B.R, (task + 1) * kRowPrep);
+  for (int r = task * kRowPrep + threadIdx.x; r < r_end; r += kThreads) {
+    const int a = B.perm[r];
+    B.src[r] = a / B.k;
+    B.grow[r] = B.gate[a];
+  }
+}
+
+// ---------------------------------------------------------------- dh
+// dHu = G W2_e for one (row tile, I tile); fused: the dgate partial sum of
+// the tile's columns, dH = g dHu and the SwiGLU backward into [dA | dB].
+__device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float* sred) {
+  typedef TileDH TL;
+  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const int d = B.d, I = B.I;
+  const bf16_t* W2 = B.w2 + (size_t)e * d * I;
+  const int c0 = nt * TL::BN;
+  KRows<TL::BM> la;
+  KCols<TL::BN> lb;
+  la.init([&](int r) -> const bf16_t* { return r < n ? B.dy + (size_t)B.src[r0 + r] * d : nullptr; });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(
+      d / 64, smem, acc, [&](int kt) { la.load(kt); },
+      [&](int kt) {
+        lb.load(kt, [&](int kk) -> const bf16_t* { return W2 + (size_t)kk * I + c0; },
+                [](int) { return 1.0f; });
+      },
+      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const size_t I2 = 2 * (size_t)I;
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * TL::WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      float part = 0.0f;
+      if (row < n) {
+        const size_t gr = (size_t)(r0 + row);
+        const float g = B.grow[gr];
+#pragma unroll
+        for (int j = 0; j < TL::NJ; ++j) {
+          const int col = c0 + wn * TL::WN + 32 * j + (lane & 31);
+          const size_t o = gr * I + col;
+          const float du = acc[i][j][r];
+          const float av = bf16_to_f32(B.a[o]), bv = bf16_to_f32(B.b[o]), hv = bf16_to_f32(B.h[o]);
+          part = fmaf(du, hv, part);
+          const float dh = g * du;
+          const float sg = sigmoid_f(av);
+          B.dab[gr * I2 + col] = f32_to_bf16(dh * bv * sg * (1.0f + av * (1.0f - sg)));
+          B.dab[gr * I2 + I + col] = f32_to_bf16(dh * av * sg);
+        }
+      }
+      // sum over the 32 lanes holding this row's columns (fixed tree)
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o);
+      if ((lane & 31) == 0) sred[wn * TL::BM + row] = part;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < TL::BM && (int)threadIdx.x < n) {
+    const int row = threadIdx.x;
+    B.dgp[(size_t)nt * B.R + r0 + row] = sred[row] + sred[TL::BM + row];
+  }
+}
+
+// ---------------------------------------------------------------- dxp
+// dXp = [dA | dB] [W1_e ; W3_e] for one (row tile, d tile).
+__device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
+  typedef TileDH TL;
+  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const int d = B.d, I = B.I;
+  const bf16_t* W1 = B.w1 + (size_t)e * I * d;
+  const bf16_t* W3 = B.w3 + (size_t)e * I * d;
+  const int c0 = nt * TL::BN;
+  KRows<TL::BM> la;
+  KCols<TL::BN> lb;
+  la.init([&](int r) -> const bf16_t* { return r < n ? B.dab + (size_t)(r0 + r) * 2 * I : nullptr; });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(
+      2 * I / 64, smem, acc, [&](int kt) { la.load(kt); },
+      [&](int kt) {
+        lb.load(kt, [&](int kk) -> const bf16_t* {
+          return (kk < I ? W1 + (size_t)kk * d : W3 + (size_t)(kk - I) * d) + c0;
+        }, [](int) { return 1.0f; });
+      },
+      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  tile_visit<TL>(acc, [&](int row, int col, float v) {
+    if (row < n) B.dxp[(size_t)(r0 + row) * d + c0 + col] = f32_to_bf16(v);
+  });
+}
+
+// ---------------------------------------------------------------- dw2
+// dW2_e[n0 .. +128, i0 .. +256] = sum over the expert's rows r of
+// g_r G[r, n] H[r, i]; K = the expert's rows (zero rows give zeros).
+__device__ void bwd_dw2_tile(const Bwd& B, int q, bf16_t* smem) {
+  typedef TileDW TL;
+  const int nper = B.nW2m * B.nW2n;
+  const int e = B.eorder[q / nper], tt = q % nper;
+  const int n0 = (tt / B.nW2n) * TL::BM, i0 = (tt % B.nW2n) * TL::BN;
+  const int d = B.d, I = B.I;
+  const int off = B.offsets[e], M = B.offsets[e + 1] - off;
+  KCols<TL::BM> la;
+  KCols<TL::BN> lb;
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(
+      cdiv(M, 64), smem, acc,
+      [&](int kt) {
+        la.load(kt, [&](int kk) -> const bf16_t* {
+          return kk < M ? B.dy + (size_t)B.src[off + kk] * d + n0 : nullptr;
+        }, [&](int kk) { return B.grow[off + kk]; });
+      },
+      [&](int kt) {
+        lb.load(kt, [&](int kk) -> const bf16_t* {
+          return kk < M ? B.h + (size_t)(off + kk) * I + i0 : nullptr;
+        }, [](int) { return 1.0f; });
+      },
+      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  bf16_t* out = B.dw2 + (size_t)e * d * I;
+  tile_visit<TL>(acc, [&](int row, int col, float v) {
+    out[(size_t)(n0 + row) * I + i0 + col] = f32_to_bf16(v);
+  });
+}
+
+// ---------------------------------------------------------------- dw13
+// Rows 0..63 of the tile are dW1_e[i0 ..], rows 64..127 dW3_e[i0 ..]:
+// both share the gathered X operand.
+__device__ void bwd_dw13_tile(const Bwd& B, int q, bf16_t* smem) {
+  typedef TileDW TL;
+  const int nper = B.nW13m * B.nW13n;
+  const int e = B.eorder[q / nper], tt = q % nper;
+  const int i0 = (tt / B.nW13n) * (TL::BM / 2), c0 = (tt % B.nW13n) * TL::BN;
+  const int d = B.d, I = B.I;
+  const int off = B.offsets[e], M = B.offsets[e + 1] - off;
+  KCols<TL::BM> la;
+  KCols<TL::BN> lb;
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(
+      cdiv(M, 64), smem, acc,
+      [&](int kt) {
+        la.load(kt, [&](int kk) -> const bf16_t* {
+          return kk < M ? B.dab + (size_t)(off + kk) * 2 * I + i0 : nullptr;
+        }, [](int) { return 1.0f; }, I - TL::BM / 2);
+      },
+      [&](int kt) {
+        lb.load(kt, [&](int kk) -> const bf16_t* {
+          return kk < M ? B.x + (size_t)B.src[off + kk] * d + c0 : nullptr;
+        }, [](int) { return 1.0f; });
+      },
+      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  bf16_t* o1 = B.dw1 + (size_t)e * I * d;
+  bf16_t* o3 = B.dw3 + (size_t)e * I * d;
+  tile_visit<TL>(acc, [&](int row, int col, float v) {
+    bf16_t* o = row < TL::BM / 2 ? o1 + (size_t)(i0 + row) * d : o3 + (size_t)(i0 + row - TL::BM / 2) * d;
+    o[c0 + col] = f32_to_bf16(v);
+  });
+}
+
+// ---------------------------------------------------------------- dx
+// dX[t] = sum_j dXp[inv[t k + j]] (fp32, slot order); dgate from the
+// partial sums in column-tile order.
+__device__ void bwd_dx_tokens(const Bwd& B, int cb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nvec = B.d / 8;
+  for (int tt = wave; tt < kCombTok; tt += 4) {
+    const int t = cb * kCombTok + tt;
+    if (t >= B.T) break;
+    int rows[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) rows[j] = j < B.k ? B.inv[(size_t)t * B.k + j] : 0;
+    if (lane < B.k) {
+      float s = 0.0f;
+      for (int p = 0; p < B.nNdh; ++p) s += B.dgp[(size_t)p * B.R + rows[lane]];
+      B.dgate[(size_t)t * B.k + lane] = s;
+    }
+    for (int v = lane; v < nvec; v += 64) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= B.k) break;
+        const uint4 u = ((const uint4*)B.dxp)[(size_t)rows[j] * nvec + v];
+        const bf16_t* p = (const bf16_t*)&u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += bf16_to_f32(p[q]);
+      }
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      ((uint4*)B.dx)[(size_t)t * nvec + v] = o;
+    }
+  }
 }
 
 }  // namespace moe

@@ -147,10 +147,11 @@ __device__ void router_partial<float>(const Fwd& F, int task) {
   }
 }
 
-// Top-k of one token, one wave.  vals[q] holds expert lane + 64 q.
-// Largest value first; equal values go to the lower expert index.
-__device__ __forceinline__ void wave_topk_gates(const float* vals, int QN, int E, int k, int score,
-                                                int renorm, int& sel_e, float& sel_g) {
+// Top-k of one token, one wave, from its E biased logits in LDS.  Lane l
+// owns experts l + 64 q.  Largest value first; equal values go to the lower
+// expert index.  Lane j < k returns the j-th choice and its gate.
+__device__ __forceinline__ void wave_topk_gates(const float* row, int E, int k, int score, int renorm,
+                                                int& sel_e, float& sel_g) {
   const int lane = threadIdx.x & 63;
   uint32_t taken = 0;
   float sv = -INFINITY;
@@ -158,13 +159,9 @@ __device__ __forceinline__ void wave_topk_gates(const float* vals, int QN, int E
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < kMaxE / 64; ++q) {
-      const int e = lane + 64 * q;
-      if (q < QN && e < E && !((taken >> q) & 1u)) {
-        const float v = vals[q];
-        if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
-      }
+    for (int e = lane, q = 0; e < E; e += 64, ++q) {
+      const float v = row[e];
+      if (!((taken >> q) & 1u) && (v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
     }
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o);
@@ -183,9 +180,7 @@ __device__ __forceinline__ void wave_topk_gates(const float* vals, int QN, int E
       g = ex / wave_sum(ex);
     } else {
       float part = 0.0f;
-#pragma unroll
-      for (int q = 0; q < kMaxE / 64; ++q)
-        if (q < QN && lane + 64 * q < E) part += expf(vals[q] - m);
+      for (int e = lane; e < E; e += 64) part += expf(row[e] - m);
       g = (mine ? expf(sv - m) : 0.0f) / wave_sum(part);
     }
   } else {
@@ -195,48 +190,56 @@ __device__ __forceinline__ void wave_topk_gates(const float* vals, int QN, int E
   sel_g = g;
 }
 
+constexpr int kTopkChunk = 16;  // tokens whose logits are staged in LDS at once
+// LDS of router_topk: block masks (kMaxE u64) + a chunk of logits
+constexpr size_t kTopkSmem = kMaxE * 8 + (size_t)kTopkChunk * kMaxE * 4;
+
 // Sums the slices, adds the bias, selects, writes idx/gates and the block's
-// expert bitmasks.  With S == 1 and lpart == the caller's logits this is
-// also the standalone route step.
+// expert bitmasks.  The logits of 16 tokens at a time are summed into LDS by
+// the whole workgroup (coalesced, independent loads), then each wave selects
+// for 4 of them.  With S == 1 and lpart == the caller's logits this is also
+// the standalone route step.
 template <bool MASKS>
-__device__ void router_topk(const Fwd& F, int b, unsigned long long* smask) {
+__device__ void router_topk(const Fwd& F, int b, char* smem) {
+  unsigned long long* smask = (unsigned long long*)smem;
+  float* sv = (float*)(smem + kMaxE * 8);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (MASKS) {
-    for (int e = threadIdx.x; e < F.E; e += kThreads) smask[e] = 0ull;
+  const int E = F.E;
+  if (MASKS)
+    for (int e = threadIdx.x; e < E; e += kThreads) smask[e] = 0ull;
+  for (int c0 = 0; c0 < kTokBlock; c0 += kTopkChunk) {
+    const int t0 = b * kTokBlock + c0;
+    if (t0 >= F.T) break;
     __syncthreads();
-  }
-  const int QN = cdiv(F.E, 64);
-  for (int tt = wave; tt < kTokBlock; tt += 4) {
-    const int t = b * kTokBlock + tt;
-    if (t >= F.T) break;
-    float vals[kMaxE / 64];
-#pragma unroll
-    for (int q = 0; q < kMaxE / 64; ++q) {
-      const int e = lane + 64 * q;
-      float v = -INFINITY;
-      if (q < QN && e < F.E) {
-        v = 0.0f;
-        for (int s = 0; s < F.S; ++s) v += F.lpart[((size_t)s * F.T + t) * F.E + e];
-        if (F.logits) F.logits[(size_t)t * F.E + e] = v;
-        if (F.bias) v += F.bias[e];
+    for (int p = threadIdx.x; p < kTopkChunk * E; p += kThreads) {
+      const int t = t0 + p / E, e = p % E;
+      if (t >= F.T) break;
+      float v = 0.0f;
+      for (int s = 0; s < F.S; ++s) v += F.lpart[((size_t)s * F.T + t) * E + e];
+      if (F.logits) F.logits[(size_t)t * E + e] = v;
+      if (F.bias) v += F.bias[e];
+      sv[p] = v;
+    }
+    __syncthreads();
+    for (int tt = wave; tt < kTopkChunk; tt += 4) {
+      const int t = t0 + tt;
+      if (t >= F.T) break;
+      int se;
+      float sg;
+      wave_topk_gates(sv + tt * E, E, F.k, F.score, F.renorm, se, sg);
+      if (lane < F.k) {
+        F.topk[(size_t)t * F.k + lane] = se;
+        F.gate[(size_t)t * F.k + lane] = sg;
+        if (MASKS) atomicOr(&smask[se], 1ull << (c0 + tt));
       }
-      vals[q] = v;
-    }
-    int se;
-    float sg;
-    wave_topk_gates(vals, QN, F.E, F.k, F.score, F.renorm, se, sg);
-    if (lane < F.k) {
-      F.topk[(size_t)t * F.k + lane] = se;
-      F.gate[(size_t)t * F.k + lane] = sg;
-      if (MASKS) atomicOr(&smask[se], 1ull << tt);
     }
   }
   if (MASKS) {
     __syncthreads();
-    for (int e = threadIdx.x; e < F.E; e += kThreads) {
+    for (int e = threadIdx.x; e < E; e += kThreads) {
       const unsigned long long m = smask[e];
-      F.bmask[(size_t)b * F.E + e] = m;
-      F.bcnt[(size_t)b * F.E + e] = __popcll(m);
+      F.bmask[(size_t)b * E + e] = m;
+      F.bcnt[(size_t)b * E + e] = __popcll(m);
     }
   }
 }

@@ -51,3 +51,21 @@ def row_rel_err(got, want, rows=None):
     if rows is not None:
         got, want = got[rows], want[rows]
     return M.max_row_rel_err(got, want)
+
+
+def dgate_err(got, want, floor=0.1):
+    """Error of dgate [T, k].  Each entry is a dot product over I terms, and a
+    token row holds only k of them: with small k a row whose entries all sit
+    near zero by cancellation is common, and its row-relative error then
+    measures the rounding of the bf16 operands, not the path.  Returns the
+    larger of (a) the max error relative to the whole tensor's max norm and
+    (b) the row-relative error over rows whose max norm is at least
+    ``floor`` times the tensor's."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    scale = np.max(np.abs(want)) if want.size else 0.0
+    if scale == 0.0:
+        return float(np.max(np.abs(got))) if got.size else 0.0
+    glob = float(np.max(np.abs(got - want)) / scale)
+    rows = np.max(np.abs(want), axis=1) >= floor * scale
+    return max(glob, M.max_row_rel_err(got[rows], want[rows]) if rows.any() else 0.0)
