@@ -2,19 +2,30 @@
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate), used by every expert GEMM of
 // the forward and backward.
 //
-// C[BM x BN] = sum_k A[m, k] * B[n, k], K consumed 64 at a time through two
-// LDS stages (register prefetch of stage k+1 while stage k feeds the MFMAs,
-// one barrier per step).  LDS holds both operands k-contiguous: a row of 64
-// bf16 is 8 chunks of 16 bytes and chunk c of row r is stored at chunk
-// c ^ (r & 7), so the 16-byte MFMA operand reads of 8 consecutive rows hit
-// 8 different bank groups, as do the 16-byte stores of the loaders.
+// C[BM x BN] = sum_k A[m, k] * B[n, k], K consumed 64 at a time: two LDS
+// stages and two register stages, so the global loads of two stages are in
+// flight while a third feeds the MFMAs; one barrier per step.  LDS holds
+// both operands k-contiguous: a row of 64 bf16 is 8 chunks of 16 bytes and
+// chunk c of row r is stored at chunk c ^ ((r >> 1) & 7) (lds_idx), so the
+// 16-byte reads and writes of 16 lanes at a time hit 16 different bank
+// groups.
 //
-// Operands come through loaders that fill one LDS stage:
+// Operands come through loaders with three steps:
+//   prep(kt)    addressing of stage kt (may itself load row indices); runs
+//               one stage ahead of load() so those loads are in flight early
+//   load(b, kt) the stage's global loads into register buffer b, all
+//               unconditional
+//               (no per-lane branches: padding rows are clamped to a
+//               readable row, or aimed at a zero row when they must add 0)
+//   store(b, lds) register buffer b into LDS; any scaling happens here, after
+//               the MFMAs of the previous stage, so no load result is
+//               consumed early
+// Loader kinds:
 //   KRows   the operand is stored as rows with k contiguous (row-major
 //           [rows, K]); rows may be gathered through an index (pull)
 //   KCols   the operand is stored with k as the row index and the tile's
-//           rows contiguous ([K, rows]); each thread loads an 8x8 block and
-//           transposes it in registers before the LDS store
+//           rows contiguous ([K, rows]); each thread loads a KK x 8 block
+//           and transposes it in registers before the LDS store
 // Four waves split the tile 2 x 2; each wave owns (BM/2) x (BN/2) in
 // (BM/64) x (BN/64) MFMA blocks of 32 x 32.
 #pragma once
@@ -23,8 +34,13 @@
 
 namespace moe {
 
+// Element index of 16-byte chunk `chunk` of tile row `row` in an LDS stage.
+// The LDS serves 256 bytes (64 banks) per cycle, i.e. one 16-byte access
+// for each of 16 lanes: the XOR key (row >> 1) & 7 places the same chunk of
+// 16 consecutive rows (two rows per 256 bytes) in 16 different slots, and
+// the 8 chunks of one row in 8 different slots.
 __device__ __forceinline__ int lds_idx(int row, int chunk) {
-  return (row << 6) + (((chunk ^ row) & 7) << 3);
+  return (row << 6) + (((chunk ^ (row >> 1)) & 7) << 3);
 }
 
 template <int BM_, int BN_>
@@ -42,116 +58,191 @@ template <int ROWS>
 struct KRows {
   static constexpr int PER = ROWS / 32;
   const bf16_t* row[PER];
-  uint4 v[PER];
-  // rowptr(r) -> pointer to element k=0 of tile row r, or nullptr for a
-  // row outside the operand (it loads as zeros).
+  uint4 v[2][PER];
+  // rowptr(r) -> pointer to element k=0 of tile row r; must be readable
+  // for every r (clamp rows past the operand to a real one).
   template <class F>
   __device__ __forceinline__ void init(F rowptr) {
     const int r0 = threadIdx.x >> 3;
 #pragma unroll
     for (int i = 0; i < PER; ++i) row[i] = rowptr(r0 + 32 * i);
   }
+  __device__ __forceinline__ void prep(int) {}
+  template <int BUF>
   __device__ __forceinline__ void load(int kt) {
     const int ch = threadIdx.x & 7;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (row[i])
-        v[i] = *(const uint4*)(row[i] + kt * 64 + ch * 8);
-      else
-        v[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < PER; ++i) v[BUF][i] = *(const uint4*)(row[i] + kt * 64 + ch * 8);
   }
+  template <int BUF>
   __device__ __forceinline__ void store(bf16_t* lds) const {
     const int r0 = threadIdx.x >> 3, ch = threadIdx.x & 7;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) *(uint4*)(lds + lds_idx(r0 + 32 * i, ch)) = v[i];
+    for (int i = 0; i < PER; ++i) *(uint4*)(lds + lds_idx(r0 + 32 * i, ch)) = v[BUF][i];
   }
 };
 
-// k is the row index of the stored operand; the tile's rows (ROWS of them)
-// are contiguous within each stored row.  Thread t covers k-chunk t%8 and
-// tile rows 8*(t/8) .. +7 (threads past ROWS/8*8 idle).
-//   kptr(k) -> pointer to the stored row holding absolute k at the tile's
-//              first row, or nullptr when k lies outside the operand
-//   kscale(k) -> factor applied to that stored row (1 for none)
-//   half_off  -> extra element offset for the second half of the tile's
-//                rows (two column ranges of one stored row, e.g. the dA and
-//                dB halves of [dA | dB]); 0 when the rows are contiguous
-template <int ROWS>
+// k is the row index of the stored operand; the tile's ROWS rows are
+// contiguous within each stored row.  Thread t covers k-group t % KG (KK
+// consecutive k) and tile rows 8*(t/KG) .. +7, with KK = 8 for 256-row
+// tiles and 4 for 128-row tiles, so all 256 threads take part.
+//   kptr(k)   pointer to the stored row holding k, at the tile's first row;
+//             never null (k past the operand -> a zero row)
+//   kscale(k) factor for that stored row (SCALED only)
+//   half_off  extra element offset for the second half of the tile's rows
+//             (two column ranges of one stored row, e.g. the dA and dB
+//             halves of [dA | dB]); 0 when the rows are contiguous
+template <int ROWS, bool SCALED, class P, class S>
 struct KCols {
-  static constexpr int NB = ROWS / 8;
-  uint4 v[8];
-  template <class P, class S>
-  __device__ __forceinline__ void load(int kt, P kptr, S kscale, int half_off = 0) {
-    const int kb = threadIdx.x & 7, nb = threadIdx.x >> 3;
-    if (nb >= NB) return;
-    const int coff = nb * 8 + (nb >= NB / 2 ? half_off : 0);
+  static constexpr int KK = ROWS >= 256 ? 8 : 4;
+  static constexpr int KG = 64 / KK;
+  static_assert(KG * (ROWS / 8) == kThreads, "KCols covers the stage with every thread");
+  P kptr;
+  S kscale;
+  int coff;
+  const bf16_t* p[KK];
+  float s[KK], sl[2][KK];
+  uint4 v[2][KK];
+  __device__ __forceinline__ KCols(P kp, S ks, int half_off) : kptr(kp), kscale(ks) {
+    const int nb = threadIdx.x / KG;
+    coff = nb * 8 + (nb >= ROWS / 16 ? half_off : 0);
+  }
+  __device__ __forceinline__ void prep(int kt) {
+    const int k0 = kt * 64 + (threadIdx.x % KG) * KK;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = kt * 64 + kb * 8 + kk;
-      const bf16_t* p = kptr(k);
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (p) {
-        x = *(const uint4*)(p + coff);
-        const float s = kscale(k);
-        if (s != 1.0f) {
-          uint32_t* w = (uint32_t*)&x;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            w[q] = pack_bf16x2(bf16_to_f32((bf16_t)(w[q] & 0xffff)) * s,
-                               bf16_to_f32((bf16_t)(w[q] >> 16)) * s);
-        }
-      }
-      v[kk] = x;
+    for (int kk = 0; kk < KK; ++kk) {
+      p[kk] = kptr(k0 + kk);
+      if (SCALED) s[kk] = kscale(k0 + kk);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-    const int kb = threadIdx.x & 7, nb = threadIdx.x >> 3;
-    if (nb >= NB) return;
-    const uint32_t* w = (const uint32_t*)v;  // w[kk*4 + q] = elements 2q, 2q+1 of k-row kk
+  template <int BUF>
+  __device__ __forceinline__ void load(int) {
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      // element mm of each k-row: dword mm/2, half mm%2
-      const int q = mm >> 1;
+    for (int kk = 0; kk < KK; ++kk) {
+      v[BUF][kk] = *(const uint4*)(p[kk] + coff);
+      if (SCALED) sl[BUF][kk] = s[kk];
+    }
+  }
+  template <int BUF>
+  __device__ __forceinline__ void store(bf16_t* lds) {
+    uint32_t* w = (uint32_t*)v[BUF];  // w[kk*4 + q] = elements 2q, 2q+1 of k-row kk
+    if (SCALED) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[kk * 4 + q] = pack_bf16x2(bf16_to_f32((bf16_t)(w[kk * 4 + q] & 0xffff)) * sl[BUF][kk],
+                                      bf16_to_f32((bf16_t)(w[kk * 4 + q] >> 16)) * sl[BUF][kk]);
+    }
+    const int kg = threadIdx.x % KG, nb = threadIdx.x / KG;
+    // lanes of odd nb walk their 8 rows in the order 1,0,3,2,...: the two
+    // lane groups written together then target rows of opposite parity,
+    // i.e. opposite halves of the 256-byte bank row
+    const int odd = nb & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int mm = i ^ odd;
+      // element mm of each k-row: dword mm/2 (= i/2), half mm%2
+      const int q = i >> 1;
       const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
-      uint4 o;
-      o.x = __builtin_amdgcn_perm(w[1 * 4 + q], w[0 * 4 + q], sel);
-      o.y = __builtin_amdgcn_perm(w[3 * 4 + q], w[2 * 4 + q], sel);
-      o.z = __builtin_amdgcn_perm(w[5 * 4 + q], w[4 * 4 + q], sel);
-      o.w = __builtin_amdgcn_perm(w[7 * 4 + q], w[6 * 4 + q], sel);
-      *(uint4*)(lds + lds_idx(nb * 8 + mm, kb)) = o;
+      if (KK == 8) {
+        uint4 o;
+        o.x = __builtin_amdgcn_perm(w[1 * 4 + q], w[0 * 4 + q], sel);
+        o.y = __builtin_amdgcn_perm(w[3 * 4 + q], w[2 * 4 + q], sel);
+        o.z = __builtin_amdgcn_perm(w[5 * 4 + q], w[4 * 4 + q], sel);
+        o.w = __builtin_amdgcn_perm(w[7 * 4 + q], w[6 * 4 + q], sel);
+        *(uint4*)(lds + lds_idx(nb * 8 + mm, kg)) = o;
+      } else {
+        uint2 o;
+        o.x = __builtin_amdgcn_perm(w[1 * 4 + q], w[0 * 4 + q], sel);
+        o.y = __builtin_amdgcn_perm(w[3 * 4 + q], w[2 * 4 + q], sel);
+        *(uint2*)(lds + lds_idx(nb * 8 + mm, kg >> 1) + (kg & 1) * 4) = o;
+      }
     }
   }
 };
+
+struct NoScale {
+  __device__ __forceinline__ float operator()(int) const { return 1.0f; }
+};
+
+template <int ROWS, class P>
+__device__ __forceinline__ KCols<ROWS, false, P, NoScale> kcols(P kptr, int half_off = 0) {
+  return KCols<ROWS, false, P, NoScale>(kptr, NoScale(), half_off);
+}
+template <int ROWS, class P, class S>
+__device__ __forceinline__ KCols<ROWS, true, P, S> kcols_scaled(P kptr, S kscale, int half_off = 0) {
+  return KCols<ROWS, true, P, S>(kptr, kscale, half_off);
+}
 
 // ---------------------------------------------------------------- core
+// The 64-deep stage as 4 k-slices of 16; the operand fragments of slice
+// s+1 are read from LDS before the MFMAs of slice s are issued, so the LDS
+// latency hides behind them.
 template <class TL>
 __device__ __forceinline__ void tile_compute(const bf16_t* As, const bf16_t* Bs,
                                              f32x16_t (&acc)[TL::MI][TL::NJ]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  bf16x8_t a[2][TL::MI], b[2][TL::NJ];
+  auto frags = [&](int ks, bf16x8_t(&fa)[TL::MI], bf16x8_t(&fb)[TL::NJ]) {
     const int ch = ks * 2 + (lane >> 5);
-    bf16x8_t a[TL::MI], b[TL::NJ];
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
-      a[i] = *(const bf16x8_t*)(As + lds_idx(wm * TL::WM + 32 * i + (lane & 31), ch));
+      fa[i] = *(const bf16x8_t*)(As + lds_idx(wm * TL::WM + 32 * i + (lane & 31), ch));
 #pragma unroll
     for (int j = 0; j < TL::NJ; ++j)
-      b[j] = *(const bf16x8_t*)(Bs + lds_idx(wn * TL::WN + 32 * j + (lane & 31), ch));
+      fb[j] = *(const bf16x8_t*)(Bs + lds_idx(wn * TL::WN + 32 * j + (lane & 31), ch));
+  };
+  frags(0, a[0], b[0]);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) frags(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < TL::NJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < TL::NJ; ++j) acc[i][j] = mfma32x32x16(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+  }
+  // instruction order for the scheduler: the reads of slice 0, then per
+  // slice the reads of the next slice ahead of this slice's MFMAs
+  constexpr int NR = TL::MI + TL::NJ, NM = TL::MI * TL::NJ;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
 }
 
-// Runs the K loop.  LoadA(kt) / LoadB(kt) fetch stage kt into registers;
-// StoreA(lds) / StoreB(lds) write the fetched stage.  nk may be 0.
-template <class TL, class LA, class LB, class SA, class SB>
-__device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&acc)[TL::MI][TL::NJ],
-                                              LA loadA, LB loadB, SA storeA, SB storeB) {
+// Runs the K loop over nk stages (nk may be 0: the tile is then zero).
+// Two stages are in flight while a third feeds the MFMAs: at step kt the
+// loads of stage kt+2 go out into the register buffer freed by step kt-1,
+// the MFMAs consume stage kt from LDS, and stage kt+1 (loaded a step
+// earlier) is written to the other LDS buffer.  Every load, prep and store
+// is unconditional -- past the last stage they repeat it -- so the only
+// waits the compiler emits are for the stage being stored.
+// One step of the K loop with register buffer CUR free (stage kt lives in
+// LDS buffer CUR, stage kt+1 in register buffer CUR ^ 1).
+template <int CUR, class TL, class LA, class LB>
+__device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16_t* Bs,
+                                              f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B) {
+  A.template load<CUR>(min(kt + 2, last));
+  B.template load<CUR>(min(kt + 2, last));
+  A.prep(min(kt + 3, last));
+  B.prep(min(kt + 3, last));
+  // keep the scheduler from sinking these loads below the LDS stores of
+  // the previous stage (which wait for their own loads)
+  __builtin_amdgcn_sched_barrier(0);
+  tile_compute<TL>(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  A.template store<CUR ^ 1>(As + (CUR ^ 1) * TL::LDS_A);
+  B.template store<CUR ^ 1>(Bs + (CUR ^ 1) * TL::LDS_B);
+  __syncthreads();
+}
+
+template <class TL, class LA, class LB>
+__device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&acc)[TL::MI][TL::NJ], LA& A,
+                                              LB& B) {
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
@@ -159,28 +250,29 @@ __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&a
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (nk <= 0) return;
+  const int last = nk - 1;
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
+  A.prep(0);
+  B.prep(0);
+  A.template load<0>(0);
+  B.template load<0>(0);
+  A.prep(min(1, last));
+  B.prep(min(1, last));
+  A.template load<1>(min(1, last));
+  B.template load<1>(min(1, last));
+  A.prep(min(2, last));
+  B.prep(min(2, last));
   __syncthreads();
-  loadA(0);
-  loadB(0);
-  storeA(As);
-  storeB(Bs);
+  A.template store<0>(As);
+  B.template store<0>(Bs);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      loadA(kt + 1);
-      loadB(kt + 1);
-    }
-    tile_compute<TL>(As + cur * TL::LDS_A, Bs + cur * TL::LDS_B, acc);
-    if (more) {
-      storeA(As + (cur ^ 1) * TL::LDS_A);
-      storeB(Bs + (cur ^ 1) * TL::LDS_B);
-    }
-    __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    mainloop_step<0, TL>(kt, last, As, Bs, acc, A, B);
+    mainloop_step<1, TL>(kt + 1, last, As, Bs, acc, A, B);
   }
+  if (kt < nk) mainloop_step<0, TL>(kt, last, As, Bs, acc, A, B);
 }
 
 // Visits every accumulator: f(tile_row, tile_col, value).
@@ -220,6 +312,29 @@ __device__ __forceinline__ void tile_visit_pairs(const f32x16_t (&acc)[TL::MI][T
         f(row, col, acc[i][j][r], acc[i][j + H][r]);
       }
 }
+
+// ---------------------------------------------------------------- epilogue
+// A [ROWS x W] bf16 block staged in LDS, then written out with 16-byte
+// stores: block row r (r < nrows) goes to dst(r), a pointer to the block's
+// first column in that output row.  The LDS row pitch is padded by 16 bytes
+// so the 2-byte writes of the MFMA accumulator layout spread over the banks.
+// The caller synchronises before reusing the LDS after flush().
+template <int ROWS, int W>
+struct Staged {
+  static constexpr int LD = W + 8;
+  static constexpr size_t bytes = (size_t)ROWS * LD * sizeof(bf16_t);
+  bf16_t* s;
+  __device__ __forceinline__ void put(int row, int col, float v) const { s[row * LD + col] = f32_to_bf16(v); }
+  template <class D>
+  __device__ __forceinline__ void flush(int nrows, D dst) const {
+    __syncthreads();
+    constexpr int CPR = W / 8;
+    for (int c = threadIdx.x; c < ROWS * CPR; c += kThreads) {
+      const int row = c / CPR, ch = c % CPR;
+      if (row < nrows) *(uint4*)(dst(row) + ch * 8) = *(const uint4*)(s + row * LD + ch * 8);
+    }
+  }
+};
 
 // Map a B-tile row of the SwiGLU tile to (which, out_col): which 0 = W1,
 // 1 = W3; out_col in [0, BN/2).

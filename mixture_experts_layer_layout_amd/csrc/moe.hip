@@ -1,13 +1,13 @@
 // moe.hip -- kernels and C-ABI entry points of libmoe.so (gfx950).
 //
-// The forward runs either as one persistent kernel (desc->fused = 1) whose
-// workgroups take tasks from a ticket queue in dependency order and wait on
-// the device counters of their inputs, or as one kernel per step on the
-// caller's stream.  Both call the same task functions (tasks_fwd.h,
-// tasks_bwd.h).  Tickets are handed out in increasing order and every task
-// waits only on tasks with lower tickets, which were claimed by workgroups
-// already running; so the queue drains whatever the grid size, and every
-// wait is additionally bounded (MOE_ERR_TIMEOUT) so a fault cannot hang it.
+// The forward and the backward each run either as one persistent kernel
+// (desc->fused = 1) whose workgroups claim tasks phase by phase from
+// per-XCD queues and wait on the device counters of their inputs, or as one
+// kernel per step on the caller's stream.  Both call the same task
+// functions (tasks_fwd.h, tasks_bwd.h).  A task waits only on tasks of
+// earlier phases, all of which were claimed by running workgroups before it
+// (sched.h); so the queues drain whatever the grid size, and every wait is
+// additionally bounded (MOE_ERR_TIMEOUT) so a fault cannot hang them.
 #include <hip/hip_runtime.h>
 
 #include <string.h>
@@ -16,6 +16,7 @@
 #include "plan.h"
 #include "tasks_fwd.h"
 #include "tasks_bwd.h"
+#include "sched.h"
 #include "mxfp8.h"
 
 namespace moe {
@@ -60,19 +61,19 @@ int make_plan(const moe_desc* D, Plan* p) {
   // row tiles of the forward (BM rows) and of the backward (TileDH::BM rows)
   const int min_bm = p->BM < TileDH::BM ? p->BM : TileDH::BM;
   p->max_tiles = p->R / min_bm + (E < p->R ? E : p->R) + 1;
-  p->bwd_ok = !f32 && !p->mxfp8 && d % 256 == 0 && I % 256 == 0;
-  p->nNdh = I / 256;
-  p->nNdx = d / 256;
-  p->nW2m = d / 128;
-  p->nW2n = I / 256;
-  p->nW13m = I / 64;
-  p->nW13n = d / 256;
+  p->bwd_ok = !f32 && !p->mxfp8 && d % 128 == 0 && I % 128 == 0;
+  p->nNdh = I / TileDH::BN;
+  p->nNdx = d / TileDH::BN;
+  p->nW2m = d / TileDW::BM;
+  p->nW2n = I / TileDW::BN;
+  p->nW13m = I / (TileDW::BM / 2);
+  p->nW13n = d / TileDW::BN;
   p->nRP = cdiv(p->R, kRowPrep);
 
   const size_t R = (size_t)p->R, es = p->act_es;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-  p->n_ctr = C_HEADER + p->nb + 3 * (size_t)p->max_tiles + 2 * (size_t)E + 16;
+  p->n_ctr = C_HEADER + kMaxPhases * kXcds + p->nb + 3 * (size_t)p->max_tiles + 2 * (size_t)E + 16;
   p->o_ctr = take(p->n_ctr * 4);
   p->o_lpart = take((size_t)p->S * T * E * 4);
   p->o_topk = take(R * 4);
@@ -96,6 +97,7 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
   if (p->bwd_ok) {
+    p->o_zero = take(((size_t)2 * I + d + 256) * 2);
     p->o_dab = take(R * 2 * I * 2);
     p->o_dgp = take((size_t)p->nNdh * R * 4);
   }
@@ -117,6 +119,7 @@ static Sync make_sync(const Plan& p, void* ws, int32_t* status, uint32_t flags) 
   s.n_mtiles = c + C_NMT;
   s.aux3 = c + C_AUX3;
   int* q = c + C_HEADER;
+  s.qctr = q; q += kMaxPhases * kXcds;
   s.r1_cnt = q; q += p.nb;
   s.ready = q; q += p.max_tiles;
   s.h_cnt = q; q += p.max_tiles;
@@ -148,6 +151,7 @@ static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved*
   F.tile_e = at<int>(ws, p.o_tile_e);
   F.tile_r0 = at<int>(ws, p.o_tile_r0);
   F.tile_n = at<int>(ws, p.o_tile_n);
+  F.etile = at<int>(ws, p.o_etile);
   F.perm = (sv && sv->perm) ? sv->perm : at<int>(ws, p.o_perm);
   F.inv = (sv && sv->inv) ? sv->inv : at<int>(ws, p.o_inv);
   F.src = at<int>(ws, p.o_src);
@@ -216,85 +220,96 @@ __device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* sme
 }
 
 template <class Act, class TL>
-__global__ void __launch_bounds__(256, 1) k_g1(Fwd F) {
+__global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g1(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = id / F.nN1, nt = id % F.nN1;
-  if (tile >= *F.s.n_mtiles) return;
+  if (id >= *F.s.n_mtiles * F.nN1) return;
+  int tile, nt;
+  raster_decode(F.etile, F.E, F.nN1, id, tile, nt);
   run_g1<Act, TL>(F, tile, nt, smem);
 }
 
 template <class Act, class TL>
-__global__ void __launch_bounds__(256, 1) k_g2(Fwd F) {
+__global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g2(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = id / F.nN2, nt = id % F.nN2;
-  if (tile >= *F.s.n_mtiles) return;
+  if (id >= *F.s.n_mtiles * F.nN2) return;
+  int tile, nt;
+  raster_decode(F.etile, F.E, F.nN2, id, tile, nt);
   run_g2<Act, TL>(F, tile, nt, smem);
 }
 
 template <class Act>
 __global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F, blockIdx.x); }
 
-// The persistent forward.
+// The persistent forward: phases router slices | top-k | layout | gather
+// | up-projection tiles | down-projection tiles | combine, claimed through
+// the per-XCD phase queues (sched.h); the projection tiles are enumerated
+// in the grouped raster, 64 consecutive tasks per XCD queue block.  Each
+// task waits on the counters its inputs raise.
 template <class Act, class TL>
-__global__ void __launch_bounds__(256, 1) k_fused_fwd(Fwd F) {
+__global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int s_t, s_flag;
+  __shared__ int s_t, s_ph, s_nmt, s_flag;
   const WaitCtx W = wctx(F.s);
-  const int n_r1 = F.nb * F.S;
+  Claim c;
+  c.own = xcc_id();
+  int nmt = -1;  // thread 0: row tiles, known once the layout is done
+  auto shape = [&](int ph, int& groups, int& per) -> bool {
+    per = 1;
+    if (ph == 0) { groups = F.nb * F.S; return true; }
+    if (ph == 1) { groups = F.nb; return true; }
+    if (ph == 2) { groups = 1; return true; }
+    if (nmt < 0) {
+      if (!thread_wait_geq(F.s.scan_done, 1, W)) return false;
+      nmt = *(volatile int*)F.s.n_mtiles;
+    }
+    if (ph == 3) { groups = nmt; return true; }
+    if (ph == 6) { groups = F.nC; return true; }
+    groups = cdiv(nmt * (ph == 4 ? F.nN1 : F.nN2), kRasterBlock);
+    per = kRasterBlock;
+    return true;
+  };
   for (;;) {
     __syncthreads();
-    if (threadIdx.x == 0) s_t = atomicAdd(F.s.queue, 1);
+    if (threadIdx.x == 0) {
+      s_t = claim_next(F.s.qctr, 7, c, shape);
+      s_ph = c.phase;
+      s_nmt = nmt;
+    }
     __syncthreads();
-    int t = s_t;
-    if (t < n_r1) {
+    const int t = s_t, ph = s_ph;
+    if (t < 0) break;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (ph == 0) {
       router_partial<Act>(F, t);
       signal_add(&F.s.r1_cnt[t / F.S], 1);
-      continue;
-    }
-    t -= n_r1;
-    if (t < F.nb) {
+    } else if (ph == 1) {
       if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
       signal_add(F.s.r2_done, 1);
-      continue;
-    }
-    t -= F.nb;
-    if (t == 0) {
+    } else if (ph == 2) {
       if (wait_geq(F.s.r2_done, F.nb, W, &s_flag)) layout_scan(F, (int*)smem);
       signal_add(F.s.scan_done, 1);
-      continue;
-    }
-    t -= 1;
-    if (!wait_geq(F.s.scan_done, 1, W, &s_flag)) break;
-    const int nmt = *(volatile int*)F.s.n_mtiles;
-    if (t < nmt) {
+    } else if (ph == 3) {
       if (F.direct)
         gather_tile<Act, false>(F, t, (int*)smem);
       else
         gather_tile<Act, true>(F, t, (int*)smem);
-      continue;
-    }
-    t -= nmt;
-    if (t < nmt * F.nN1) {
-      const int tile = t / F.nN1, nt = t % F.nN1;
+    } else if (ph == 4) {
+      if (t >= s_nmt * F.nN1) continue;
+      int tile, nt;
+      raster_decode(F.etile, F.E, F.nN1, t, tile, nt);
       if (wait_geq(&F.s.ready[tile], 1, W, &s_flag)) run_g1<Act, TL>(F, tile, nt, smem);
       signal_add(&F.s.h_cnt[tile], 1);
-      continue;
-    }
-    t -= nmt * F.nN1;
-    if (t < nmt * F.nN2) {
-      const int tile = t / F.nN2, nt = t % F.nN2;
+    } else if (ph == 5) {
+      if (t >= s_nmt * F.nN2) continue;
+      int tile, nt;
+      raster_decode(F.etile, F.E, F.nN2, t, tile, nt);
       if (wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) run_g2<Act, TL>(F, tile, nt, smem);
       signal_add(F.s.g2_done, 1);
-      continue;
+    } else {
+      if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
     }
-    t -= nmt * F.nN2;
-    if (t < F.nC) {
-      if (wait_geq(F.s.g2_done, nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
-      continue;
-    }
-    break;
   }
 }
 
@@ -319,92 +334,114 @@ __global__ void __launch_bounds__(256) k_bwd_setup(Bwd B) {
 
 __global__ void __launch_bounds__(256) k_bwd_rowprep(Bwd B) { bwd_rowprep(B, blockIdx.x); }
 
-__global__ void __launch_bounds__(256, 1) k_bwd_dh(Bwd B) {
+__global__ void __launch_bounds__(256, 2) k_bwd_dh(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = id / B.nNdh, nt = id % B.nNdh;
-  if (tile >= *B.s.n_mtiles) return;
+  if (id >= *B.s.n_mtiles * B.nNdh) return;
+  int tile, nt;
+  raster_decode(B.etile, B.E, B.nNdh, id, tile, nt);
   bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
 }
 
-__global__ void __launch_bounds__(256, 1) k_bwd_dxp(Bwd B) {
+__global__ void __launch_bounds__(256, 2) k_bwd_dxp(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = id / B.nNdx, nt = id % B.nNdx;
-  if (tile >= *B.s.n_mtiles) return;
+  if (id >= *B.s.n_mtiles * B.nNdx) return;
+  int tile, nt;
+  raster_decode(B.etile, B.E, B.nNdx, id, tile, nt);
   bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
 }
 
-__global__ void __launch_bounds__(256, 1) k_bwd_dw2(Bwd B) {
+__global__ void __launch_bounds__(256, 2) k_bwd_dw2(Bwd B) {
   extern __shared__ __align__(16) char smem[];
-  bwd_dw2_tile(B, xcd_remap(blockIdx.x, gridDim.x), (bf16_t*)smem);
+  // dispatch order (heaviest experts first) spread round-robin over the XCDs
+  const int nper = B.nW2m * B.nW2n;
+  bwd_dw2_tile(B, blockIdx.x / nper, blockIdx.x % nper, (bf16_t*)smem);
 }
 
-__global__ void __launch_bounds__(256, 1) k_bwd_dw13(Bwd B) {
+__global__ void __launch_bounds__(256, 2) k_bwd_dw13(Bwd B) {
   extern __shared__ __align__(16) char smem[];
-  bwd_dw13_tile(B, xcd_remap(blockIdx.x, gridDim.x), (bf16_t*)smem);
+  const int nper = B.nW13m * B.nW13n;
+  bwd_dw13_tile(B, blockIdx.x / nper, blockIdx.x % nper, (bf16_t*)smem);
 }
 
 __global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockIdx.x); }
 
-// The persistent backward: the same tasks in ticket order.
+// The persistent backward: phases setup | rowprep | dh | dw2 | dxp | dw13
+// | dx through the per-XCD phase queues (dh and dxp tiles in the grouped
+// raster, 64 per queue block; the weight-gradient tiles of the expert of
+// load rank q -> queue q % 8, kWgradPerTicket tiles per claim).
 __global__ void __launch_bounds__(256, 1) k_fused_bwd(Bwd B) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int s_t, s_flag;
+  __shared__ int s_t, s_ph, s_nmt, s_flag;
   const WaitCtx W = wctx(B.s);
   const int nper2 = B.nW2m * B.nW2n, nper13 = B.nW13m * B.nW13n;
-  const int nW2 = B.E * nper2, nW13 = B.E * nper13;
+  const int g2 = cdiv(nper2, kWgradPerTicket), g13 = cdiv(nper13, kWgradPerTicket);
+  Claim c;
+  c.own = xcc_id();
+  int nmt = -1;
+  auto shape = [&](int ph, int& groups, int& per) -> bool {
+    per = 1;
+    if (ph == 0) { groups = 1; return true; }
+    if (ph == 1) { groups = B.nRP; return true; }
+    if (ph == 3) { groups = B.E; per = g2; return true; }
+    if (ph == 5) { groups = B.E; per = g13; return true; }
+    if (nmt < 0) {
+      if (!thread_wait_geq(B.s.scan_done, 1 + B.nRP, W)) return false;
+      nmt = *(volatile int*)B.s.n_mtiles;
+    }
+    if (ph == 6) { groups = B.nC; return true; }
+    groups = cdiv(nmt * (ph == 2 ? B.nNdh : B.nNdx), kRasterBlock);
+    per = kRasterBlock;
+    return true;
+  };
   for (;;) {
     __syncthreads();
-    if (threadIdx.x == 0) s_t = atomicAdd(B.s.queue, 1);
+    if (threadIdx.x == 0) {
+      s_t = claim_next(B.s.qctr, 7, c, shape);
+      s_ph = c.phase;
+      s_nmt = nmt;
+    }
     __syncthreads();
-    int t = s_t;
-    if (t == 0) {
+    const int t = s_t, ph = s_ph;
+    if (t < 0) break;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (ph == 0) {
       bwd_setup(B, (int*)smem);
       signal_add(B.s.scan_done, 1);
-      continue;
-    }
-    t -= 1;
-    if (t < B.nRP) {
+    } else if (ph == 1) {
       bwd_rowprep(B, t);
       signal_add(B.s.scan_done, 1);
-      continue;
-    }
-    t -= B.nRP;
-    if (!wait_geq(B.s.scan_done, 1 + B.nRP, W, &s_flag)) break;
-    const int nmt = *(volatile int*)B.s.n_mtiles;
-    if (t < nmt * B.nNdh) {
-      const int tile = t / B.nNdh, nt = t % B.nNdh;
+    } else if (ph == 3 || ph == 5) {
+      // the expert order comes from setup
+      if (!wait_geq(B.s.scan_done, 1 + B.nRP, W, &s_flag)) continue;
+      const int per = ph == 3 ? g2 : g13, nper = ph == 3 ? nper2 : nper13;
+      const int rank = t / per, t0 = (t % per) * kWgradPerTicket;
+      const int t1 = min(nper, t0 + kWgradPerTicket);
+      if (ph == 3) {
+        for (int tt = t0; tt < t1; ++tt) bwd_dw2_tile(B, rank, tt, (bf16_t*)smem);
+      } else {
+        const int e = B.eorder[rank];
+        const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
+        if (wait_geq(&B.s.aux1[e], need, W, &s_flag))
+          for (int tt = t0; tt < t1; ++tt) bwd_dw13_tile(B, rank, tt, (bf16_t*)smem);
+      }
+    } else if (ph == 2) {
+      if (t >= s_nmt * B.nNdh) continue;
+      int tile, nt;
+      raster_decode(B.etile, B.E, B.nNdh, t, tile, nt);
       bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
       signal_add(&B.s.h_cnt[tile], 1);
       signal_add(&B.s.aux1[B.tile_e[tile]], 1);
-      continue;
-    }
-    t -= nmt * B.nNdh;
-    if (t < nW2) {
-      bwd_dw2_tile(B, t, (bf16_t*)smem);
-      continue;
-    }
-    t -= nW2;
-    if (t < nmt * B.nNdx) {
-      const int tile = t / B.nNdx, nt = t % B.nNdx;
+    } else if (ph == 4) {
+      if (t >= s_nmt * B.nNdx) continue;
+      int tile, nt;
+      raster_decode(B.etile, B.E, B.nNdx, t, tile, nt);
       if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
       signal_add(B.s.g2_done, 1);
-      continue;
+    } else {
+      if (wait_geq(B.s.g2_done, s_nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
     }
-    t -= nmt * B.nNdx;
-    if (t < nW13) {
-      const int e = B.eorder[t / nper13];
-      const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
-      if (wait_geq(&B.s.aux1[e], need, W, &s_flag)) bwd_dw13_tile(B, t, (bf16_t*)smem);
-      continue;
-    }
-    t -= nW13;
-    if (t < B.nC) {
-      if (wait_geq(B.s.g2_done, nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
-      continue;
-    }
-    break;
   }
 }
 
@@ -428,6 +465,17 @@ static bool set_smem(K kernel, size_t bytes) {
          hipSuccess;
 }
 
+// Workgroups of a persistent kernel: as many as can be resident at once
+// (more would only queue behind the first wave of workgroups).
+template <class K>
+static int persistent_grid(K kernel, size_t smem, int requested) {
+  if (requested > 0) return requested;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, smem) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return per_cu * num_cus();
+}
+
 static int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -449,7 +497,7 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   }
   if (D->fused) {
     if (!set_smem(k_fused_fwd<Act, TL>, smem)) return MOE_ERR_HIP;
-    const int n_wg = D->n_workgroups > 0 ? D->n_workgroups : num_cus();
+    const int n_wg = persistent_grid(k_fused_fwd<Act, TL>, smem, D->n_workgroups);
     if (n_wg <= 0) return MOE_ERR_HIP;
     hipLaunchKernelGGL((k_fused_fwd<Act, TL>), dim3(n_wg), dim3(256), smem, st, F);
     return launch_status();
@@ -486,13 +534,16 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   B.etile = at<int>(ws, p.o_etile); B.eorder = at<int>(ws, p.o_eorder);
   B.src = at<int>(ws, p.o_src); B.grow = at<float>(ws, p.o_grow);
   B.dab = at<bf16_t>(ws, p.o_dab); B.dxp = at<bf16_t>(ws, p.o_big2); B.dgp = at<float>(ws, p.o_dgp);
+  B.zrow = at<bf16_t>(ws, p.o_zero);
   B.s = make_sync(p, ws, sv->status, D->flags);
   hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, B.s.queue, (int)p.n_ctr);
+  const int nz = (int)(((size_t)2 * p.I + p.d + 256) / 2);
+  hipLaunchKernelGGL(k_zero, dim3(cdiv(nz, 256)), dim3(256), 0, st, at<int>(ws, p.o_zero), nz);
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes;
   if (D->fused) {
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
     if (!set_smem(k_fused_bwd, smem)) return MOE_ERR_HIP;
-    const int n_wg = D->n_workgroups > 0 ? D->n_workgroups : num_cus();
+    const int n_wg = persistent_grid(k_fused_bwd, smem, D->n_workgroups);
     if (n_wg <= 0) return MOE_ERR_HIP;
     hipLaunchKernelGGL(k_fused_bwd, dim3(n_wg), dim3(256), smem, st, B);
     return launch_status();

@@ -35,9 +35,10 @@
 
 namespace moe {
 
-typedef Tile<128, 256> TileDH;  // row tiles: dh, dxp
-typedef Tile<128, 256> TileDW;  // weight-gradient tiles: dw2, dw13
+typedef Tile<128, 128> TileDH;  // row tiles: dh, dxp
+typedef Tile<128, 128> TileDW;  // weight-gradient tiles: dw2, dw13
 constexpr int kRowPrep = 1024;  // rows per rowprep task
+constexpr int kWgradPerTicket = 4;  // weight-gradient tiles per claim
 
 struct Bwd {
   int T, d, E, k, I, R, BM;
@@ -69,6 +70,7 @@ struct Bwd {
   bf16_t* dab;           // [R, 2I]  dA | dB
   bf16_t* dxp;           // [R, d]
   float* dgp;            // [nNdh, R] dgate partial sums
+  const bf16_t* zrow;    // >= 2I + d + 256 zeros: the K tail of weight-gradient tiles
   Sync s;
 };
 
@@ -126,41 +128,39 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
   const bf16_t* W2 = B.w2 + (size_t)e * d * I;
   const int c0 = nt * TL::BN;
   KRows<TL::BM> la;
-  KCols<TL::BN> lb;
-  la.init([&](int r) -> const bf16_t* { return r < n ? B.dy + (size_t)B.src[r0 + r] * d : nullptr; });
+  // rows past n repeat the last row (their outputs are dropped)
+  la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)B.src[r0 + min(r, n - 1)] * d; });
+  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(
-      d / 64, smem, acc, [&](int kt) { la.load(kt); },
-      [&](int kt) {
-        lb.load(kt, [&](int kk) -> const bf16_t* { return W2 + (size_t)kk * I + c0; },
-                [](int) { return 1.0f; });
-      },
-      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  tile_mainloop<TL>(d / 64, smem, acc, la, lb);
 
+  // dA staged in LDS (dB kept in the accumulators), then dB; the dgate
+  // partial sums go through a small LDS area past the staging block
+  typedef Staged<TL::BM, TL::BN> St;
+  static_assert(St::bytes + 2 * TL::BM * sizeof(float) <= TL::smem_bytes, "dh staging fits the tile's LDS");
+  const St st{smem};
+  sred = (float*)(smem + TL::BM * St::LD);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const size_t I2 = 2 * (size_t)I;
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * TL::WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const size_t gr = (size_t)(r0 + min(row, n - 1));
+      const float g = B.grow[gr];
       float part = 0.0f;
-      if (row < n) {
-        const size_t gr = (size_t)(r0 + row);
-        const float g = B.grow[gr];
 #pragma unroll
-        for (int j = 0; j < TL::NJ; ++j) {
-          const int col = c0 + wn * TL::WN + 32 * j + (lane & 31);
-          const size_t o = gr * I + col;
-          const float du = acc[i][j][r];
-          const float av = bf16_to_f32(B.a[o]), bv = bf16_to_f32(B.b[o]), hv = bf16_to_f32(B.h[o]);
-          part = fmaf(du, hv, part);
-          const float dh = g * du;
-          const float sg = sigmoid_f(av);
-          B.dab[gr * I2 + col] = f32_to_bf16(dh * bv * sg * (1.0f + av * (1.0f - sg)));
-          B.dab[gr * I2 + I + col] = f32_to_bf16(dh * av * sg);
-        }
+      for (int j = 0; j < TL::NJ; ++j) {
+        const int col = wn * TL::WN + 32 * j + (lane & 31);
+        const size_t o = gr * I + c0 + col;
+        const float du = acc[i][j][r];
+        const float av = bf16_to_f32(B.a[o]), bv = bf16_to_f32(B.b[o]), hv = bf16_to_f32(B.h[o]);
+        part = fmaf(du, hv, part);
+        const float dh = g * du;
+        const float sg = sigmoid_f(av);
+        st.put(row, col, dh * bv * sg * (1.0f + av * (1.0f - sg)));
+        acc[i][j][r] = dh * av * sg;
       }
       // sum over the 32 lanes holding this row's columns (fixed tree)
 #pragma unroll
@@ -168,11 +168,15 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
       if ((lane & 31) == 0) sred[wn * TL::BM + row] = part;
     }
   }
-  __syncthreads();
+  const size_t I2 = 2 * (size_t)I;
+  st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + c0; });
   if (threadIdx.x < TL::BM && (int)threadIdx.x < n) {
     const int row = threadIdx.x;
     B.dgp[(size_t)nt * B.R + r0 + row] = sred[row] + sred[TL::BM + row];
   }
+  __syncthreads();
+  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
+  st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + I + c0; });
 }
 
 // ---------------------------------------------------------------- dxp
@@ -185,85 +189,69 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const bf16_t* W3 = B.w3 + (size_t)e * I * d;
   const int c0 = nt * TL::BN;
   KRows<TL::BM> la;
-  KCols<TL::BN> lb;
-  la.init([&](int r) -> const bf16_t* { return r < n ? B.dab + (size_t)(r0 + r) * 2 * I : nullptr; });
-  f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(
-      2 * I / 64, smem, acc, [&](int kt) { la.load(kt); },
-      [&](int kt) {
-        lb.load(kt, [&](int kk) -> const bf16_t* {
-          return (kk < I ? W1 + (size_t)kk * d : W3 + (size_t)(kk - I) * d) + c0;
-        }, [](int) { return 1.0f; });
-      },
-      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
-  tile_visit<TL>(acc, [&](int row, int col, float v) {
-    if (row < n) B.dxp[(size_t)(r0 + row) * d + c0 + col] = f32_to_bf16(v);
+  la.init([&](int r) -> const bf16_t* { return B.dab + (size_t)(r0 + min(r, n - 1)) * 2 * I; });
+  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* {
+    return (kk < I ? W1 + (size_t)kk * d : W3 + (size_t)(kk - I) * d) + c0;
   });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(2 * I / 64, smem, acc, la, lb);
+  const Staged<TL::BM, TL::BN> st{smem};
+  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
+  st.flush(n, [&](int row) { return B.dxp + (size_t)(r0 + row) * d + c0; });
 }
 
 // ---------------------------------------------------------------- dw2
-// dW2_e[n0 .. +128, i0 .. +256] = sum over the expert's rows r of
+// dW2_e[n0 .. +128, i0 .. +128] = sum over the expert's rows r of
 // g_r G[r, n] H[r, i]; K = the expert's rows (zero rows give zeros).
-__device__ void bwd_dw2_tile(const Bwd& B, int q, bf16_t* smem) {
+__device__ void bwd_dw2_tile(const Bwd& B, int rank, int tt, bf16_t* smem) {
   typedef TileDW TL;
-  const int nper = B.nW2m * B.nW2n;
-  const int e = B.eorder[q / nper], tt = q % nper;
+  const int e = B.eorder[rank];
   const int n0 = (tt / B.nW2n) * TL::BM, i0 = (tt % B.nW2n) * TL::BN;
   const int d = B.d, I = B.I;
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
-  KCols<TL::BM> la;
-  KCols<TL::BN> lb;
-  f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(
-      cdiv(M, 64), smem, acc,
-      [&](int kt) {
-        la.load(kt, [&](int kk) -> const bf16_t* {
-          return kk < M ? B.dy + (size_t)B.src[off + kk] * d + n0 : nullptr;
-        }, [&](int kk) { return B.grow[off + kk]; });
+  // k past the expert's rows reads the zero row; the index loads are
+  // clamped so they stay inside the expert
+  auto la = kcols_scaled<TL::BM>(
+      [&](int kk) -> const bf16_t* {
+        const bf16_t* q = B.dy + (size_t)B.src[off + min(kk, M - 1)] * d + n0;
+        return kk < M ? q : B.zrow;
       },
-      [&](int kt) {
-        lb.load(kt, [&](int kk) -> const bf16_t* {
-          return kk < M ? B.h + (size_t)(off + kk) * I + i0 : nullptr;
-        }, [](int) { return 1.0f; });
-      },
-      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
-  bf16_t* out = B.dw2 + (size_t)e * d * I;
-  tile_visit<TL>(acc, [&](int row, int col, float v) {
-    out[(size_t)(n0 + row) * I + i0 + col] = f32_to_bf16(v);
+      [&](int kk) { return B.grow[off + min(kk, M - 1)]; });
+  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* {
+    return kk < M ? B.h + (size_t)(off + kk) * I + i0 : B.zrow;
   });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(cdiv(M, 64), smem, acc, la, lb);
+  bf16_t* out = B.dw2 + (size_t)e * d * I;
+  const Staged<TL::BM, TL::BN> st{smem};
+  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
+  st.flush(TL::BM, [&](int row) { return out + (size_t)(n0 + row) * I + i0; });
 }
 
 // ---------------------------------------------------------------- dw13
 // Rows 0..63 of the tile are dW1_e[i0 ..], rows 64..127 dW3_e[i0 ..]:
 // both share the gathered X operand.
-__device__ void bwd_dw13_tile(const Bwd& B, int q, bf16_t* smem) {
+__device__ void bwd_dw13_tile(const Bwd& B, int rank, int tt, bf16_t* smem) {
   typedef TileDW TL;
-  const int nper = B.nW13m * B.nW13n;
-  const int e = B.eorder[q / nper], tt = q % nper;
+  const int e = B.eorder[rank];
   const int i0 = (tt / B.nW13n) * (TL::BM / 2), c0 = (tt % B.nW13n) * TL::BN;
   const int d = B.d, I = B.I;
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
-  KCols<TL::BM> la;
-  KCols<TL::BN> lb;
+  auto la = kcols<TL::BM>(
+      [&](int kk) -> const bf16_t* { return kk < M ? B.dab + (size_t)(off + kk) * 2 * I + i0 : B.zrow; },
+      I - TL::BM / 2);
+  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* {
+    const bf16_t* q = B.x + (size_t)B.src[off + min(kk, M - 1)] * d + c0;
+    return kk < M ? q : B.zrow;
+  });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(
-      cdiv(M, 64), smem, acc,
-      [&](int kt) {
-        la.load(kt, [&](int kk) -> const bf16_t* {
-          return kk < M ? B.dab + (size_t)(off + kk) * 2 * I + i0 : nullptr;
-        }, [](int) { return 1.0f; }, I - TL::BM / 2);
-      },
-      [&](int kt) {
-        lb.load(kt, [&](int kk) -> const bf16_t* {
-          return kk < M ? B.x + (size_t)B.src[off + kk] * d + c0 : nullptr;
-        }, [](int) { return 1.0f; });
-      },
-      [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  tile_mainloop<TL>(cdiv(M, 64), smem, acc, la, lb);
   bf16_t* o1 = B.dw1 + (size_t)e * I * d;
   bf16_t* o3 = B.dw3 + (size_t)e * I * d;
-  tile_visit<TL>(acc, [&](int row, int col, float v) {
-    bf16_t* o = row < TL::BM / 2 ? o1 + (size_t)(i0 + row) * d : o3 + (size_t)(i0 + row - TL::BM / 2) * d;
-    o[c0 + col] = f32_to_bf16(v);
+  const Staged<TL::BM, TL::BN> st{smem};
+  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
+  st.flush(TL::BM, [&](int row) {
+    return (row < TL::BM / 2 ? o1 + (size_t)(i0 + row) * d : o3 + (size_t)(i0 + row - TL::BM / 2) * d) + c0;
   });
 }
 

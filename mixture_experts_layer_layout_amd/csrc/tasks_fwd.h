@@ -32,11 +32,12 @@ constexpr int kCombTok = 8;    // tokens per combine task
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 
-typedef Tile<128, 256> TileB128;
-typedef Tile<256, 256> TileB256;
+typedef Tile<128, 128> TileB128;  // 64 KB of LDS: two workgroups per CU
+typedef Tile<256, 128> TileB256;
 
 struct Sync {
-  int* queue;
+  int* queue;    // start of the counter region
+  int* qctr;     // phase queues [kMaxPhases][8]
   int* abort;
   int* r2_done;
   int* scan_done;
@@ -75,6 +76,7 @@ struct Fwd {
   int* tile_e;       // [max_tiles]
   int* tile_r0;
   int* tile_n;
+  int* etile;        // [E+1] first row tile of each expert (+ the total)
   int* perm;         // [R]
   int* inv;          // [R]
   int* src;          // [R]
@@ -190,14 +192,14 @@ __device__ __forceinline__ void wave_topk_gates(const float* row, int E, int k, 
   sel_g = g;
 }
 
-constexpr int kTopkChunk = 16;  // tokens whose logits are staged in LDS at once
+constexpr int kTopkChunk = 8;   // tokens whose logits are staged in LDS at once
 // LDS of router_topk: block masks (kMaxE u64) + a chunk of logits
 constexpr size_t kTopkSmem = kMaxE * 8 + (size_t)kTopkChunk * kMaxE * 4;
 
 // Sums the slices, adds the bias, selects, writes idx/gates and the block's
-// expert bitmasks.  The logits of 16 tokens at a time are summed into LDS by
+// expert bitmasks.  The logits of 8 tokens at a time are summed into LDS by
 // the whole workgroup (coalesced, independent loads), then each wave selects
-// for 4 of them.  With S == 1 and lpart == the caller's logits this is also
+// for 2 of them.  With S == 1 and lpart == the caller's logits this is also
 // the standalone route step.
 template <bool MASKS>
 __device__ void router_topk(const Fwd& F, int b, char* smem) {
@@ -320,6 +322,7 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   for (int e = threadIdx.x; e < F.E; e += kThreads) {
     const int off = scnt[e];
     F.offsets[e] = off;
+    F.etile[e] = stile[e];
     int run = off;
     for (int b = 0; b < F.nb; ++b) {
       F.bbase[(size_t)b * F.E + e] = run;
@@ -334,6 +337,7 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   }
   if (threadIdx.x == 0) {
     F.offsets[F.E] = R;
+    F.etile[F.E] = ntiles;
     *F.s.n_mtiles = ntiles;
   }
 }
@@ -415,12 +419,13 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const int c0 = nt * (TL::BN / 2);
   KRows<TL::BM> la;
   KRows<TL::BN> lb;
+  // rows past the tile's n repeat its last row (their outputs are dropped)
   if (F.direct) {
     const bf16_t* X = (const bf16_t*)F.x;
-    la.init([&](int r) -> const bf16_t* { return r < n ? X + (size_t)F.src[r0 + r] * d : nullptr; });
+    la.init([&](int r) -> const bf16_t* { return X + (size_t)F.src[r0 + min(r, n - 1)] * d; });
   } else {
     const bf16_t* XP = (const bf16_t*)F.xp;
-    la.init([&](int r) -> const bf16_t* { return r < n ? XP + (size_t)(r0 + r) * d : nullptr; });
+    la.init([&](int r) -> const bf16_t* { return XP + (size_t)(r0 + min(r, n - 1)) * d; });
   }
   lb.init([&](int nr) -> const bf16_t* {
     int which, col;
@@ -428,19 +433,26 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
     return (which ? W3 : W1) + (size_t)(c0 + col) * d;
   });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(d / 64, smem, acc, [&](int kt) { la.load(kt); }, [&](int kt) { lb.load(kt); },
-                    [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  tile_mainloop<TL>(d / 64, smem, acc, la, lb);
+  // H (then the saved pre-activations) staged in LDS, stored 16 bytes a lane
+  typedef Staged<TL::BM, TL::BN / 2> St;
+  static_assert(St::bytes <= TL::smem_bytes, "SwiGLU staging fits the tile's LDS");
   bf16_t* H = (bf16_t*)F.h;
   bf16_t* A = (bf16_t*)F.a;
   bf16_t* B = (bf16_t*)F.b;
-  tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float bv) {
-    if (row < n) {
-      const size_t o = (size_t)(r0 + row) * I + c0 + col;
-      H[o] = f32_to_bf16(silu_f(av) * bv);
-      if (A) A[o] = f32_to_bf16(av);
-      if (B) B[o] = f32_to_bf16(bv);
-    }
-  });
+  const St st{smem};
+  tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float bv) { st.put(row, col, silu_f(av) * bv); });
+  st.flush(n, [&](int row) { return H + (size_t)(r0 + row) * I + c0; });
+  if (A) {
+    __syncthreads();
+    tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float) { st.put(row, col, av); });
+    st.flush(n, [&](int row) { return A + (size_t)(r0 + row) * I + c0; });
+  }
+  if (B) {
+    __syncthreads();
+    tile_visit_pairs<TL>(acc, [&](int row, int col, float, float bv) { st.put(row, col, bv); });
+    st.flush(n, [&](int row) { return B + (size_t)(r0 + row) * I + c0; });
+  }
 }
 
 template <class TL>
@@ -452,15 +464,14 @@ __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const int c0 = nt * TL::BN;
   KRows<TL::BM> la;
   KRows<TL::BN> lb;
-  la.init([&](int r) -> const bf16_t* { return r < n ? H + (size_t)(r0 + r) * I : nullptr; });
+  la.init([&](int r) -> const bf16_t* { return H + (size_t)(r0 + min(r, n - 1)) * I; });
   lb.init([&](int nr) -> const bf16_t* { return W2 + (size_t)(c0 + nr) * I; });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(I / 64, smem, acc, [&](int kt) { la.load(kt); }, [&](int kt) { lb.load(kt); },
-                    [&](bf16_t* p) { la.store(p); }, [&](bf16_t* p) { lb.store(p); });
+  tile_mainloop<TL>(I / 64, smem, acc, la, lb);
   bf16_t* YP = (bf16_t*)F.yp;
-  tile_visit<TL>(acc, [&](int row, int col, float v) {
-    if (row < n) YP[(size_t)(r0 + row) * d + c0 + col] = f32_to_bf16(v);
-  });
+  const Staged<TL::BM, TL::BN> st{smem};
+  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
+  st.flush(n, [&](int row) { return YP + (size_t)(r0 + row) * d + c0; });
 }
 
 __device__ void g1_tile_f32(const Fwd& F, int tile, int nt, float* smem) {

@@ -1,0 +1,103 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/moe.h declares, and its host-side paths (workspace sizing,
+descriptor validation, status strings) behave as the header states.  No
+call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "mixture_experts_layer_layout_amd", "lib", "libmoe.so")
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from mixture_experts_layer_layout_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared_entry_points()
+    for n in ("moe_route", "moe_layout", "moe_forward", "moe_backward", "moe_workspace_size",
+              "moe_status_string", "moe_gather"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_entry_points()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/moe.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    # nothing else of the library is exported
+    assert {e for e in exported if e.startswith("moe_")} == set(names)
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "E", "k", "I", "act_dtype", "expert_dtype",
+                                              "score", "renorm", "fused", "stage_rows",
+                                              "n_workgroups")] + [("flags", ctypes.c_uint32)]
+
+
+def _desc(**kw):
+    base = dict(T=4096, d=7168, E=256, k=8, I=2048, act_dtype=1, expert_dtype=1, score=1, renorm=1,
+                fused=1, stage_rows=0, n_workgroups=0, flags=0)
+    base.update(kw)
+    return Desc(**base)
+
+
+def test_workspace_size_and_validation(lib):
+    lib.moe_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(_desc()), ctypes.byref(n)) == 0
+    # at least the staged rows, dA|dB and the router partial sums
+    R = 4096 * 8
+    assert n.value > R * 7168 * 2 + R * 2 * 2048 * 2
+    small = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(_desc(T=64, d=256, E=8, k=2, I=128)), ctypes.byref(small)) == 0
+    assert 0 < small.value < n.value
+    # invalid descriptors: k > E, k = 0, E too large, bad dtype, bf16 d not a multiple of 256
+    for bad, code in ((dict(k=9, E=8), -1), (dict(k=0), -1), (dict(E=5000), -1), (dict(act_dtype=7), -1),
+                      (dict(d=7000), -2), (dict(stage_rows=64), -2), (dict(act_dtype=0, expert_dtype=1), -2)):
+        assert lib.moe_workspace_size(ctypes.byref(_desc(**bad)), ctypes.byref(n)) == code, bad
+    assert lib.moe_workspace_size(None, ctypes.byref(n)) == -1
+    assert lib.moe_workspace_size(ctypes.byref(_desc()), None) == -1
+
+
+def test_entry_points_reject_bad_arguments_before_launching(lib):
+    vp = ctypes.c_void_p
+    lib.moe_route.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp]
+    lib.moe_layout.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_forward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    d = _desc(T=64, d=256, E=8, k=2, I=128)
+    assert lib.moe_route(ctypes.byref(_desc(k=9, E=8)), None, None, None, None, None) == -1
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, None) == -1
+    assert lib.moe_layout(ctypes.byref(d), None, None, None, None, None, None, None, 0, None) == -1
+    # a missing weights struct, then a missing workspace
+    assert lib.moe_forward(ctypes.byref(d), None, None, None, None, None, None, None, 0, None) == -1
+    # the backward is bf16 only
+    assert lib.moe_backward(ctypes.byref(_desc(T=64, d=256, E=8, k=2, I=128, act_dtype=0, expert_dtype=0)),
+                            None, None, None, None, None, None, None, None, None, None, 0, None) == -2
+
+
+def test_status_strings(lib):
+    lib.moe_status_string.restype = ctypes.c_char_p
+    for code in range(0, -7, -1):
+        s = lib.moe_status_string(code).decode()
+        assert s.startswith("MOE_")
+    assert "unknown" in lib.moe_status_string(-99).decode()
