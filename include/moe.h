@@ -96,6 +96,12 @@ typedef struct moe_desc {
 #define MOE_FLAG_DIRECT_PULL 0x1u  /* fused bf16 forward: the up-projection
                                       reads token rows from X through the
                                       layout instead of a staged copy       */
+#define MOE_FLAG_PERSISTENT_SPLIT 0x2u /* fused = 1: run the persistent
+                                      scheduler as one launch per phase
+                                      group instead of one launch for all */
+#define MOE_FLAG_PERSISTENT_WGRAD_APART 0x4u /* fused backward: the weight
+                                      gradients in a second persistent
+                                      launch after the rest              */
 #define MOE_FLAG_SPIN_LIMIT_TINY 0x100u /* test only: bounded waits give up
                                       after a few polls (exercises the
                                       MOE_ERR_TIMEOUT path)                 */

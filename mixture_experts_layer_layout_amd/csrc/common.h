@@ -58,20 +58,30 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 }
 
 // ---------------------------------------------------------------- waits
-// A bounded wait on a device counter.  Thread 0 of the workgroup polls with
-// agent-scope acquire loads; the whole workgroup then proceeds or, when the
-// bound expires or another workgroup has aborted, records MOE_ERR_TIMEOUT
-// and returns false.  `abort` is a workspace word every wait also watches,
-// so one expired wait drains the whole grid instead of hanging it.
+// Producer -> consumer hand-off between workgroups, possibly on different
+// XCDs (each XCD has its own, non-coherent L2):
+//   producer  every wave waits for its stores to reach the L2, then one
+//             wave writes the XCD's L2 back (agent-scope release) and bumps
+//             the counter
+//   consumer  thread 0 polls the counter with relaxed agent-scope atomic
+//             loads (coherent, no cache maintenance) and the workgroup
+//             proceeds behind a workgroup-scope acquire
+// The consumer invalidates no cache: every exchanged buffer in the
+// workspace is written once per launch and read only after its counter
+// shows it complete, so no L1 or L2 can hold an older copy of it from this
+// launch, and the dispatch's own acquire leaves none from earlier launches.
+// (An agent-scope acquire would invalidate the whole XCD's L2 every time,
+// destroying the reuse of the operand rows other workgroups share there.)
+// Every wait is bounded: when the bound expires, or another workgroup has
+// aborted, it records MOE_ERR_TIMEOUT and returns false; `abort` is a
+// workspace word every wait also watches, so one expired wait drains the
+// whole grid instead of hanging it.
 struct WaitCtx {
   int* abort;
   int32_t* status;
   long long spin_limit;
 };
 
-__device__ __forceinline__ int load_acquire(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ int load_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -80,37 +90,40 @@ __device__ __forceinline__ void set_status(int32_t* status, int code) {
   if (status) atomicCAS((int*)status, 0, code);
 }
 
-// Returns true when *ctr >= target; false on timeout/abort.  Block-uniform.
-__device__ __forceinline__ bool wait_geq(const int* ctr, int target, const WaitCtx& w,
-                                         int* lds_flag) {
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    long long spins = 0;
-    while (load_acquire(ctr) < target) {
-      if (load_relaxed(w.abort)) { ok = 0; break; }
-      if (++spins > w.spin_limit) {
-        set_status(w.status, MOE_ERR_TIMEOUT);
-        __hip_atomic_store(w.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+// Thread 0 only: true when *ctr >= target; false on timeout/abort.
+__device__ __forceinline__ bool thread_wait_geq(const int* ctr, int target, const WaitCtx& w) {
+  long long spins = 0;
+  while (load_relaxed(ctr) < target) {
+    if (load_relaxed(w.abort)) return false;
+    if (++spins > w.spin_limit) {
+      set_status(w.status, MOE_ERR_TIMEOUT);
+      __hip_atomic_store(w.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
     }
-    *lds_flag = ok;
+    __builtin_amdgcn_s_sleep(2);
   }
+  return true;
+}
+
+// Block-uniform: true when *ctr >= target; false on timeout/abort.
+__device__ __forceinline__ bool wait_geq(const int* ctr, int target, const WaitCtx& w, int* lds_flag) {
+  if (threadIdx.x == 0) *lds_flag = thread_wait_geq(ctr, target, w) ? 1 : 0;
   __syncthreads();
-  int ok = *lds_flag;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int ok = *lds_flag;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   __syncthreads();
   return ok != 0;
 }
 
-// Makes every prior global store of the workgroup visible at agent scope,
-// then adds `v` to *ctr.  Block-uniform call.
+// Block-uniform: publishes every prior global store of the workgroup at
+// agent scope, then adds `v` to *ctr.
 __device__ __forceinline__ void signal_add(int* ctr, int v) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------- misc

@@ -86,8 +86,9 @@ struct KRows {
 // contiguous within each stored row.  Thread t covers k-group t % KG (KK
 // consecutive k) and tile rows 8*(t/KG) .. +7, with KK = 8 for 256-row
 // tiles and 4 for 128-row tiles, so all 256 threads take part.
-//   kptr(k)   pointer to the stored row holding k, at the tile's first row;
-//             never null (k past the operand -> a zero row)
+//   kptr(k, c) pointer to the stored row holding k, at the tile's first
+//             row; never null (k past the operand -> a zero row).  c is the
+//             column tile of a stream (tile_stream), 0 otherwise
 //   kscale(k) factor for that stored row (SCALED only)
 //   half_off  extra element offset for the second half of the tile's rows
 //             (two column ranges of one stored row, e.g. the dA and dB
@@ -100,6 +101,7 @@ struct KCols {
   P kptr;
   S kscale;
   int coff;
+  int nk_ = 0;  // stages per column tile when streamed (tile_stream), else 0
   const bf16_t* p[KK];
   float s[KK], sl[2][KK];
   uint4 v[2][KK];
@@ -108,10 +110,11 @@ struct KCols {
     coff = nb * 8 + (nb >= ROWS / 16 ? half_off : 0);
   }
   __device__ __forceinline__ void prep(int kt) {
-    const int k0 = kt * 64 + (threadIdx.x % KG) * KK;
+    const int c = nk_ ? kt / nk_ : 0;
+    const int k0 = (kt - c * nk_) * 64 + (threadIdx.x % KG) * KK;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      p[kk] = kptr(k0 + kk);
+      p[kk] = kptr(k0 + kk, c);
       if (SCALED) s[kk] = kscale(k0 + kk);
     }
   }
@@ -310,6 +313,98 @@ __device__ __forceinline__ void tile_visit_pairs(const f32x16_t (&acc)[TL::MI][T
         const int row = wm * TL::WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int col = wn * (TL::WN / 2) + 32 * j + (lane & 31);
         f(row, col, acc[i][j][r], acc[i][j + H][r]);
+      }
+}
+
+// ---------------------------------------------------------------- stream
+// nc output tiles that share their A rows, each over nk K-stages, run as one
+// stream of nc * nk steps (step j = column tile j / nk, stage j % nk): the
+// two-stage prefetch runs across tile boundaries, so the next tile's loads
+// overlap this tile's MFMAs and stores.  After the last stage of column tile
+// c, epi(c, acc) writes the tile and the accumulators restart from zero.
+// The loaders' prep(j) must map the step to (c, stage) (KCols::nk_).
+template <int CUR, class TL, class LA, class LB, class EPI>
+__device__ __forceinline__ void stream_step(int j, int nk, int last, bf16_t* As, bf16_t* Bs,
+                                            f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B, EPI& epi) {
+  A.template load<CUR>(min(j + 2, last));
+  B.template load<CUR>(min(j + 2, last));
+  A.prep(min(j + 3, last));
+  B.prep(min(j + 3, last));
+  __builtin_amdgcn_sched_barrier(0);
+  tile_compute<TL>(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  A.template store<CUR ^ 1>(As + (CUR ^ 1) * TL::LDS_A);
+  B.template store<CUR ^ 1>(Bs + (CUR ^ 1) * TL::LDS_B);
+  if ((j + 1) % nk == 0) {
+    epi(j / nk, acc);
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TL::NJ; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+  }
+  __syncthreads();
+}
+
+template <class TL, class LA, class LB, class EPI>
+__device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A, LB& B, EPI epi) {
+  f32x16_t acc[TL::MI][TL::NJ];
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int total = nc * nk;
+  if (total <= 0) return;
+  const int last = total - 1;
+  bf16_t* As = smem;
+  bf16_t* Bs = smem + 2 * TL::LDS_A;
+  A.prep(0);
+  B.prep(0);
+  A.template load<0>(0);
+  B.template load<0>(0);
+  A.prep(min(1, last));
+  B.prep(min(1, last));
+  A.template load<1>(min(1, last));
+  B.template load<1>(min(1, last));
+  A.prep(min(2, last));
+  B.prep(min(2, last));
+  __syncthreads();
+  A.template store<0>(As);
+  B.template store<0>(Bs);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < total; j += 2) {
+    stream_step<0, TL>(j, nk, last, As, Bs, acc, A, B, epi);
+    stream_step<1, TL>(j + 1, nk, last, As, Bs, acc, A, B, epi);
+  }
+  if (j < total) stream_step<0, TL>(j, nk, last, As, Bs, acc, A, B, epi);
+}
+
+// Writes the accumulators as bf16 straight from registers, two columns per
+// 4-byte store: lane pairs swap values so the even lane of a pair stores
+// (row of r, its two columns) and the odd lane (row of r+1, the same two
+// columns).  dst(row) points at the tile's first column of that output row.
+template <class TL, class D>
+__device__ __forceinline__ void tile_store_pairs(const f32x16_t (&acc)[TL::MI][TL::NJ], int nrows, D dst) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+        const float o0 = __shfl_xor(v0, 1), o1 = __shfl_xor(v1, 1);
+        const int rr = odd ? r + 1 : r;
+        const int row = wm * TL::WM + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const int col = wn * TL::WN + 32 * j + (lane & 31 & ~1);
+        const uint32_t w = odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0);
+        if (row < nrows) *(uint32_t*)(dst(row) + col) = w;
       }
 }
 

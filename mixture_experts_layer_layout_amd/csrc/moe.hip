@@ -97,6 +97,7 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
   if (p->bwd_ok) {
+    p->o_gg = take(R * d * 2);
     p->o_zero = take(((size_t)2 * I + d + 256) * 2);
     p->o_dab = take(R * 2 * I * 2);
     p->o_dgp = take((size_t)p->nNdh * R * 4);
@@ -247,67 +248,73 @@ __global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F,
 // the per-XCD phase queues (sched.h); the projection tiles are enumerated
 // in the grouped raster, 64 consecutive tasks per XCD queue block.  Each
 // task waits on the counters its inputs raise.
-template <class Act, class TL>
+template <class Act, class TL, unsigned MASK>
 __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int s_t, s_ph, s_nmt, s_flag;
-  const WaitCtx W = wctx(F.s);
-  Claim c;
-  c.own = xcc_id();
-  int nmt = -1;  // thread 0: row tiles, known once the layout is done
-  auto shape = [&](int ph, int& groups, int& per) -> bool {
-    per = 1;
-    if (ph == 0) { groups = F.nb * F.S; return true; }
-    if (ph == 1) { groups = F.nb; return true; }
-    if (ph == 2) { groups = 1; return true; }
-    if (nmt < 0) {
-      if (!thread_wait_geq(F.s.scan_done, 1, W)) return false;
-      nmt = *(volatile int*)F.s.n_mtiles;
-    }
-    if (ph == 3) { groups = nmt; return true; }
-    if (ph == 6) { groups = F.nC; return true; }
-    groups = cdiv(nmt * (ph == 4 ? F.nN1 : F.nN2), kRasterBlock);
-    per = kRasterBlock;
-    return true;
-  };
+  __shared__ Claim c;
+  __shared__ int s_flag;
+  if (threadIdx.x == 0) {
+    c.phase = 0;
+    c.qoff = 0;
+    c.own = xcc_id();
+    c.nmt = -1;
+  }
   for (;;) {
     __syncthreads();
     if (threadIdx.x == 0) {
-      s_t = claim_next(F.s.qctr, 7, c, shape);
-      s_ph = c.phase;
-      s_nmt = nmt;
+      const WaitCtx W = wctx(F.s);
+      auto shape = [&](int ph, int& groups, int& per) -> bool {
+        per = 1;
+        groups = 0;
+        if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
+        if (ph == 0) { groups = F.nb * F.S; return true; }
+        if (ph == 1) { groups = F.nb; return true; }
+        if (ph == 2) { groups = 1; return true; }
+        if (c.nmt < 0) {
+          if (!thread_wait_geq(F.s.scan_done, 1, W)) return false;
+          c.nmt = load_relaxed(F.s.n_mtiles);
+        }
+        if (ph == 3) { groups = c.nmt; return true; }
+        if (ph == 6) { groups = F.nC; return true; }
+        groups = cdiv(c.nmt * (ph == 4 ? F.nN1 : F.nN2), kRasterBlock);
+        per = kRasterBlock;
+        return true;
+      };
+      c.task = claim_next(F.s.qctr, 7, c, shape);
     }
     __syncthreads();
-    const int t = s_t, ph = s_ph;
+    const int t = c.task, ph = c.phase;
     if (t < 0) break;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (ph == 0) {
+    const WaitCtx W = wctx(F.s);
+    const int s_nmt = c.nmt;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if ((MASK & 1u) && ph == 0) {
       router_partial<Act>(F, t);
       signal_add(&F.s.r1_cnt[t / F.S], 1);
-    } else if (ph == 1) {
+    } else if ((MASK & 2u) && ph == 1) {
       if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
       signal_add(F.s.r2_done, 1);
-    } else if (ph == 2) {
+    } else if ((MASK & 4u) && ph == 2) {
       if (wait_geq(F.s.r2_done, F.nb, W, &s_flag)) layout_scan(F, (int*)smem);
       signal_add(F.s.scan_done, 1);
-    } else if (ph == 3) {
+    } else if ((MASK & 8u) && ph == 3) {
       if (F.direct)
         gather_tile<Act, false>(F, t, (int*)smem);
       else
         gather_tile<Act, true>(F, t, (int*)smem);
-    } else if (ph == 4) {
+    } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * F.nN1) continue;
       int tile, nt;
       raster_decode(F.etile, F.E, F.nN1, t, tile, nt);
       if (wait_geq(&F.s.ready[tile], 1, W, &s_flag)) run_g1<Act, TL>(F, tile, nt, smem);
       signal_add(&F.s.h_cnt[tile], 1);
-    } else if (ph == 5) {
+    } else if ((MASK & 32u) && ph == 5) {
       if (t >= s_nmt * F.nN2) continue;
       int tile, nt;
       raster_decode(F.etile, F.E, F.nN2, t, tile, nt);
       if (wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) run_g2<Act, TL>(F, tile, nt, smem);
       signal_add(F.s.g2_done, 1);
-    } else {
+    } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
     }
   }
@@ -355,14 +362,14 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dxp(Bwd B) {
 __global__ void __launch_bounds__(256, 2) k_bwd_dw2(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   // dispatch order (heaviest experts first) spread round-robin over the XCDs
-  const int nper = B.nW2m * B.nW2n;
-  bwd_dw2_tile(B, blockIdx.x / nper, blockIdx.x % nper, (bf16_t*)smem);
+  const int per = B.nW2m * cdiv(B.nW2n, kWgradPerTicket);
+  bwd_dw2_band(B, blockIdx.x / per, blockIdx.x % per, (bf16_t*)smem);
 }
 
 __global__ void __launch_bounds__(256, 2) k_bwd_dw13(Bwd B) {
   extern __shared__ __align__(16) char smem[];
-  const int nper = B.nW13m * B.nW13n;
-  bwd_dw13_tile(B, blockIdx.x / nper, blockIdx.x % nper, (bf16_t*)smem);
+  const int per = B.nW13m * cdiv(B.nW13n, kWgradPerTicket);
+  bwd_dw13_band(B, blockIdx.x / per, blockIdx.x % per, (bf16_t*)smem);
 }
 
 __global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockIdx.x); }
@@ -370,76 +377,84 @@ __global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockI
 // The persistent backward: phases setup | rowprep | dh | dw2 | dxp | dw13
 // | dx through the per-XCD phase queues (dh and dxp tiles in the grouped
 // raster, 64 per queue block; the weight-gradient tiles of the expert of
-// load rank q -> queue q % 8, kWgradPerTicket tiles per claim).
-__global__ void __launch_bounds__(256, 1) k_fused_bwd(Bwd B) {
+// load rank q -> queue q % 8, one band of kWgradPerTicket column tiles per
+// claim).
+template <unsigned MASK>
+__global__ void __launch_bounds__(256, (MASK & 0x28u) == MASK || (MASK & 0x14u) == MASK ? 2 : 1)
+    k_fused_bwd(Bwd B) {
   extern __shared__ __align__(16) char smem[];
-  __shared__ int s_t, s_ph, s_nmt, s_flag;
-  const WaitCtx W = wctx(B.s);
-  const int nper2 = B.nW2m * B.nW2n, nper13 = B.nW13m * B.nW13n;
-  const int g2 = cdiv(nper2, kWgradPerTicket), g13 = cdiv(nper13, kWgradPerTicket);
-  Claim c;
-  c.own = xcc_id();
-  int nmt = -1;
-  auto shape = [&](int ph, int& groups, int& per) -> bool {
-    per = 1;
-    if (ph == 0) { groups = 1; return true; }
-    if (ph == 1) { groups = B.nRP; return true; }
-    if (ph == 3) { groups = B.E; per = g2; return true; }
-    if (ph == 5) { groups = B.E; per = g13; return true; }
-    if (nmt < 0) {
-      if (!thread_wait_geq(B.s.scan_done, 1 + B.nRP, W)) return false;
-      nmt = *(volatile int*)B.s.n_mtiles;
-    }
-    if (ph == 6) { groups = B.nC; return true; }
-    groups = cdiv(nmt * (ph == 2 ? B.nNdh : B.nNdx), kRasterBlock);
-    per = kRasterBlock;
-    return true;
-  };
+  __shared__ Claim c;
+  __shared__ int s_flag;
+  if (threadIdx.x == 0) {
+    c.phase = 0;
+    c.qoff = 0;
+    c.own = xcc_id();
+    c.nmt = -1;
+  }
   for (;;) {
     __syncthreads();
     if (threadIdx.x == 0) {
-      s_t = claim_next(B.s.qctr, 7, c, shape);
-      s_ph = c.phase;
-      s_nmt = nmt;
+      const WaitCtx W = wctx(B.s);
+      const int g2 = B.nW2m * cdiv(B.nW2n, kWgradPerTicket), g13 = B.nW13m * cdiv(B.nW13n, kWgradPerTicket);
+      auto shape = [&](int ph, int& groups, int& per) -> bool {
+        per = 1;
+        groups = 0;
+        if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
+        if (ph == 0) { groups = 1; return true; }
+        if (ph == 1) { groups = B.nRP; return true; }
+        if (ph == 3) { groups = B.E; per = g2; return true; }
+        if (ph == 5) { groups = B.E; per = g13; return true; }
+        if (c.nmt < 0) {
+          if (!thread_wait_geq(B.s.scan_done, 1 + B.nRP, W)) return false;
+          c.nmt = load_relaxed(B.s.n_mtiles);
+        }
+        if (ph == 6) { groups = B.nC; return true; }
+        groups = cdiv(c.nmt * (ph == 2 ? B.nNdh : B.nNdx), kRasterBlock);
+        per = kRasterBlock;
+        return true;
+      };
+      c.task = claim_next(B.s.qctr, 7, c, shape);
     }
     __syncthreads();
-    const int t = s_t, ph = s_ph;
+    const int t = c.task, ph = c.phase;
     if (t < 0) break;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (ph == 0) {
+    const WaitCtx W = wctx(B.s);
+    const int s_nmt = c.nmt;
+    const int g2 = B.nW2m * cdiv(B.nW2n, kWgradPerTicket), g13 = B.nW13m * cdiv(B.nW13n, kWgradPerTicket);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if ((MASK & 1u) && ph == 0) {
       bwd_setup(B, (int*)smem);
       signal_add(B.s.scan_done, 1);
-    } else if (ph == 1) {
+    } else if ((MASK & 2u) && ph == 1) {
       bwd_rowprep(B, t);
       signal_add(B.s.scan_done, 1);
-    } else if (ph == 3 || ph == 5) {
+    } else if ((MASK & 0x28u) && (ph == 3 || ph == 5)) {
       // the expert order comes from setup
       if (!wait_geq(B.s.scan_done, 1 + B.nRP, W, &s_flag)) continue;
-      const int per = ph == 3 ? g2 : g13, nper = ph == 3 ? nper2 : nper13;
-      const int rank = t / per, t0 = (t % per) * kWgradPerTicket;
-      const int t1 = min(nper, t0 + kWgradPerTicket);
-      if (ph == 3) {
-        for (int tt = t0; tt < t1; ++tt) bwd_dw2_tile(B, rank, tt, (bf16_t*)smem);
-      } else {
+      const int per = ph == 3 ? g2 : g13;
+      const int rank = t / per;
+      if ((MASK & 8u) && ph == 3) {
+        bwd_dw2_band(B, rank, t % per, (bf16_t*)smem);
+      } else if (MASK & 0x20u) {
         const int e = B.eorder[rank];
         const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
         if (wait_geq(&B.s.aux1[e], need, W, &s_flag))
-          for (int tt = t0; tt < t1; ++tt) bwd_dw13_tile(B, rank, tt, (bf16_t*)smem);
+          bwd_dw13_band(B, rank, t % per, (bf16_t*)smem);
       }
-    } else if (ph == 2) {
+    } else if ((MASK & 4u) && ph == 2) {
       if (t >= s_nmt * B.nNdh) continue;
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdh, t, tile, nt);
       bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
       signal_add(&B.s.h_cnt[tile], 1);
       signal_add(&B.s.aux1[B.tile_e[tile]], 1);
-    } else if (ph == 4) {
+    } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * B.nNdx) continue;
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdx, t, tile, nt);
       if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
       signal_add(B.s.g2_done, 1);
-    } else {
+    } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(B.s.g2_done, s_nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
     }
   }
@@ -481,6 +496,24 @@ static int launch_status() {
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+template <class Act, class TL, unsigned MASK>
+static int launch_fused_fwd(const moe_desc* D, const Fwd& F, size_t smem, hipStream_t st) {
+  if (!set_smem(k_fused_fwd<Act, TL, MASK>, smem)) return MOE_ERR_HIP;
+  const int n_wg = persistent_grid(k_fused_fwd<Act, TL, MASK>, smem, D->n_workgroups);
+  if (n_wg <= 0) return MOE_ERR_HIP;
+  hipLaunchKernelGGL((k_fused_fwd<Act, TL, MASK>), dim3(n_wg), dim3(256), smem, st, F);
+  return launch_status();
+}
+
+template <unsigned MASK>
+static int launch_fused_bwd(const moe_desc* D, const Bwd& B, size_t smem, hipStream_t st) {
+  if (!set_smem(k_fused_bwd<MASK>, smem)) return MOE_ERR_HIP;
+  const int n_wg = persistent_grid(k_fused_bwd<MASK>, smem, D->n_workgroups);
+  if (n_wg <= 0) return MOE_ERR_HIP;
+  hipLaunchKernelGGL(k_fused_bwd<MASK>, dim3(n_wg), dim3(256), smem, st, B);
+  return launch_status();
+}
+
 template <class Act, class TL>
 static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStream_t st) {
   constexpr bool isf = std::is_same<Act, float>::value;
@@ -496,11 +529,15 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
     return launch_status();
   }
   if (D->fused) {
-    if (!set_smem(k_fused_fwd<Act, TL>, smem)) return MOE_ERR_HIP;
-    const int n_wg = persistent_grid(k_fused_fwd<Act, TL>, smem, D->n_workgroups);
-    if (n_wg <= 0) return MOE_ERR_HIP;
-    hipLaunchKernelGGL((k_fused_fwd<Act, TL>), dim3(n_wg), dim3(256), smem, st, F);
-    return launch_status();
+    if (D->flags & MOE_FLAG_PERSISTENT_SPLIT) {
+      // the same persistent scheduler, one launch per phase group
+      int rc = launch_fused_fwd<Act, TL, 0x0Fu>(D, F, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x10u>(D, F, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, smem, st);
+      return rc;
+    }
+    return launch_fused_fwd<Act, TL, 0x7Fu>(D, F, smem, st);
   }
   hipLaunchKernelGGL(k_router_partial<Act>, dim3(p.nb * p.S), dim3(256), 0, st, F);
   if (!set_smem(k_router_topk<true>, kTopkSmem)) return MOE_ERR_HIP;
@@ -535,6 +572,8 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   B.src = at<int>(ws, p.o_src); B.grow = at<float>(ws, p.o_grow);
   B.dab = at<bf16_t>(ws, p.o_dab); B.dxp = at<bf16_t>(ws, p.o_big2); B.dgp = at<float>(ws, p.o_dgp);
   B.zrow = at<bf16_t>(ws, p.o_zero);
+  B.xp = at<bf16_t>(ws, p.o_big1);
+  B.gg = at<bf16_t>(ws, p.o_gg);
   B.s = make_sync(p, ws, sv->status, D->flags);
   hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, B.s.queue, (int)p.n_ctr);
   const int nz = (int)(((size_t)2 * p.I + p.d + 256) / 2);
@@ -542,11 +581,21 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes;
   if (D->fused) {
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
-    if (!set_smem(k_fused_bwd, smem)) return MOE_ERR_HIP;
-    const int n_wg = persistent_grid(k_fused_bwd, smem, D->n_workgroups);
-    if (n_wg <= 0) return MOE_ERR_HIP;
-    hipLaunchKernelGGL(k_fused_bwd, dim3(n_wg), dim3(256), smem, st, B);
-    return launch_status();
+    if (D->flags & MOE_FLAG_PERSISTENT_SPLIT) {
+      int rc = launch_fused_bwd<0x03u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x10u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x40u>(D, B, smem, st);
+      return rc;
+    }
+    if (D->flags & MOE_FLAG_PERSISTENT_WGRAD_APART) {
+      int rc = launch_fused_bwd<0x57u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x28u>(D, B, smem, st);
+      return rc;
+    }
+    return launch_fused_bwd<0x7Fu>(D, B, smem, st);
   }
   if (!set_smem(k_bwd_dh, sm_dh) || !set_smem(k_bwd_dxp, sm_dh) || !set_smem(k_bwd_dw2, sm_dw) ||
       !set_smem(k_bwd_dw13, sm_dw))
@@ -554,9 +603,10 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   hipLaunchKernelGGL(k_bwd_setup, dim3(1), dim3(256), 0, st, B);
   if (p.nRP > 0) hipLaunchKernelGGL(k_bwd_rowprep, dim3(p.nRP), dim3(256), 0, st, B);
   if (p.R > 0) hipLaunchKernelGGL(k_bwd_dh, dim3(p.max_tiles * p.nNdh), dim3(256), sm_dh, st, B);
-  hipLaunchKernelGGL(k_bwd_dw2, dim3(p.E * p.nW2m * p.nW2n), dim3(256), sm_dw, st, B);
+  hipLaunchKernelGGL(k_bwd_dw2, dim3(p.E * p.nW2m * cdiv(p.nW2n, kWgradPerTicket)), dim3(256), sm_dw, st, B);
   if (p.R > 0) hipLaunchKernelGGL(k_bwd_dxp, dim3(p.max_tiles * p.nNdx), dim3(256), sm_dh, st, B);
-  hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * p.nW13n), dim3(256), sm_dw, st, B);
+  hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * cdiv(p.nW13n, kWgradPerTicket)), dim3(256), sm_dw, st,
+                     B);
   if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
   return launch_status();
 }

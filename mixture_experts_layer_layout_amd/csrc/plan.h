@@ -25,13 +25,13 @@ struct Plan {
   int nNdx;        // column tiles of the dXp GEMM (over d)
   int nW2m, nW2n;  // dW2 tiles per expert: over d, over I
   int nW13m, nW13n;// dW1/dW3 tiles per expert: over I (half a tile of each), over d
-  int nRP;         // rowprep tasks
+  int nRP;         // rowprep (pull) tasks
   // workspace carving (byte offsets)
   size_t o_ctr, n_ctr;
   size_t o_lpart, o_topk, o_gate, o_bmask, o_bcnt, o_bbase, o_counts, o_offsets;
   size_t o_tile_e, o_tile_r0, o_tile_n, o_perm, o_inv, o_src, o_grow;
   size_t o_etile, o_eorder;
-  size_t o_h, o_big1, o_big2, o_dab, o_dgp, o_hs, o_zero;
+  size_t o_h, o_big1, o_big2, o_dab, o_dgp, o_hs, o_zero, o_gg;
   size_t total;
 };
 

@@ -25,26 +25,14 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcds - 1);
 }
 
-// Thread 0 only: a bounded wait (true when *ctr >= target).
-__device__ __forceinline__ bool thread_wait_geq(const int* ctr, int target, const WaitCtx& w) {
-  long long spins = 0;
-  while (load_acquire(ctr) < target) {
-    if (load_relaxed(w.abort)) return false;
-    if (++spins > w.spin_limit) {
-      set_status(w.status, MOE_ERR_TIMEOUT);
-      __hip_atomic_store(w.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return true;
-}
-
-// Claim state of one workgroup (meaningful in thread 0).
+// Claim state of one workgroup, kept in LDS (only thread 0 touches it) so
+// it occupies no registers across the tasks of the persistent loop.
 struct Claim {
-  int phase = 0;  // current phase
-  int qoff = 0;   // sub-queue being drained: (own + qoff) % 8
-  int own = 0;    // this workgroup's XCD
+  int phase;  // current phase
+  int qoff;   // sub-queue being drained: (own + qoff) % 8
+  int own;    // this workgroup's XCD
+  int nmt;    // row tiles once known, else -1
+  int task;   // the claimed task (-1: done)
 };
 
 // Thread 0 only.  shape(phase, groups, per) gives the phase's group count

@@ -20,11 +20,14 @@
 //                         gather-sum, so the result is deterministic)
 // Tasks, in ticket order, and what each waits for:
 //   setup      row tiles and expert order from the saved offsets
-//   rowprep    src[r] = perm[r] / k and g[r] = gate[perm[r]]
+//   rowprep    src[r] = perm[r] / k, g[r] = gate[perm[r]], and the pulls
+//              Xp[r] = X[src[r]], gG[r] = g[r] dY[src[r]] (the operands
+//              of the weight gradients, as plain rows)
 //   dh         (row tile, I tile): dHu, dgate partial, dA | dB   [setup]
-//   dw2        (expert, d tile, I tile)                          [setup]
+//   dw2        (expert, band of d, 8 column tiles of I)          [setup]
 //   dxp        (row tile, d tile), K = 2I over [dA | dB]         [dh of the row tile]
-//   dw13       (expert, I tile, d tile): dW1 and dW3 together    [dh of the expert]
+//   dw13       (expert, band of I, 8 column tiles of d): dW1 and dW3 together
+//                                                                [dh of the expert]
 //   dx         8 tokens: dX and dgate                            [every dxp]
 // Weight-gradient tiles are taken in order of decreasing expert load so the
 // longest tiles start first.
@@ -37,8 +40,8 @@ namespace moe {
 
 typedef Tile<128, 128> TileDH;  // row tiles: dh, dxp
 typedef Tile<128, 128> TileDW;  // weight-gradient tiles: dw2, dw13
-constexpr int kRowPrep = 1024;  // rows per rowprep task
-constexpr int kWgradPerTicket = 4;  // weight-gradient tiles per claim
+constexpr int kRowPrep = 32;    // rows per rowprep (pull) task
+constexpr int kWgradPerTicket = 8;  // column tiles per weight-gradient task (one band)
 
 struct Bwd {
   int T, d, E, k, I, R, BM;
@@ -70,6 +73,8 @@ struct Bwd {
   bf16_t* dab;           // [R, 2I]  dA | dB
   bf16_t* dxp;           // [R, d]
   float* dgp;            // [nNdh, R] dgate partial sums
+  bf16_t* xp;            // [R, d] X pulled into expert order
+  bf16_t* gg;            // [R, d] g_r * dY pulled into expert order
   const bf16_t* zrow;    // >= 2I + d + 256 zeros: the K tail of weight-gradient tiles
   Sync s;
 };
@@ -110,11 +115,31 @@ __device__ void bwd_setup(const Bwd& B, int* sh /* >= 2*kMaxE + 16 ints */) {
 }
 
 __device__ void bwd_rowprep(const Bwd& B, int task) {
-  const int r_end = min(B.R, (task + 1) * kRowPrep);
-  for (int r = task * kRowPrep + threadIdx.x; r < r_end; r += kThreads) {
+  const int r0 = task * kRowPrep, n = min(kRowPrep, B.R - r0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nvec = B.d / 8;
+  for (int i = wave; i < n; i += 4) {
+    const int r = r0 + i;
     const int a = B.perm[r];
-    B.src[r] = a / B.k;
-    B.grow[r] = B.gate[a];
+    const int t = a / B.k;
+    const float g = B.gate[a];
+    if (lane == 0) {
+      B.src[r] = t;
+      B.grow[r] = g;
+    }
+    const uint4* xs = (const uint4*)(B.x + (size_t)t * B.d);
+    const uint4* ys = (const uint4*)(B.dy + (size_t)t * B.d);
+    uint4* xd = (uint4*)(B.xp + (size_t)r * B.d);
+    uint4* gd = (uint4*)(B.gg + (size_t)r * B.d);
+    for (int v = lane; v < nvec; v += 64) {
+      xd[v] = xs[v];
+      uint4 u = ys[v];
+      uint32_t* w = (uint32_t*)&u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = pack_bf16x2(bf16_to_f32((bf16_t)(w[q] & 0xffff)) * g, bf16_to_f32((bf16_t)(w[q] >> 16)) * g);
+      gd[v] = u;
+    }
   }
 }
 
@@ -130,7 +155,7 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
   KRows<TL::BM> la;
   // rows past n repeat the last row (their outputs are dropped)
   la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)B.src[r0 + min(r, n - 1)] * d; });
-  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
+  auto lb = kcols<TL::BN>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
   f32x16_t acc[TL::MI][TL::NJ];
   tile_mainloop<TL>(d / 64, smem, acc, la, lb);
 
@@ -190,7 +215,7 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const int c0 = nt * TL::BN;
   KRows<TL::BM> la;
   la.init([&](int r) -> const bf16_t* { return B.dab + (size_t)(r0 + min(r, n - 1)) * 2 * I; });
-  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* {
+  auto lb = kcols<TL::BN>([&](int kk, int) -> const bf16_t* {
     return (kk < I ? W1 + (size_t)kk * d : W3 + (size_t)(kk - I) * d) + c0;
   });
   f32x16_t acc[TL::MI][TL::NJ];
@@ -202,57 +227,72 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
 
 // ---------------------------------------------------------------- dw2
 // dW2_e[n0 .. +128, i0 .. +128] = sum over the expert's rows r of
-// g_r G[r, n] H[r, i]; K = the expert's rows (zero rows give zeros).
-__device__ void bwd_dw2_tile(const Bwd& B, int rank, int tt, bf16_t* smem) {
+// gG[r, n] H[r, i] (gG pulled by rowprep): K = the expert's rows, k past
+// them reads the zero row.  One task is
+// a band of 128 output rows (n0) over kWgradPerTicket column tiles, streamed
+// (tile_stream) so consecutive column tiles overlap.
+__device__ void bwd_dw2_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   typedef TileDW TL;
   const int e = B.eorder[rank];
-  const int n0 = (tt / B.nW2n) * TL::BM, i0 = (tt % B.nW2n) * TL::BN;
+  const int chunks = cdiv(B.nW2n, kWgradPerTicket);
+  const int n0 = (task / chunks) * TL::BM;
+  const int cb = (task % chunks) * kWgradPerTicket, nc = min(kWgradPerTicket, B.nW2n - cb);
   const int d = B.d, I = B.I;
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
-  // k past the expert's rows reads the zero row; the index loads are
-  // clamped so they stay inside the expert
-  auto la = kcols_scaled<TL::BM>(
-      [&](int kk) -> const bf16_t* {
-        const bf16_t* q = B.dy + (size_t)B.src[off + min(kk, M - 1)] * d + n0;
-        return kk < M ? q : B.zrow;
-      },
-      [&](int kk) { return B.grow[off + min(kk, M - 1)]; });
-  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* {
-    return kk < M ? B.h + (size_t)(off + kk) * I + i0 : B.zrow;
+  bf16_t* out = B.dw2 + (size_t)e * d * I + (size_t)n0 * I;
+  auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
+    tile_store_pairs<TL>(acc, TL::BM, [&](int row) { return out + (size_t)row * I + (cb + c) * TL::BN; });
+  };
+  if (M == 0) {
+    f32x16_t zero[TL::MI][TL::NJ] = {};
+    for (int c = 0; c < nc; ++c) epi(c, zero);
+    return;
+  }
+  auto la = kcols<TL::BM>(
+      [&](int kk, int) -> const bf16_t* { return kk < M ? B.gg + (size_t)(off + kk) * d + n0 : B.zrow; });
+  auto lb = kcols<TL::BN>([&](int kk, int c) -> const bf16_t* {
+    return kk < M ? B.h + (size_t)(off + kk) * I + (cb + c) * TL::BN : B.zrow;
   });
-  f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(cdiv(M, 64), smem, acc, la, lb);
-  bf16_t* out = B.dw2 + (size_t)e * d * I;
-  const Staged<TL::BM, TL::BN> st{smem};
-  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
-  st.flush(TL::BM, [&](int row) { return out + (size_t)(n0 + row) * I + i0; });
+  const int nk = cdiv(M, 64);
+  la.nk_ = nk;
+  lb.nk_ = nk;
+  tile_stream<TL>(nc, nk, smem, la, lb, epi);
 }
 
 // ---------------------------------------------------------------- dw13
-// Rows 0..63 of the tile are dW1_e[i0 ..], rows 64..127 dW3_e[i0 ..]:
-// both share the gathered X operand.
-__device__ void bwd_dw13_tile(const Bwd& B, int rank, int tt, bf16_t* smem) {
+// Rows 0..63 of a tile are dW1_e[i0 ..], rows 64..127 dW3_e[i0 ..]: both
+// share the pulled X operand (Xp).  One task is a band (i0) over
+// kWgradPerTicket column tiles of d, streamed like dw2.
+__device__ void bwd_dw13_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   typedef TileDW TL;
   const int e = B.eorder[rank];
-  const int i0 = (tt / B.nW13n) * (TL::BM / 2), c0 = (tt % B.nW13n) * TL::BN;
+  const int chunks = cdiv(B.nW13n, kWgradPerTicket);
+  const int i0 = (task / chunks) * (TL::BM / 2);
+  const int cb = (task % chunks) * kWgradPerTicket, nc = min(kWgradPerTicket, B.nW13n - cb);
   const int d = B.d, I = B.I;
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
+  bf16_t* o1 = B.dw1 + (size_t)e * I * d + (size_t)i0 * d;
+  bf16_t* o3 = B.dw3 + (size_t)e * I * d + (size_t)i0 * d;
+  auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
+    tile_store_pairs<TL>(acc, TL::BM, [&](int row) {
+      return (row < TL::BM / 2 ? o1 + (size_t)row * d : o3 + (size_t)(row - TL::BM / 2) * d) + (cb + c) * TL::BN;
+    });
+  };
+  if (M == 0) {
+    f32x16_t zero[TL::MI][TL::NJ] = {};
+    for (int c = 0; c < nc; ++c) epi(c, zero);
+    return;
+  }
   auto la = kcols<TL::BM>(
-      [&](int kk) -> const bf16_t* { return kk < M ? B.dab + (size_t)(off + kk) * 2 * I + i0 : B.zrow; },
+      [&](int kk, int) -> const bf16_t* { return kk < M ? B.dab + (size_t)(off + kk) * 2 * I + i0 : B.zrow; },
       I - TL::BM / 2);
-  auto lb = kcols<TL::BN>([&](int kk) -> const bf16_t* {
-    const bf16_t* q = B.x + (size_t)B.src[off + min(kk, M - 1)] * d + c0;
-    return kk < M ? q : B.zrow;
+  auto lb = kcols<TL::BN>([&](int kk, int c) -> const bf16_t* {
+    return kk < M ? B.xp + (size_t)(off + kk) * d + (cb + c) * TL::BN : B.zrow;
   });
-  f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(cdiv(M, 64), smem, acc, la, lb);
-  bf16_t* o1 = B.dw1 + (size_t)e * I * d;
-  bf16_t* o3 = B.dw3 + (size_t)e * I * d;
-  const Staged<TL::BM, TL::BN> st{smem};
-  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
-  st.flush(TL::BM, [&](int row) {
-    return (row < TL::BM / 2 ? o1 + (size_t)(i0 + row) * d : o3 + (size_t)(i0 + row - TL::BM / 2) * d) + c0;
-  });
+  const int nk = cdiv(M, 64);
+  la.nk_ = nk;
+  lb.nk_ = nk;
+  tile_stream<TL>(nc, nk, smem, la, lb, epi);
 }
 
 // ---------------------------------------------------------------- dx
