@@ -96,12 +96,17 @@ typedef struct moe_desc {
 #define MOE_FLAG_DIRECT_PULL 0x1u  /* fused bf16 forward: the up-projection
                                       reads token rows from X through the
                                       layout instead of a staged copy       */
-#define MOE_FLAG_PERSISTENT_SPLIT 0x2u /* fused = 1: run the persistent
+#define MOE_FLAG_PERSISTENT_SPLIT 0x2u /* fused forward: run the persistent
                                       scheduler as one launch per phase
-                                      group instead of one launch for all */
-#define MOE_FLAG_PERSISTENT_WGRAD_APART 0x4u /* fused backward: the weight
-                                      gradients in a second persistent
-                                      launch after the rest              */
+                                      group instead of one launch for all
+                                      (the fused backward always does so
+                                      unless one of the two flags below
+                                      is set)                            */
+#define MOE_FLAG_PERSISTENT_WGRAD_APART 0x4u /* fused backward: two
+                                      persistent launches, the weight
+                                      gradients after the rest           */
+#define MOE_FLAG_PERSISTENT_SINGLE 0x8u /* fused backward: every phase in
+                                      one persistent launch              */
 #define MOE_FLAG_SPIN_LIMIT_TINY 0x100u /* test only: bounded waits give up
                                       after a few polls (exercises the
                                       MOE_ERR_TIMEOUT path)                 */
@@ -123,7 +128,7 @@ typedef struct moe_weights {
 } moe_weights;
 
 /* Optional device buffers.  moe_forward writes each non-NULL one;
- * moe_backward reads topk_idx, gate, offsets, perm, inv, a, b and h
+ * moe_backward reads gate, offsets, perm, inv, a, b and h
  * (all required there).
  *   logits   float [T, E]   router logits (bias not included)
  *   topk_idx int32 [T, k]   chosen experts, largest logit first
@@ -207,9 +212,10 @@ MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K,
  *   saved optional outputs (may be NULL).
  * With desc->fused = 1 the layer is one persistent launch (after a small
  * clearing launch): routing, counting, layout, gather, the two grouped
- * GEMMs and the combine are tasks taken from a device-side queue in
- * dependency order; a GEMM tile starts as soon as the ready counter of its
- * rows shows them staged (MoK flash §02). */
+ * GEMMs and the combine are tasks claimed from device-side queues phase by
+ * phase; a GEMM tile starts as soon as the ready counter of its rows shows
+ * them staged (MoK flash §02).  MOE_FLAG_PERSISTENT_SPLIT runs the same
+ * scheduler as one launch per phase group. */
 MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
                 const float* bias, const moe_weights* w, void* y,
                 const moe_saved* saved, void* workspace,
@@ -219,11 +225,16 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
  * pull reverse-combine, expert dgrad and wgrad, push reverse-dispatch).
  * bf16 only.
  *   dy    act [T, d] upstream gradient;  x act [T, d] the forward input;
- *   saved the forward's topk_idx, gate, offsets, perm, inv, a, b, h;
+ *   saved the forward's gate, offsets, perm, inv, a, b, h;
  *   dx    act [T, d] output, gradient through the experts only;
  *   dw1, dw3 act [E, I, d], dw2 act [E, d, I] outputs (overwritten; zero
  *         for experts without rows);
- *   dgate float [T, k] output, dL/dgate. */
+ *   dgate float [T, k] output, dL/dgate.
+ * With desc->fused = 1 the phases (setup, rowprep and pulls, dH, dW2, dXp,
+ * dW1/dW3, dX) run through the persistent scheduler, one launch per phase
+ * unless MOE_FLAG_PERSISTENT_SINGLE or MOE_FLAG_PERSISTENT_WGRAD_APART is
+ * set; with fused = 0 each phase is an ordinary grid.  Needs bf16 with
+ * d % 256 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED). */
 MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
                  const moe_weights* w, const moe_saved* saved, void* dx,
                  void* dw1, void* dw3, void* dw2, float* dgate,

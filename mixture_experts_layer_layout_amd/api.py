@@ -32,6 +32,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_FLAG_DIRECT_PULL = 0x1
 MOE_FLAG_PERSISTENT_SPLIT = 0x2
 MOE_FLAG_PERSISTENT_WGRAD_APART = 0x4
+MOE_FLAG_PERSISTENT_SINGLE = 0x8
 MOE_FLAG_SPIN_LIMIT_TINY = 0x100
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}

@@ -43,6 +43,16 @@ __device__ __forceinline__ int lds_idx(int row, int chunk) {
   return (row << 6) + (((chunk ^ (row >> 1)) & 7) << 3);
 }
 
+// Stages whose global loads are in flight while one stage feeds the MFMAs
+// (register buffers per loader).  Measured: 2 gave no gain over 1 on the
+// expert GEMMs, and its 32 extra VGPRs keep the persistent kernels from
+// fitting two workgroups per CU.
+#ifndef MOE_PREFETCH
+#define MOE_PREFETCH 1
+#endif
+constexpr int kPrefetch = MOE_PREFETCH;
+static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch distance 1 or 2");
+
 template <int BM_, int BN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_;
@@ -58,7 +68,7 @@ template <int ROWS>
 struct KRows {
   static constexpr int PER = ROWS / 32;
   const bf16_t* row[PER];
-  uint4 v[2][PER];
+  uint4 v[kPrefetch][PER];
   // rowptr(r) -> pointer to element k=0 of tile row r; must be readable
   // for every r (clamp rows past the operand to a real one).
   template <class F>
@@ -103,8 +113,8 @@ struct KCols {
   int coff;
   int nk_ = 0;  // stages per column tile when streamed (tile_stream), else 0
   const bf16_t* p[KK];
-  float s[KK], sl[2][KK];
-  uint4 v[2][KK];
+  float s[KK], sl[kPrefetch][KK];
+  uint4 v[kPrefetch][KK];
   __device__ __forceinline__ KCols(P kp, S ks, int half_off) : kptr(kp), kscale(ks) {
     const int nb = threadIdx.x / KG;
     coff = nb * 8 + (nb >= ROWS / 16 ? half_off : 0);
@@ -224,22 +234,47 @@ __device__ __forceinline__ void tile_compute(const bf16_t* As, const bf16_t* Bs,
 // earlier) is written to the other LDS buffer.  Every load, prep and store
 // is unconditional -- past the last stage they repeat it -- so the only
 // waits the compiler emits are for the stage being stored.
-// One step of the K loop with register buffer CUR free (stage kt lives in
-// LDS buffer CUR, stage kt+1 in register buffer CUR ^ 1).
+// One step of the K loop.  kPrefetch = 2: register buffer CUR is free
+// (stage kt lives in LDS buffer CUR, stage kt+1 in register buffer CUR ^ 1)
+// and receives stage kt+2.  kPrefetch = 1: one register buffer, which
+// receives stage kt+1 while stage kt feeds the MFMAs.
 template <int CUR, class TL, class LA, class LB>
 __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16_t* Bs,
                                               f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B) {
-  A.template load<CUR>(min(kt + 2, last));
-  B.template load<CUR>(min(kt + 2, last));
-  A.prep(min(kt + 3, last));
-  B.prep(min(kt + 3, last));
+  constexpr int RB = kPrefetch == 2 ? CUR : 0;        // register buffer loaded now
+  constexpr int SB = kPrefetch == 2 ? (CUR ^ 1) : 0;  // register buffer stored now
+  A.template load<RB>(min(kt + kPrefetch, last));
+  B.template load<RB>(min(kt + kPrefetch, last));
+  A.prep(min(kt + kPrefetch + 1, last));
+  B.prep(min(kt + kPrefetch + 1, last));
   // keep the scheduler from sinking these loads below the LDS stores of
   // the previous stage (which wait for their own loads)
   __builtin_amdgcn_sched_barrier(0);
   tile_compute<TL>(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
-  A.template store<CUR ^ 1>(As + (CUR ^ 1) * TL::LDS_A);
-  B.template store<CUR ^ 1>(Bs + (CUR ^ 1) * TL::LDS_B);
+  A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
+  B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);
+  __syncthreads();
+}
+
+// Loads the first stages and stores stage 0 into LDS buffer 0.
+template <class LA, class LB>
+__device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* Bs, LA& A, LB& B) {
+  A.prep(0);
+  B.prep(0);
+  A.template load<0>(0);
+  B.template load<0>(0);
+  A.prep(min(1, last));
+  B.prep(min(1, last));
+  if (kPrefetch == 2) {
+    A.template load<1>(min(1, last));
+    B.template load<1>(min(1, last));
+    A.prep(min(2, last));
+    B.prep(min(2, last));
+  }
+  __syncthreads();
+  A.template store<0>(As);
+  B.template store<0>(Bs);
   __syncthreads();
 }
 
@@ -256,20 +291,7 @@ __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&a
   const int last = nk - 1;
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
-  A.prep(0);
-  B.prep(0);
-  A.template load<0>(0);
-  B.template load<0>(0);
-  A.prep(min(1, last));
-  B.prep(min(1, last));
-  A.template load<1>(min(1, last));
-  B.template load<1>(min(1, last));
-  A.prep(min(2, last));
-  B.prep(min(2, last));
-  __syncthreads();
-  A.template store<0>(As);
-  B.template store<0>(Bs);
-  __syncthreads();
+  mainloop_prologue(last, As, Bs, A, B);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     mainloop_step<0, TL>(kt, last, As, Bs, acc, A, B);
@@ -326,15 +348,17 @@ __device__ __forceinline__ void tile_visit_pairs(const f32x16_t (&acc)[TL::MI][T
 template <int CUR, class TL, class LA, class LB, class EPI>
 __device__ __forceinline__ void stream_step(int j, int nk, int last, bf16_t* As, bf16_t* Bs,
                                             f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B, EPI& epi) {
-  A.template load<CUR>(min(j + 2, last));
-  B.template load<CUR>(min(j + 2, last));
-  A.prep(min(j + 3, last));
-  B.prep(min(j + 3, last));
+  constexpr int RB = kPrefetch == 2 ? CUR : 0;
+  constexpr int SB = kPrefetch == 2 ? (CUR ^ 1) : 0;
+  A.template load<RB>(min(j + kPrefetch, last));
+  B.template load<RB>(min(j + kPrefetch, last));
+  A.prep(min(j + kPrefetch + 1, last));
+  B.prep(min(j + kPrefetch + 1, last));
   __builtin_amdgcn_sched_barrier(0);
   tile_compute<TL>(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
-  A.template store<CUR ^ 1>(As + (CUR ^ 1) * TL::LDS_A);
-  B.template store<CUR ^ 1>(Bs + (CUR ^ 1) * TL::LDS_B);
+  A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
+  B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);
   if ((j + 1) % nk == 0) {
     epi(j / nk, acc);
 #pragma unroll
@@ -361,20 +385,7 @@ __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A,
   const int last = total - 1;
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
-  A.prep(0);
-  B.prep(0);
-  A.template load<0>(0);
-  B.template load<0>(0);
-  A.prep(min(1, last));
-  B.prep(min(1, last));
-  A.template load<1>(min(1, last));
-  B.template load<1>(min(1, last));
-  A.prep(min(2, last));
-  B.prep(min(2, last));
-  __syncthreads();
-  A.template store<0>(As);
-  B.template store<0>(Bs);
-  __syncthreads();
+  mainloop_prologue(last, As, Bs, A, B);
   int j = 0;
   for (; j + 1 < total; j += 2) {
     stream_step<0, TL>(j, nk, last, As, Bs, acc, A, B, epi);

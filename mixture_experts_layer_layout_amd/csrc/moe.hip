@@ -379,9 +379,14 @@ __global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockI
 // raster, 64 per queue block; the weight-gradient tiles of the expert of
 // load rank q -> queue q % 8, one band of kWgradPerTicket column tiles per
 // claim).
+// Workgroups per CU the persistent backward asks the compiler to fit: two
+// where the phases' registers allow it without spilling, else one.
+constexpr int bwd_occupancy(unsigned mask) {
+  return mask == 0x7Fu || mask == 0x57u || mask == 0x28u ? 1 : 2;
+}
+
 template <unsigned MASK>
-__global__ void __launch_bounds__(256, (MASK & 0x28u) == MASK || (MASK & 0x14u) == MASK ? 2 : 1)
-    k_fused_bwd(Bwd B) {
+__global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   __shared__ Claim c;
   __shared__ int s_flag;
@@ -581,7 +586,10 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes;
   if (D->fused) {
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
-    if (D->flags & MOE_FLAG_PERSISTENT_SPLIT) {
+    // one persistent launch per phase group unless asked for a single
+    // launch: every backward task together does not fit two workgroups'
+    // registers per CU (MOE_FLAG_PERSISTENT_SINGLE runs it anyway)
+    if (!(D->flags & (MOE_FLAG_PERSISTENT_SINGLE | MOE_FLAG_PERSISTENT_WGRAD_APART))) {
       int rc = launch_fused_bwd<0x03u>(D, B, smem, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, smem, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, smem, st);

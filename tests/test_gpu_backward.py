@@ -119,3 +119,20 @@ def test_backward_rejects_unsupported_shapes():
         api.moe_backward(d, None, None, api.make_weights(None, None, None), api.make_saved(), None,
                          None, None, None, None, None)
     assert e.value.code == api.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("flags", [0, "PERSISTENT_SINGLE", "PERSISTENT_WGRAD_APART"])
+def test_backward_persistent_variants_equal_unfused(flags):
+    """Every way of running the persistent scheduler gives the bits of the
+    one-kernel-per-step backward."""
+    flags = getattr(api, "MOE_FLAG_" + flags) if flags else 0
+    w = SMALL["dsv3-zipf-small"]
+    inp = synth.make_inputs(w, 9, with_dy=True)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    y, sv = layer.forward(w, dev, fused=False)
+    g1 = layer.backward(w, dev, sv, fused=True, flags=flags)
+    g2 = layer.backward(w, dev, sv, fused=False)
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    for n in ("dx", "dw1", "dw3", "dw2", "dgate"):
+        assert torch.equal(g1[n], g2[n]), n

@@ -109,3 +109,17 @@ def test_empty_batch():
     torch.cuda.synchronize()
     assert y.numel() == 0
     assert host(sv["counts"]).sum() == 0 and np.all(host(sv["offsets"]) == 0)
+
+
+@pytest.mark.parametrize("flags", ["PERSISTENT_SPLIT", "DIRECT_PULL"])
+def test_forward_persistent_variants_equal_unfused(flags):
+    w = SMALL["dsv3-zipf-small"]
+    f = getattr(api, "MOE_FLAG_" + flags)
+    inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 10).items()}
+    y1, s1 = layer.forward(w, inp, fused=True, flags=f)
+    y2, s2 = layer.forward(w, inp, fused=False)
+    torch.cuda.synchronize()
+    assert s1["status"].item() == 0
+    assert torch.equal(y1, y2)
+    for n in ("topk_idx", "counts", "offsets", "perm", "inv", "h", "a", "b"):
+        assert torch.equal(s1[n], s2[n]), n
