@@ -53,13 +53,18 @@ __device__ __forceinline__ int lds_idx(int row, int chunk) {
 constexpr int kPrefetch = MOE_PREFETCH;
 static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch distance 1 or 2");
 
+// A tile shape and its operand type.  LDS_A / LDS_B are the sizes of one
+// stage of each operand in bf16 units; stage() runs the MFMAs of one stage
+// held in LDS (the main loop below is shared by every tile type).
 template <int BM_, int BN_>
 struct Tile {
+  static constexpr bool kMX = false;
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NJ = WN / 32;
   static constexpr int LDS_A = BM * 64, LDS_B = BN * 64;
   static constexpr size_t smem_bytes = 2 * (LDS_A + LDS_B) * sizeof(bf16_t);
+  static __device__ __forceinline__ void stage(const bf16_t* As, const bf16_t* Bs, f32x16_t (&acc)[MI][NJ]);
 };
 
 // ---------------------------------------------------------------- loaders
@@ -227,6 +232,11 @@ __device__ __forceinline__ void tile_compute(const bf16_t* As, const bf16_t* Bs,
   }
 }
 
+template <int BM_, int BN_>
+__device__ __forceinline__ void Tile<BM_, BN_>::stage(const bf16_t* As, const bf16_t* Bs, f32x16_t (&acc)[MI][NJ]) {
+  tile_compute<Tile<BM_, BN_>>(As, Bs, acc);
+}
+
 // Runs the K loop over nk stages (nk may be 0: the tile is then zero).
 // Two stages are in flight while a third feeds the MFMAs: at step kt the
 // loads of stage kt+2 go out into the register buffer freed by step kt-1,
@@ -250,7 +260,7 @@ __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16
   // keep the scheduler from sinking these loads below the LDS stores of
   // the previous stage (which wait for their own loads)
   __builtin_amdgcn_sched_barrier(0);
-  tile_compute<TL>(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
+  TL::stage(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
   A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
   B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);
@@ -355,7 +365,7 @@ __device__ __forceinline__ void stream_step(int j, int nk, int last, bf16_t* As,
   A.prep(min(j + kPrefetch + 1, last));
   B.prep(min(j + kPrefetch + 1, last));
   __builtin_amdgcn_sched_barrier(0);
-  tile_compute<TL>(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
+  TL::stage(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
   A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
   B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);

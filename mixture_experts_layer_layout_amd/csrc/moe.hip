@@ -94,6 +94,7 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_eorder = take((size_t)E * 4);
   p->o_h = take(R * I * es);
   p->o_hs = take(R * (I / 32));
+  p->o_xs = p->mxfp8 ? take((size_t)T * (d / 32)) : 0;
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
   if (p->bwd_ok) {
@@ -119,6 +120,7 @@ static Sync make_sync(const Plan& p, void* ws, int32_t* status, uint32_t flags) 
   s.g2_done = c + C_G2;
   s.n_mtiles = c + C_NMT;
   s.aux3 = c + C_AUX3;
+  s.q_done = c + C_QDONE;
   int* q = c + C_HEADER;
   s.qctr = q; q += kMaxPhases * kXcds;
   s.r1_cnt = q; q += p.nb;
@@ -139,7 +141,8 @@ static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved*
   F.nb = p.nb; F.S = p.S; F.BM = p.BM; F.nN1 = p.nN1; F.nN2 = p.nN2; F.nC = p.nC;
   F.max_tiles = p.max_tiles;
   F.score = D->score; F.renorm = D->renorm ? 1 : 0;
-  F.direct = (D->flags & MOE_FLAG_DIRECT_PULL) && !p.f32 && !p.mxfp8 ? 1 : 0;
+  // MXFP8 always pulls token rows from the quantised x (no gathered copy)
+  F.direct = p.mxfp8 || ((D->flags & MOE_FLAG_DIRECT_PULL) && !p.f32) ? 1 : 0;
   F.lpart = at<float>(ws, p.o_lpart);
   F.logits = sv ? sv->logits : nullptr;
   F.topk = (sv && sv->topk_idx) ? sv->topk_idx : at<int>(ws, p.o_topk);
@@ -162,6 +165,14 @@ static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved*
   F.b = sv ? sv->b : nullptr;
   F.h = (sv && sv->h) ? sv->h : at<char>(ws, p.o_h);
   F.yp = at<char>(ws, p.o_big2);
+  if (p.mxfp8) {
+    // H codes take the workspace H; H itself is written only if asked for
+    F.h = sv ? sv->h : nullptr;
+    F.hq = at<uint8_t>(ws, p.o_h);
+    F.hs = at<uint8_t>(ws, p.o_hs);
+    F.xq = at<uint8_t>(ws, p.o_big1);
+    F.xs = at<uint8_t>(ws, p.o_xs);
+  }
   F.s = make_sync(p, ws, sv ? sv->status : nullptr, D->flags);
   return F;
 }
@@ -209,6 +220,8 @@ template <class Act, class TL>
 __device__ __forceinline__ void run_g1(const Fwd& F, int tile, int nt, char* smem) {
   if constexpr (std::is_same<Act, float>::value)
     g1_tile_f32(F, tile, nt, (float*)smem);
+  else if constexpr (TL::kMX)
+    g1_tile_mx<TL>(F, tile, nt, (bf16_t*)smem);
   else
     g1_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
 }
@@ -216,9 +229,13 @@ template <class Act, class TL>
 __device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* smem) {
   if constexpr (std::is_same<Act, float>::value)
     g2_tile_f32(F, tile, nt, (float*)smem);
+  else if constexpr (TL::kMX)
+    g2_tile_mx<TL>(F, tile, nt, (bf16_t*)smem);
   else
     g2_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
 }
+
+__global__ void __launch_bounds__(256) k_quant_tokens(Fwd F) { quant_tokens(F, blockIdx.x); }
 
 template <class Act, class TL>
 __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g1(Fwd F) {
@@ -243,8 +260,9 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g2(Fwd F) {
 template <class Act>
 __global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F, blockIdx.x); }
 
-// The persistent forward: phases router slices | top-k | layout | gather
-// | up-projection tiles | down-projection tiles | combine, claimed through
+// The persistent forward: phases router slices (+ the MXFP8 quantisation
+// of x by token block) | top-k | layout | gather | up-projection tiles |
+// down-projection tiles | combine, claimed through
 // the per-XCD phase queues (sched.h); the projection tiles are enumerated
 // in the grouped raster, 64 consecutive tasks per XCD queue block.  Each
 // task waits on the counters its inputs raise.
@@ -267,7 +285,7 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F)
         per = 1;
         groups = 0;
         if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
-        if (ph == 0) { groups = F.nb * F.S; return true; }
+        if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0); return true; }
         if (ph == 1) { groups = F.nb; return true; }
         if (ph == 2) { groups = 1; return true; }
         if (c.nmt < 0) {
@@ -289,8 +307,13 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F)
     const int s_nmt = c.nmt;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if ((MASK & 1u) && ph == 0) {
-      router_partial<Act>(F, t);
-      signal_add(&F.s.r1_cnt[t / F.S], 1);
+      if (TL::kMX && t >= F.nb * F.S) {
+        quant_tokens(F, t - F.nb * F.S);
+        signal_add(F.s.q_done, 1);
+      } else {
+        router_partial<Act>(F, t);
+        signal_add(&F.s.r1_cnt[t / F.S], 1);
+      }
     } else if ((MASK & 2u) && ph == 1) {
       if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
       signal_add(F.s.r2_done, 1);
@@ -298,6 +321,8 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F)
       if (wait_geq(F.s.r2_done, F.nb, W, &s_flag)) layout_scan(F, (int*)smem);
       signal_add(F.s.scan_done, 1);
     } else if ((MASK & 8u) && ph == 3) {
+      // MXFP8: a row tile is ready once the codes of x are complete too
+      if (TL::kMX && !wait_geq(F.s.q_done, F.nb, W, &s_flag)) continue;
       if (F.direct)
         gather_tile<Act, false>(F, t, (int*)smem);
       else
@@ -548,6 +573,7 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   if (!set_smem(k_router_topk<true>, kTopkSmem)) return MOE_ERR_HIP;
   hipLaunchKernelGGL(k_router_topk<true>, dim3(p.nb), dim3(256), kTopkSmem, st, F);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
+  if (TL::kMX) hipLaunchKernelGGL(k_quant_tokens, dim3(p.nb), dim3(256), 0, st, F);
   if (F.direct)
     hipLaunchKernelGGL((k_gather<Act, false>), dim3(p.max_tiles), dim3(256), 0, st, F);
   else
@@ -726,7 +752,10 @@ int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float
   Fwd F = make_fwd(p, desc, workspace, saved);
   F.x = x; F.wr = wr; F.bias = bias; F.w1 = w->w1; F.w3 = w->w3; F.w2 = w->w2; F.y = y;
   hipStream_t st = (hipStream_t)stream;
-  if (p.mxfp8) return mxfp8_forward(p, desc, F, w, st);
+  if (p.mxfp8) {
+    F.w1s = w->w1_scale; F.w3s = w->w3_scale; F.w2s = w->w2_scale;
+    return forward_impl<bf16_t, TileMX128>(p, desc, F, st);
+  }
   if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st);
   if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st);
   return forward_impl<bf16_t, TileB128>(p, desc, F, st);

@@ -32,12 +32,13 @@ struct Plan {
   size_t o_tile_e, o_tile_r0, o_tile_n, o_perm, o_inv, o_src, o_grow;
   size_t o_etile, o_eorder;
   size_t o_h, o_big1, o_big2, o_dab, o_dgp, o_hs, o_zero, o_gg;
+  size_t o_xs;     // MXFP8: x scales (the codes sit at o_big1)
   size_t total;
 };
 
 // Counter region, in ints.
 enum CtrSlot {
-  C_QUEUE = 0, C_ABORT, C_R2, C_SCAN, C_G2, C_NMT, C_AUX3, C_HEADER = 16
+  C_QUEUE = 0, C_ABORT, C_R2, C_SCAN, C_G2, C_NMT, C_AUX3, C_QDONE, C_HEADER = 16
 };
 
 int make_plan(const moe_desc* d, Plan* p);

@@ -50,6 +50,7 @@ struct Sync {
   int* aux1;     // backward: [E]
   int* aux2;     // backward: [E]
   int* aux3;     // backward: scalar
+  int* q_done;   // MXFP8 forward: token blocks quantised
   int32_t* status;
   long long spin_limit;
 };
@@ -86,6 +87,15 @@ struct Fwd {
   void* b;           // [R, I] or null
   void* h;           // [R, I]
   void* yp;          // [R, d]
+  // MXFP8 (null otherwise): weight scales, token-major x codes/scales,
+  // row-major H codes/scales
+  const uint8_t* w1s;  // [E, I, d/32]
+  const uint8_t* w3s;  // [E, I, d/32]
+  const uint8_t* w2s;  // [E, d, I/32]
+  uint8_t* xq;         // [T, d]
+  uint8_t* xs;         // [T, d/32]
+  uint8_t* hq;         // [R, I]
+  uint8_t* hs;         // [R, I/32]
   Sync s;
 };
 

@@ -57,9 +57,10 @@ def _positive_codes():
     return _POS
 
 
-def e4m3_encode(v):
+def e4m3_encode_nearest(v):
     """Round fp64 values to E4M3 codes: nearest, ties to the even code
-    (the even mantissa), magnitudes above 448 clamped to 448."""
+    (the even mantissa), magnitudes above 448 clamped to 448.  The
+    definition, by search in the table of representable values."""
     v = np.asarray(v, dtype=np.float64)
     vals, codes = _positive_codes()
     mag = np.minimum(np.abs(v), E4M3_MAX)
@@ -71,6 +72,26 @@ def e4m3_encode(v):
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
     pick_hi |= (hi == lo)
     out = np.where(pick_hi, codes[hi], codes[lo])
+    neg = np.signbit(v) & (out != 0)
+    return (out | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_encode(v):
+    """The rounding of e4m3_encode_nearest in arithmetic form (fast on large
+    arrays; the two are pinned equal in the tests).  With m = min(|v|, 448):
+    the representable magnitudes are the multiples of 2^-9 below 2^-6
+    (subnormals) and, in the binade [2^e, 2^(e+1)) for e >= -6, the
+    multiples of 2^(e-3) (3 mantissa bits).  m divided by that step is
+    exact in fp64 and is rounded half-to-even; counting grid points from
+    zero (8 subnormal codes, then 8 codes per binade) gives the code, and a
+    quotient that rounds up to 16 lands on the first code of the next
+    binade."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.minimum(np.abs(v), E4M3_MAX)
+    _, ex = np.frexp(mag)                       # mag = f 2^ex, f in [0.5, 1)
+    e = np.where(mag > 0, np.maximum(ex - 1, -6), -6)   # floor(log2 mag), at least -6
+    q = np.rint(np.ldexp(mag, 3 - e))           # half to even
+    out = ((e + 6) * 8 + q).astype(np.int64)
     neg = np.signbit(v) & (out != 0)
     return (out | np.where(neg, 0x80, 0)).astype(np.uint8)
 
@@ -92,21 +113,34 @@ def block_scale_code(amax):
     return out.astype(np.uint8)
 
 
-def quantize(v):
-    """Quantise along the last axis in blocks of 32.
-
-    Returns (codes uint8 [..., K], scales uint8 [..., K/32]).
-    """
-    v = np.asarray(v, dtype=np.float64)
+def _quantize_rows(v):
     K = v.shape[-1]
-    if K % BLOCK:
-        raise ValueError("last axis must be a multiple of 32")
     blocks = v.reshape(v.shape[:-1] + (K // BLOCK, BLOCK))
     amax = np.max(np.abs(blocks), axis=-1)
     sc = block_scale_code(amax)
     scale = e8m0_value(sc)[..., None]
     codes = e4m3_encode(blocks / scale)
     return codes.reshape(v.shape), sc
+
+
+def quantize(v):
+    """Quantise along the last axis in blocks of 32.
+
+    Returns (codes uint8 [..., K], scales uint8 [..., K/32]).  Rows are
+    independent; large inputs go through in chunks of rows only to keep the
+    temporaries small.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % BLOCK:
+        raise ValueError("last axis must be a multiple of 32")
+    flat = v.reshape(-1, K)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    sc = np.empty((flat.shape[0], K // BLOCK), dtype=np.uint8)
+    step = max(1, (1 << 19) // K)
+    for r in range(0, flat.shape[0], step):
+        codes[r:r + step], sc[r:r + step] = _quantize_rows(flat[r:r + step])
+    return codes.reshape(v.shape), sc.reshape(v.shape[:-1] + (K // BLOCK,))
 
 
 def dequantize(codes, scales):
@@ -120,8 +154,15 @@ def dequantize(codes, scales):
 
 
 def fake_quant(v):
-    """quantize then dequantize, in fp64."""
-    return dequantize(*quantize(v))
+    """quantize then dequantize, in fp64 (row chunks as in quantize)."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    flat = v.reshape(-1, K)
+    out = np.empty(flat.shape)
+    step = max(1, (1 << 16) // K)
+    for r in range(0, flat.shape[0], step):
+        out[r:r + step] = dequantize(*quantize(flat[r:r + step]))
+    return out.reshape(v.shape)
 
 
 def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):

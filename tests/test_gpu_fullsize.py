@@ -122,3 +122,31 @@ def test_fullsize_bf16(name):
             e3 = row_rel_err(host(g[n][e]).reshape(1, -1), eb[n].reshape(1, -1))
             print(f"  {n}[{e}] ({hi - lo} rows) rel err {e3:.2e}", flush=True)
             assert e3 <= BF16_TOL, (n, e)
+
+
+def test_fullsize_mxfp8():
+    """dsv3-mxfp8 at full size: routing and layout over every token exact;
+    y of a sampled token against the oracle's MXFP8 forward, which quantises
+    that token's experts' bf16 weights itself."""
+    from oracle import mxfp8 as Q
+    w = synth.WORKLOADS["dsv3-mxfp8"]
+    print(f"\nfull-size {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}", flush=True)
+    inp, dev = full_inputs(w, 0)
+    y, sv = layer.forward(w, dev, fused=True)
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    x = host(inp["x"])
+    wr = host(inp["wr"])
+    bias = None if inp["bias"] is None else inp["bias"].numpy()
+    logits = sv["logits"].cpu().numpy()
+    idx, gate = M.route(logits, w.k, w.score, w.renorm, bias)
+    assert np.array_equal(host(sv["topk_idx"]), idx)
+    counts, offsets, perm, inv, src = M.layout(idx, w.E)
+    for n, want in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)):
+        assert np.array_equal(host(sv[n]), want), n
+    ts = np.array([w.T - 1])
+    W1, W3, W2 = (DeviceExperts(dev[n]) for n in ("w1", "w3", "w2"))
+    f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts])
+    err = row_rel_err(host(y)[ts], f["y"])
+    print(f"  y sampled max row-rel err {err:.2e}", flush=True)
+    assert err <= 6e-2

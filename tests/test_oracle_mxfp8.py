@@ -64,6 +64,16 @@ def test_encode_vs_torch_cast_with_ties():
     assert Q.e4m3_value(Q.e4m3_encode(19.0)) == 20.0
 
 
+def test_arithmetic_encode_equals_table_search():
+    vals = Q.e4m3_table()[:127]
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(1)
+    wide = rng.standard_normal(200000) * np.exp2(rng.integers(-14, 10, 200000))
+    v = np.concatenate([vals, -vals, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        wide, [0.0, -0.0, 448.0, 449.0, 480.0, 1e30, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11]])
+    assert np.array_equal(Q.e4m3_encode(v), Q.e4m3_encode_nearest(v))
+
+
 def test_saturation():
     assert Q.e4m3_encode(1e6) == 0x7E and Q.e4m3_encode(-500.0) == 0xFE
     assert Q.e4m3_encode(464.0) == 0x7E
