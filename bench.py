@@ -40,7 +40,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix-core peak, TFLOP/s
+# dense matrix-core peaks, TFLOP/s, by the expert GEMMs' operand type
+MFMA_PEAK_TFS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
 
 DEFAULT_WORKLOAD = "dsv3-fwdbwd-zipf"
 METRIC = "MoE layer tokens/s fwd+bwd on 1 MI355X; grouped-GEMM MFMA util %; gather GB/s"
@@ -90,8 +91,10 @@ def algorithmic_bytes(w, counts, part):
               saved a/b/h, dX, dgate, and the routing/layout arrays
     """
     es = 2 if w.act == "bf16" else 4
+    # MXFP8 weights: one code byte per element plus one scale byte per 32
+    wes = {"f32": 4.0, "bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}[w.experts]
     active = int((counts > 0).sum())
-    wbytes = active * 3 * w.I * w.d * es
+    wbytes = int(active * 3 * w.I * w.d * wes)
     tok = w.T * w.d * es
     small = w.R * 4 * 4 + (w.E + 1) * 8
     saved = 3 * w.R * w.I * es if w.backward else 0
@@ -121,6 +124,10 @@ def cpu_baseline(w, inp_cpu, w_gpu, budget_s=15.0):
     logits = M.router_logits(x, f64(inp_cpu["wr"]))
     idx, gate = M.route(logits, w.k, w.score, w.renorm, bias)
     counts, offsets, perm, inv, src = M.layout(idx, w.E)
+    mx = w.experts == "mxfp8"
+    if mx:
+        from oracle import mxfp8 as Q
+        x = Q.fake_quant(x)      # the dispatch's quantisation of every token
     t_route = time.perf_counter() - t0
     g_row = gate.reshape(-1)[perm]
     dy = f64(inp_cpu["dy"]) if w.backward else None
@@ -132,7 +139,7 @@ def cpu_baseline(w, inp_cpu, w_gpu, budget_s=15.0):
         w1, w3, w2 = (f64(w_gpu[n][e]) for n in ("w1", "w3", "w2"))
         t1 = time.perf_counter()
         xr = M.gather(x, src[lo:hi])
-        a, b, h, yp = M.expert_ffn(xr, w1, w3, w2)
+        a, b, h, yp = (Q.expert_ffn_mxfp8 if mx else M.expert_ffn)(xr, w1, w3, w2)
         contrib = g_row[lo:hi, None] * yp          # this expert's share of the combine
         if w.backward:
             M.expert_backward(xr, M.gather(dy, src[lo:hi]), g_row[lo:hi], w1, w3, w2, saved=(a, b, h))
@@ -147,7 +154,8 @@ def cpu_baseline(w, inp_cpu, w_gpu, budget_s=15.0):
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     return {"value": w.T * frac / secs, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": (f"fp64 numpy oracle: routing+layout of all {w.T} tokens, expert "
+            "sample": (f"fp64 numpy oracle: routing+layout{'+quantisation' if mx else ''} of all "
+                       f"{w.T} tokens, expert "
                        f"{'forward+backward' if w.backward else 'forward'} of experts 0..{n_exp - 1} "
                        f"({rows_done} of {w.R} routed rows), scaled by rows")}
 
@@ -274,7 +282,7 @@ def main():
     phases = {"forward_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
               "forward_expert_tflops": round(expert_flops(w, "forward") / (fwd_ms * 1e-3) / 1e12, 1),
               "forward_mfma_util": round(expert_flops(w, "forward") / (fwd_ms * 1e-3) / 1e12
-                                         / MFMA_BF16_PEAK_TFS, 4),
+                                         / MFMA_PEAK_TFS[w.experts], 4),
               "forward_hbm_frac": round(algorithmic_bytes(w, counts, "forward") / (fwd_ms * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
               "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())}

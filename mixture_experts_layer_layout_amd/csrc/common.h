@@ -22,16 +22,26 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
 
-// float -> bfloat16, round to nearest even (finite inputs; NaN stays NaN).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16, round to nearest even: the conversion compiles to the
+// gfx950 instruction v_cvt_pk_bf16_f32 (NaN stays NaN).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
+// Two floats as packed bfloat16 (lo in bits 0-15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  bf16x2_hw_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The value of the neighbouring lane (lane ^ 1) through a DPP quad
+// permutation [1,0,3,2] (one VALU instruction, no LDS round trip).
+__device__ __forceinline__ float swap_lane_pair(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
 }
 
 template <typename T> struct Elem;

@@ -404,29 +404,30 @@ __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A,
   if (j < total) stream_step<0, TL>(j, nk, last, As, Bs, acc, A, B, epi);
 }
 
-// Writes the accumulators as bf16 straight from registers, two columns per
-// 4-byte store: lane pairs swap values so the even lane of a pair stores
-// (row of r, its two columns) and the odd lane (row of r+1, the same two
-// columns).  dst(row) points at the tile's first column of that output row.
-template <class TL, class D>
-__device__ __forceinline__ void tile_store_pairs(const f32x16_t (&acc)[TL::MI][TL::NJ], int nrows, D dst) {
+// Writes a tile whose rows are all valid as bf16 straight from registers,
+// two columns per 4-byte store: lane pairs swap values so the even lane of
+// a pair stores (row of r, its two columns) and the odd lane (row of r+1,
+// the same two columns).  No per-row test and one address computation per
+// lane: wave row block wm (tile rows wm * WM ..) starts at base(wm),
+// consecutive rows ld elements apart.
+template <class TL, class BASE>
+__device__ __forceinline__ void tile_store_full(const f32x16_t (&acc)[TL::MI][TL::NJ], BASE base, size_t ld) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const bool odd = lane & 1;
+  const int odd = lane & 1;
+  bf16_t* p = base(wm) + (size_t)(4 * (lane >> 5) + odd) * ld + wn * TL::WN + (lane & 30);
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < TL::NJ; ++j)
+    for (int r = 0; r < 16; r += 2) {
+      bf16_t* q = p + (size_t)(32 * i + 8 * (r >> 2) + (r & 3)) * ld;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
+      for (int j = 0; j < TL::NJ; ++j) {
         const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-        const float o0 = __shfl_xor(v0, 1), o1 = __shfl_xor(v1, 1);
-        const int rr = odd ? r + 1 : r;
-        const int row = wm * TL::WM + 32 * i + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-        const int col = wn * TL::WN + 32 * j + (lane & 31 & ~1);
-        const uint32_t w = odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0);
-        if (row < nrows) *(uint32_t*)(dst(row) + col) = w;
+        const float o0 = swap_lane_pair(v0), o1 = swap_lane_pair(v1);
+        *(uint32_t*)(q + 32 * j) = odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0);
       }
+    }
 }
 
 // ---------------------------------------------------------------- epilogue

@@ -241,7 +241,7 @@ __device__ void bwd_dw2_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
   bf16_t* out = B.dw2 + (size_t)e * d * I + (size_t)n0 * I;
   auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
-    tile_store_pairs<TL>(acc, TL::BM, [&](int row) { return out + (size_t)row * I + (cb + c) * TL::BN; });
+    tile_store_full<TL>(acc, [&](int wm) { return out + (size_t)(wm * TL::WM) * I + (cb + c) * TL::BN; }, I);
   };
   if (M == 0) {
     f32x16_t zero[TL::MI][TL::NJ] = {};
@@ -273,10 +273,10 @@ __device__ void bwd_dw13_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
   bf16_t* o1 = B.dw1 + (size_t)e * I * d + (size_t)i0 * d;
   bf16_t* o3 = B.dw3 + (size_t)e * I * d + (size_t)i0 * d;
+  // wave row block 0 holds the dW1 rows, block 1 the dW3 rows
+  static_assert(TL::WM == TL::BM / 2, "one wave row block per gradient");
   auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
-    tile_store_pairs<TL>(acc, TL::BM, [&](int row) {
-      return (row < TL::BM / 2 ? o1 + (size_t)row * d : o3 + (size_t)(row - TL::BM / 2) * d) + (cb + c) * TL::BN;
-    });
+    tile_store_full<TL>(acc, [&](int wm) { return (wm ? o3 : o1) + (cb + c) * TL::BN; }, d);
   };
   if (M == 0) {
     f32x16_t zero[TL::MI][TL::NJ] = {};

@@ -12,6 +12,10 @@ Workloads (sizes from the MoE shapes the method is measured on):
   dsv3-mxfp8         T=8192, otherwise as dsv3-bf16, expert GEMMs in MXFP8
   dsv3-fwdbwd-zipf   as dsv3-bf16 plus a router bias giving Zipf(1.2) expert
                      loads, and an upstream gradient dY for the backward
+  dsv3-ep8-share     one GPU's share of the DeepSeek-V3 layer split 8 ways by
+                     expert: E=32 local experts, ~1024 rows each (a
+                     matrix-core-bound shape; not one of the five parity
+                     configurations)
 
 Distributions: tiny-fp32 draws everything from N(0, 0.02^2).  The others draw
 X ~ N(0,1), W1 and W3 ~ N(0, 1/d), W2 ~ N(0, 1/I) (fan-in scaling keeps every
@@ -86,6 +90,8 @@ WORKLOADS = {
                            experts="mxfp8"),
     "dsv3-fwdbwd-zipf": Workload("dsv3-fwdbwd-zipf", T=4096, d=7168, E=256,
                                  k=8, I=2048, zipf_s=1.2, backward=True),
+    "dsv3-ep8-share": Workload("dsv3-ep8-share", T=4096, d=7168, E=32, k=8,
+                               I=2048),
 }
 
 _TAGS = {"x": 1, "wr": 2, "w1": 3, "w3": 4, "w2": 5, "dy": 6, "zipf": 7,

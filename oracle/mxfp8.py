@@ -165,15 +165,30 @@ def fake_quant(v):
     return out.reshape(v.shape)
 
 
+def expert_ffn_mxfp8(xq_rows, w1, w3, w2):
+    """One expert's SwiGLU FFN on rows that are already quantised (xq_rows,
+    fp64 values of MXFP8 codes): W1/W3 quantised along d and W2 along I
+    (blocks along each GEMM's contraction axis), H quantised along I after
+    SwiGLU.  Returns (A, B, H, Yp) with H before its quantisation."""
+    from . import moe as M
+    w1q = fake_quant(w1)          # [I, d], blocks along d
+    w3q = fake_quant(w3)
+    w2q = fake_quant(w2)          # [d, I], blocks along I
+    A = xq_rows @ w1q.T
+    B = xq_rows @ w3q.T
+    h = M.silu(A) * B
+    return A, B, h, fake_quant(h) @ w2q.T
+
+
 def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
     """The forward with the expert GEMMs in MXFP8.
 
     MoK flash §02 folds quantisation into dispatch, the grouped GEMM and
     SwiGLU.  Quantised here: each gathered token row along d (the dispatch),
     W1/W3 along d and W2 along I (blocks along the contraction axis of each
-    GEMM), and H along I after SwiGLU.  Routing and the weighted combine stay
-    in high precision.  Every product of dequantised operands is exact in
-    fp64 before summation.
+    GEMM), and H along I after SwiGLU (expert_ffn_mxfp8).  Routing and the
+    weighted combine stay in high precision.  Every product of dequantised
+    operands is exact in fp64 before summation.
     """
     from . import moe as M
     T = np.shape(x)[0]
@@ -193,14 +208,7 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        w1q = fake_quant(w1[e])          # [I, d], blocks along d
-        w3q = fake_quant(w3[e])
-        w2q = fake_quant(w2[e])          # [d, I], blocks along I
-        A = xp[lo:hi] @ w1q.T
-        B = xp[lo:hi] @ w3q.T
-        h = M.silu(A) * B
-        H[lo:hi] = h
-        Yp[lo:hi] = fake_quant(h) @ w2q.T
+        _, _, H[lo:hi], Yp[lo:hi] = expert_ffn_mxfp8(xp[lo:hi], w1[e], w3[e], w2[e])
     y = M.combine(Yp, gate, inv, T, k)
     return dict(logits=logits, topk_idx=idx, gate=gate, counts=counts,
                 offsets=offsets, perm=perm, inv=inv, src=src, H=H, Yp=Yp,
