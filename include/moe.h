@@ -84,7 +84,7 @@ typedef struct moe_desc {
   int32_t expert_dtype;  /* MOE_F32 (needs act F32), MOE_BF16 or MOE_MXFP8 */
   int32_t score;         /* moe_score                                       */
   int32_t renorm;        /* 1: gates renormalised over the chosen k          */
-  int32_t fused;         /* 1: one persistent launch driven by device-side
+  int32_t fused;         /* 1: persistent launches driven by device-side
                             ready counters; 0: one launch per step          */
   int32_t stage_rows;    /* rows per ready counter (the minibatch handed to
                             the expert GEMM): 0 = auto, else 128 or 256     */
@@ -96,17 +96,15 @@ typedef struct moe_desc {
 #define MOE_FLAG_DIRECT_PULL 0x1u  /* fused bf16 forward: the up-projection
                                       reads token rows from X through the
                                       layout instead of a staged copy       */
-#define MOE_FLAG_PERSISTENT_SPLIT 0x2u /* fused forward: run the persistent
-                                      scheduler as one launch per phase
-                                      group instead of one launch for all
-                                      (the fused backward always does so
-                                      unless one of the two flags below
-                                      is set)                            */
+#define MOE_FLAG_PERSISTENT_SPLIT 0x2u /* fused forward: one persistent
+                                      launch per phase group (routing and
+                                      gather | up projection | down
+                                      projection | combine)              */
 #define MOE_FLAG_PERSISTENT_WGRAD_APART 0x4u /* fused backward: two
                                       persistent launches, the weight
                                       gradients after the rest           */
-#define MOE_FLAG_PERSISTENT_SINGLE 0x8u /* fused backward: every phase in
-                                      one persistent launch              */
+#define MOE_FLAG_PERSISTENT_SINGLE 0x8u /* fused forward and backward: every
+                                      phase in one persistent launch     */
 #define MOE_FLAG_SPIN_LIMIT_TINY 0x100u /* test only: bounded waits give up
                                       after a few polls (exercises the
                                       MOE_ERR_TIMEOUT path)                 */
@@ -210,12 +208,13 @@ MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K,
  *   y     act [T, d] output: y[t] = sum_j gate[t,j] * FFN_{idx[t,j]}(x[t]),
  *         FFN_e(v) = (silu(v W1_e^T) * (v W3_e^T)) W2_e^T;
  *   saved optional outputs (may be NULL).
- * With desc->fused = 1 the layer is one persistent launch (after a small
- * clearing launch): routing, counting, layout, gather, the two grouped
- * GEMMs and the combine are tasks claimed from device-side queues phase by
- * phase; a GEMM tile starts as soon as the ready counter of its rows shows
- * them staged (MoK flash §02).  MOE_FLAG_PERSISTENT_SPLIT runs the same
- * scheduler as one launch per phase group. */
+ * With desc->fused = 1 the layer runs as tasks claimed from device-side
+ * queues phase by phase (after a small clearing launch), in three
+ * persistent launches: routing, counting, layout, gather and the up
+ * projection, where an up-projection tile starts as soon as the ready
+ * counter of its rows shows them staged (MoK flash §02); the down
+ * projection; the combine.  MOE_FLAG_PERSISTENT_SINGLE puts all phases in
+ * one launch, MOE_FLAG_PERSISTENT_SPLIT gives each phase group its own. */
 MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
                 const float* bias, const moe_weights* w, void* y,
                 const moe_saved* saved, void* workspace,
@@ -232,8 +231,9 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
  *   dgate float [T, k] output, dL/dgate.
  * With desc->fused = 1 the phases (setup, rowprep and pulls, dH, dW2, dXp,
  * dW1/dW3, dX) run through the persistent scheduler, one launch per phase
- * unless MOE_FLAG_PERSISTENT_SINGLE or MOE_FLAG_PERSISTENT_WGRAD_APART is
- * set; with fused = 0 each phase is an ordinary grid.  Needs bf16 with
+ * (setup and pulls together) unless MOE_FLAG_PERSISTENT_SINGLE or
+ * MOE_FLAG_PERSISTENT_WGRAD_APART is set;
+ * with fused = 0 each phase is an ordinary grid.  Needs bf16 with
  * d % 256 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED). */
 MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
                  const moe_weights* w, const moe_saved* saved, void* dx,

@@ -126,12 +126,17 @@ __device__ __forceinline__ bool wait_geq(const int* ctr, int target, const WaitC
 }
 
 // Block-uniform: publishes every prior global store of the workgroup at
-// agent scope, then adds `v` to *ctr.
+// agent scope, then adds `v` to *ctr.  The agent-scope release writes the
+// XCD's L2 back, which is costly; REL = false skips it and is correct only
+// when every reader of the published data runs in a later kernel launch
+// (the end of a kernel writes the L2s back and the next launch starts with
+// an acquire).  The count itself is still raised, atomically at agent scope.
+template <bool REL = true>
 __device__ __forceinline__ void signal_add(int* ctr, int v) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (REL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(256) k_gather(Fwd F) {
   __shared__ int ssrc[256];
   const int tile = blockIdx.x;
   if (tile >= *F.s.n_mtiles) return;
-  gather_tile<Act, COPY>(F, tile, ssrc);
+  gather_tile<Act, COPY, false>(F, tile, ssrc);
 }
 
 template <class Act, class TL>
@@ -266,6 +266,9 @@ __global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F,
 // the per-XCD phase queues (sched.h); the projection tiles are enumerated
 // in the grouped raster, 64 consecutive tasks per XCD queue block.  Each
 // task waits on the counters its inputs raise.
+// A task's signal releases its stores at agent scope only when a phase
+// that reads them runs in this launch (MASK); readers in later launches see
+// them through the kernel boundary.
 template <class Act, class TL, unsigned MASK>
 __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F) {
   extern __shared__ __align__(16) char smem[];
@@ -309,36 +312,36 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F)
     if ((MASK & 1u) && ph == 0) {
       if (TL::kMX && t >= F.nb * F.S) {
         quant_tokens(F, t - F.nb * F.S);
-        signal_add(F.s.q_done, 1);
+        signal_add<(MASK & 0x18u) != 0>(F.s.q_done, 1);  // read by gather, g1
       } else {
         router_partial<Act>(F, t);
-        signal_add(&F.s.r1_cnt[t / F.S], 1);
+        signal_add<(MASK & 2u) != 0>(&F.s.r1_cnt[t / F.S], 1);
       }
     } else if ((MASK & 2u) && ph == 1) {
       if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
-      signal_add(F.s.r2_done, 1);
+      signal_add<(MASK & 0x4Cu) != 0>(F.s.r2_done, 1);  // read by scan, gather, combine
     } else if ((MASK & 4u) && ph == 2) {
       if (wait_geq(F.s.r2_done, F.nb, W, &s_flag)) layout_scan(F, (int*)smem);
-      signal_add(F.s.scan_done, 1);
+      signal_add<(MASK & 0x78u) != 0>(F.s.scan_done, 1);
     } else if ((MASK & 8u) && ph == 3) {
       // MXFP8: a row tile is ready once the codes of x are complete too
       if (TL::kMX && !wait_geq(F.s.q_done, F.nb, W, &s_flag)) continue;
       if (F.direct)
-        gather_tile<Act, false>(F, t, (int*)smem);
+        gather_tile<Act, false, (MASK & 0x50u) != 0>(F, t, (int*)smem);  // read by g1, combine
       else
-        gather_tile<Act, true>(F, t, (int*)smem);
+        gather_tile<Act, true, (MASK & 0x50u) != 0>(F, t, (int*)smem);
     } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * F.nN1) continue;
       int tile, nt;
       raster_decode(F.etile, F.E, F.nN1, t, tile, nt);
       if (wait_geq(&F.s.ready[tile], 1, W, &s_flag)) run_g1<Act, TL>(F, tile, nt, smem);
-      signal_add(&F.s.h_cnt[tile], 1);
+      signal_add<(MASK & 32u) != 0>(&F.s.h_cnt[tile], 1);
     } else if ((MASK & 32u) && ph == 5) {
       if (t >= s_nmt * F.nN2) continue;
       int tile, nt;
       raster_decode(F.etile, F.E, F.nN2, t, tile, nt);
       if (wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) run_g2<Act, TL>(F, tile, nt, smem);
-      signal_add(F.s.g2_done, 1);
+      signal_add<(MASK & 64u) != 0>(F.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
     }
@@ -454,10 +457,10 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if ((MASK & 1u) && ph == 0) {
       bwd_setup(B, (int*)smem);
-      signal_add(B.s.scan_done, 1);
+      signal_add<(MASK & 0x7Cu) != 0>(B.s.scan_done, 1);
     } else if ((MASK & 2u) && ph == 1) {
       bwd_rowprep(B, t);
-      signal_add(B.s.scan_done, 1);
+      signal_add<(MASK & 0x7Cu) != 0>(B.s.scan_done, 1);
     } else if ((MASK & 0x28u) && (ph == 3 || ph == 5)) {
       // the expert order comes from setup
       if (!wait_geq(B.s.scan_done, 1 + B.nRP, W, &s_flag)) continue;
@@ -476,14 +479,16 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdh, t, tile, nt);
       bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
-      signal_add(&B.s.h_cnt[tile], 1);
-      signal_add(&B.s.aux1[B.tile_e[tile]], 1);
+      // dA|dB and the dgate partials are read by dxp, dw13 and dx; the
+      // first signal publishes them, the second has nothing new to publish
+      signal_add<(MASK & 0x70u) != 0>(&B.s.h_cnt[tile], 1);
+      signal_add<false>(&B.s.aux1[B.tile_e[tile]], 1);
     } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * B.nNdx) continue;
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdx, t, tile, nt);
       if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
-      signal_add(B.s.g2_done, 1);
+      signal_add<(MASK & 64u) != 0>(B.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(B.s.g2_done, s_nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
     }
@@ -559,6 +564,7 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
     return launch_status();
   }
   if (D->fused) {
+    if (D->flags & MOE_FLAG_PERSISTENT_SINGLE) return launch_fused_fwd<Act, TL, 0x7Fu>(D, F, smem, st);
     if (D->flags & MOE_FLAG_PERSISTENT_SPLIT) {
       // the same persistent scheduler, one launch per phase group
       int rc = launch_fused_fwd<Act, TL, 0x0Fu>(D, F, smem, st);
@@ -567,7 +573,15 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
       if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, smem, st);
       return rc;
     }
-    return launch_fused_fwd<Act, TL, 0x7Fu>(D, F, smem, st);
+    // Routing through the up projection in one launch (each up-projection
+    // tile starts once its rows are staged), then the down projection, then
+    // the combine: a down-projection tile would need every up-projection
+    // tile of its rows released at agent scope, an L2 write-back per tile,
+    // which costs more on this chip than the launch boundary.
+    int rc = launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st);
+    if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
+    if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, smem, st);
+    return rc;
   }
   hipLaunchKernelGGL(k_router_partial<Act>, dim3(p.nb * p.S), dim3(256), 0, st, F);
   if (!set_smem(k_router_topk<true>, kTopkSmem)) return MOE_ERR_HIP;
@@ -612,9 +626,12 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes;
   if (D->fused) {
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
-    // one persistent launch per phase group unless asked for a single
-    // launch: every backward task together does not fit two workgroups'
-    // registers per CU (MOE_FLAG_PERSISTENT_SINGLE runs it anyway)
+    // By default one persistent launch per phase (setup and row pulls
+    // together): no phase reads what another phase of its launch writes, so
+    // no task needs the agent-scope release, and each launch's registers
+    // are those of one task kind.  Every backward task in one launch does
+    // not fit two workgroups' registers per CU (MOE_FLAG_PERSISTENT_SINGLE
+    // runs it anyway).
     if (!(D->flags & (MOE_FLAG_PERSISTENT_SINGLE | MOE_FLAG_PERSISTENT_WGRAD_APART))) {
       int rc = launch_fused_bwd<0x03u>(D, B, smem, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, smem, st);

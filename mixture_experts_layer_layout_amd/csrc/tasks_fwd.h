@@ -389,8 +389,9 @@ __device__ __forceinline__ int row_source(const Fwd& F, int e, int r) {
 }
 
 // Rows of one tile: writes perm, inv, src (and the per-row gate), then (if
-// COPY) pulls the token rows into expert order.  Raises ready[tile].
-template <class Act, bool COPY>
+// COPY) pulls the token rows into expert order.  Raises ready[tile] (with
+// the agent-scope release when REL: a reader runs in the same launch).
+template <class Act, bool COPY, bool REL>
 __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
   const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
   __syncthreads();
@@ -416,7 +417,7 @@ __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
       for (int v = lane; v < nvec; v += 64) dst[v] = s[v];
     }
   }
-  signal_add(&F.s.ready[tile], 1);
+  signal_add<REL>(&F.s.ready[tile], 1);
 }
 
 // ---------------------------------------------------------------- GEMMs

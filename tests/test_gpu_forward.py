@@ -111,7 +111,7 @@ def test_empty_batch():
     assert host(sv["counts"]).sum() == 0 and np.all(host(sv["offsets"]) == 0)
 
 
-@pytest.mark.parametrize("flags", ["PERSISTENT_SPLIT", "DIRECT_PULL"])
+@pytest.mark.parametrize("flags", ["PERSISTENT_SPLIT", "PERSISTENT_SINGLE", "DIRECT_PULL"])
 def test_forward_persistent_variants_equal_unfused(flags):
     w = SMALL["dsv3-zipf-small"]
     f = getattr(api, "MOE_FLAG_" + flags)
