@@ -266,6 +266,29 @@ def main():
     if saved["status"].item() != 0:
         raise RuntimeError("device status " + api.moe_status_string(saved["status"].item()))
 
+    # the standalone layout and pull gather (moe_layout, moe_gather) on this
+    # step's routing, timed with events on the same stream
+    side = {}
+    if w.experts != "f32":
+        gdesc = layer.desc_for(w, fused=False)
+        xq_ = torch.empty((w.R, w.d), dtype=torch.uint8 if w.experts == "mxfp8" else torch.bfloat16,
+                          device="cuda")
+        xs_ = torch.empty((w.R, w.d // 32), dtype=torch.uint8, device="cuda") if w.experts == "mxfp8" else None
+        lay = {n: torch.empty_like(saved[n]) for n in ("counts", "offsets", "perm", "inv")}
+        lws = layer.workspace(gdesc)
+        reps = 20
+        for name, fn in (("layout", lambda: api.moe_layout(gdesc, saved["topk_idx"], lay["counts"], lay["offsets"],
+                                                           lay["perm"], lay["inv"], None, lws, stream)),
+                         ("gather", lambda: api.moe_gather(gdesc, dev["x"], saved["perm"], xq_, xs_, stream))):
+            fn()
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            side[name] = a.elapsed_time(b) / reps
+        del xq_, xs_, lay, lws
     fwd_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
     bwd_ms = sum(b.elapsed_time(c) for _, b, c in marks) / args.steps if w.backward else 0.0
     ms_step = elapsed * 1e3 / args.steps
@@ -286,6 +309,13 @@ def main():
               "forward_hbm_frac": round(algorithmic_bytes(w, counts, "forward") / (fwd_ms * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
               "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())}
+    if side:
+        # gather: X read once, the routed rows written (MXFP8: codes + scales)
+        gbytes = w.T * w.d * 2 + (w.R * w.d * (1 + 1 / 32) if w.experts == "mxfp8" else w.R * w.d * 2)
+        phases["layout_us"] = round(side["layout"] * 1e3, 1)
+        phases["gather_ms"] = round(side["gather"], 4)
+        phases["gather_gbs"] = round(gbytes / (side["gather"] * 1e-3) / 1e9, 1)
+        phases["gather_hbm_frac"] = round(gbytes / (side["gather"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

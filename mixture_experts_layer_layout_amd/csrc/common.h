@@ -141,6 +141,31 @@ __device__ __forceinline__ void signal_add(int* ctr, int v) {
   }
 }
 
+// ---------------------------------------------------------------- copies
+// One wave copies one row of nvec 16-byte vectors: every lane issues up to
+// kCopyUnroll loads before its first store (the source and destination may
+// alias as far as the compiler knows, so a plain loop would wait for each
+// load in turn).  f(v, u) may transform each vector before it is stored.
+constexpr int kCopyUnroll = 16;  // a whole d = 7168 bf16 row (14 vectors a lane) in one batch
+template <class F>
+__device__ __forceinline__ void wave_copy_row(const uint4* __restrict__ src, uint4* __restrict__ dst, int nvec,
+                                              F f) {
+  const int lane = threadIdx.x & 63;
+  for (int v0 = lane; v0 < nvec; v0 += 64 * kCopyUnroll) {
+    uint4 t[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (v0 + 64 * u < nvec) t[u] = src[v0 + 64 * u];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (v0 + 64 * u < nvec) dst[v0 + 64 * u] = f(v0 + 64 * u, t[u]);
+  }
+}
+
+struct CopyAsIs {
+  __device__ __forceinline__ uint4 operator()(int, uint4 u) const { return u; }
+};
+
 // ---------------------------------------------------------------- misc
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -117,6 +117,9 @@ struct KCols {
   S kscale;
   int coff;
   int nk_ = 0;  // stages per column tile when streamed (tile_stream), else 0
+  // position of the last prepared step: step pj_ = column tile pc_, stage
+  // ps_ (prep is called with steps that grow by 0 or 1 at a time)
+  int pj_ = -1, pc_ = 0, ps_ = -1;
   const bf16_t* p[KK];
   float s[KK], sl[kPrefetch][KK];
   uint4 v[kPrefetch][KK];
@@ -125,8 +128,21 @@ struct KCols {
     coff = nb * 8 + (nb >= ROWS / 16 ? half_off : 0);
   }
   __device__ __forceinline__ void prep(int kt) {
-    const int c = nk_ ? kt / nk_ : 0;
-    const int k0 = (kt - c * nk_) * 64 + (threadIdx.x % KG) * KK;
+    if (nk_ == 0) {
+      pc_ = 0;
+      ps_ = kt;
+    } else if (kt == pj_ + 1) {
+      if (++ps_ == nk_) {
+        ps_ = 0;
+        ++pc_;
+      }
+    } else if (kt != pj_) {
+      pc_ = kt / nk_;
+      ps_ = kt - pc_ * nk_;
+    }
+    pj_ = kt;
+    const int c = pc_;
+    const int k0 = ps_ * 64 + (threadIdx.x % KG) * KK;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       p[kk] = kptr(k0 + kk, c);
@@ -405,11 +421,14 @@ __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A,
 }
 
 // Writes a tile whose rows are all valid as bf16 straight from registers,
-// two columns per 4-byte store: lane pairs swap values so the even lane of
-// a pair stores (row of r, its two columns) and the odd lane (row of r+1,
-// the same two columns).  No per-row test and one address computation per
-// lane: wave row block wm (tile rows wm * WM ..) starts at base(wm),
-// consecutive rows ld elements apart.
+// two columns per 4-byte store: lane pairs swap values (DPP) so the even
+// lane of a pair stores (row of r, its two columns) and the odd lane (row of
+// r+1, the same two columns); one store instruction then covers 64
+// contiguous bytes of each of 4 rows.  No per-row test and one address
+// computation per lane: wave row block wm (tile rows wm * WM ..) starts at
+// base(wm), consecutive rows ld elements apart.  (Storing the tile
+// transposed in registers, 8 bytes per lane over 32 rows per instruction,
+// measured slower: the write path prefers fewer, longer row segments.)
 template <class TL, class BASE>
 __device__ __forceinline__ void tile_store_full(const f32x16_t (&acc)[TL::MI][TL::NJ], BASE base, size_t ld) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

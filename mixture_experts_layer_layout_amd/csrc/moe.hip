@@ -352,13 +352,9 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F)
 template <class Act>
 __global__ void __launch_bounds__(256) k_gather_perm(const Act* __restrict__ x, const int* __restrict__ perm,
                                                      Act* __restrict__ xp, int R, int d, int k) {
-  const int lane = threadIdx.x & 63;
   const int nvec = d * (int)sizeof(Act) / 16;
-  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4) {
-    const uint4* s = (const uint4*)x + (size_t)(perm[r] / k) * nvec;
-    uint4* dst = (uint4*)xp + (size_t)r * nvec;
-    for (int v = lane; v < nvec; v += 64) dst[v] = s[v];
-  }
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4)
+    wave_copy_row((const uint4*)x + (size_t)(perm[r] / k) * nvec, (uint4*)xp + (size_t)r * nvec, nvec, CopyAsIs());
 }
 
 // ------------------------------------------------------------------ backward

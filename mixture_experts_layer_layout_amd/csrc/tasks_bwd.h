@@ -129,17 +129,14 @@ __device__ void bwd_rowprep(const Bwd& B, int task) {
     }
     const uint4* xs = (const uint4*)(B.x + (size_t)t * B.d);
     const uint4* ys = (const uint4*)(B.dy + (size_t)t * B.d);
-    uint4* xd = (uint4*)(B.xp + (size_t)r * B.d);
-    uint4* gd = (uint4*)(B.gg + (size_t)r * B.d);
-    for (int v = lane; v < nvec; v += 64) {
-      xd[v] = xs[v];
-      uint4 u = ys[v];
+    wave_copy_row(xs, (uint4*)(B.xp + (size_t)r * B.d), nvec, CopyAsIs());
+    wave_copy_row(ys, (uint4*)(B.gg + (size_t)r * B.d), nvec, [&](int, uint4 u) {
       uint32_t* w = (uint32_t*)&u;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         w[q] = pack_bf16x2(bf16_to_f32((bf16_t)(w[q] & 0xffff)) * g, bf16_to_f32((bf16_t)(w[q] >> 16)) * g);
-      gd[v] = u;
-    }
+      return u;
+    });
   }
 }
 
@@ -297,40 +294,80 @@ __device__ void bwd_dw13_band(const Bwd& B, int rank, int task, bf16_t* smem) {
 
 // ---------------------------------------------------------------- dx
 // dX[t] = sum_j dXp[inv[t k + j]] (fp32, slot order); dgate from the
-// partial sums in column-tile order.
-__device__ void bwd_dx_tokens(const Bwd& B, int cb) {
+// partial sums in column-tile order.  K as in combine_tokens_k.
+template <int K>
+__device__ void bwd_dx_tokens_k(const Bwd& B, int cb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NR = K ? K : kMaxK;
+  const int k = K ? K : B.k;
   const int nvec = B.d / 8;
   for (int tt = wave; tt < kCombTok; tt += 4) {
     const int t = cb * kCombTok + tt;
     if (t >= B.T) break;
-    int rows[kMaxK];
+    int rows[NR];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) rows[j] = j < B.k ? B.inv[(size_t)t * B.k + j] : 0;
-    if (lane < B.k) {
+    for (int j = 0; j < NR; ++j) rows[j] = j < k ? B.inv[(size_t)t * k + j] : 0;
+    if (lane < k) {
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < NR; ++j)
+        if (j == lane) mine = rows[j];
       float s = 0.0f;
-      for (int p = 0; p < B.nNdh; ++p) s += B.dgp[(size_t)p * B.R + rows[lane]];
-      B.dgate[(size_t)t * B.k + lane] = s;
+      for (int p = 0; p < B.nNdh; ++p) s += B.dgp[(size_t)p * B.R + mine];
+      B.dgate[(size_t)t * k + lane] = s;
     }
-    for (int v = lane; v < nvec; v += 64) {
-      float acc[8];
+    auto put = [&](int v, const float (&acc)[8]) {
+      ((uint4*)B.dx)[(size_t)t * nvec + v] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    };
+    // known k: two vectors per lane per iteration, all row loads up front
+    constexpr int VU = K ? 2 : 1;
+    for (int v0 = lane; v0 < nvec; v0 += 64 * VU) {
+      if constexpr (K != 0) {
+        uint4 u[VU][K];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int h = 0; h < VU; ++h)
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j >= B.k) break;
-        const uint4 u = ((const uint4*)B.dxp)[(size_t)rows[j] * nvec + v];
-        const bf16_t* p = (const bf16_t*)&u;
+          for (int j = 0; j < K; ++j)
+            if (v0 + 64 * h < nvec) u[h][j] = ((const uint4*)B.dxp)[(size_t)rows[j] * nvec + v0 + 64 * h];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += bf16_to_f32(p[q]);
+        for (int h = 0; h < VU; ++h) {
+          if (v0 + 64 * h >= nvec) break;
+          float acc[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            const bf16_t* p = (const bf16_t*)&u[h][j];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] += bf16_to_f32(p[q]);
+          }
+          put(v0 + 64 * h, acc);
+        }
+      } else {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+          const uint4 u = ((const uint4*)B.dxp)[(size_t)rows[j] * nvec + v0];
+          const bf16_t* p = (const bf16_t*)&u;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] += bf16_to_f32(p[q]);
+        }
+        put(v0, acc);
       }
-      uint4 o;
-      o.x = pack_bf16x2(acc[0], acc[1]);
-      o.y = pack_bf16x2(acc[2], acc[3]);
-      o.z = pack_bf16x2(acc[4], acc[5]);
-      o.w = pack_bf16x2(acc[6], acc[7]);
-      ((uint4*)B.dx)[(size_t)t * nvec + v] = o;
     }
+  }
+}
+
+__device__ void bwd_dx_tokens(const Bwd& B, int cb) {
+  switch (B.k) {
+    case 1: bwd_dx_tokens_k<1>(B, cb); break;
+    case 2: bwd_dx_tokens_k<2>(B, cb); break;
+    case 4: bwd_dx_tokens_k<4>(B, cb); break;
+    case 6: bwd_dx_tokens_k<6>(B, cb); break;
+    case 8: bwd_dx_tokens_k<8>(B, cb); break;
+    default: bwd_dx_tokens_k<0>(B, cb); break;
   }
 }
 

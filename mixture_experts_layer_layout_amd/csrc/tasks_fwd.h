@@ -407,15 +407,12 @@ __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
   }
   __syncthreads();
   if (COPY) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;
     const int nvec = F.d * (int)sizeof(Act) / 16;
     const uint4* X = (const uint4*)F.x;
     uint4* XP = (uint4*)F.xp;
-    for (int i = wave; i < n; i += 4) {
-      const uint4* s = X + (size_t)ssrc[i] * nvec;
-      uint4* dst = XP + (size_t)(r0 + i) * nvec;
-      for (int v = lane; v < nvec; v += 64) dst[v] = s[v];
-    }
+    for (int i = wave; i < n; i += 4)
+      wave_copy_row(X + (size_t)ssrc[i] * nvec, XP + (size_t)(r0 + i) * nvec, nvec, CopyAsIs());
   }
   signal_add<REL>(&F.s.ready[tile], 1);
 }
@@ -527,38 +524,84 @@ __device__ void g2_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
 
 // ---------------------------------------------------------------- combine
 // y[t] = sum_j gate[t,j] * yp[inv[t*k+j]], fp32 accumulation in slot order.
-template <class Act>
-__device__ void combine_tokens(const Fwd& F, int cb) {
+// K = k when known at compile time (every row load of a vector is issued
+// before the first one is used), 0 for any k up to kMaxK.
+template <class Act, int K>
+__device__ void combine_tokens_k(const Fwd& F, int cb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int EPV = 16 / sizeof(Act);  // elements per 16-byte vector
+  constexpr int NR = K ? K : kMaxK;
+  const int k = K ? K : F.k;
   const int nvec = F.d / EPV;
   for (int tt = wave; tt < kCombTok; tt += 4) {
     const int t = cb * kCombTok + tt;
     if (t >= F.T) break;
-    int rows[kMaxK];
-    float g[kMaxK];
+    int rows[NR];
+    float g[NR];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      rows[j] = j < F.k ? F.inv[(size_t)t * F.k + j] : 0;
-      g[j] = j < F.k ? F.gate[(size_t)t * F.k + j] : 0.0f;
+    for (int j = 0; j < NR; ++j) {
+      rows[j] = j < k ? F.inv[(size_t)t * k + j] : 0;
+      g[j] = j < k ? F.gate[(size_t)t * k + j] : 0.0f;
     }
-    for (int v = lane; v < nvec; v += 64) {
-      float acc[EPV];
+    // known k: two vectors per lane per iteration, all 2k row loads issued
+    // before the first is used
+    constexpr int VU = K ? 2 : 1;
+    for (int v0 = lane; v0 < nvec; v0 += 64 * VU) {
+      if constexpr (K != 0) {
+        uint4 u[VU][K];
 #pragma unroll
-      for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;
+        for (int h = 0; h < VU; ++h)
 #pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j >= F.k) break;
-        const uint4 u = ((const uint4*)F.yp)[(size_t)rows[j] * nvec + v];
-        const Act* p = (const Act*)&u;
+          for (int j = 0; j < K; ++j)
+            if (v0 + 64 * h < nvec) u[h][j] = ((const uint4*)F.yp)[(size_t)rows[j] * nvec + v0 + 64 * h];
 #pragma unroll
-        for (int q = 0; q < EPV; ++q) acc[q] = fmaf(g[j], Elem<Act>::to_f32(p[q]), acc[q]);
+        for (int h = 0; h < VU; ++h) {
+          if (v0 + 64 * h >= nvec) break;
+          float acc[EPV];
+#pragma unroll
+          for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < K; ++j) {
+            const Act* p = (const Act*)&u[h][j];
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) acc[q] = fmaf(g[j], Elem<Act>::to_f32(p[q]), acc[q]);
+          }
+          uint4 o;
+          Act* po = (Act*)&o;
+#pragma unroll
+          for (int q = 0; q < EPV; ++q) po[q] = Elem<Act>::from_f32(acc[q]);
+          ((uint4*)F.y)[(size_t)t * nvec + v0 + 64 * h] = o;
+        }
+      } else {
+        const int v = v0;
+        float acc[EPV];
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+          const uint4 u = ((const uint4*)F.yp)[(size_t)rows[j] * nvec + v];
+          const Act* p = (const Act*)&u;
+#pragma unroll
+          for (int q = 0; q < EPV; ++q) acc[q] = fmaf(g[j], Elem<Act>::to_f32(p[q]), acc[q]);
+        }
+        uint4 o;
+        Act* po = (Act*)&o;
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) po[q] = Elem<Act>::from_f32(acc[q]);
+        ((uint4*)F.y)[(size_t)t * nvec + v] = o;
       }
-      uint4 o;
-      Act* po = (Act*)&o;
-      for (int q = 0; q < EPV; ++q) po[q] = Elem<Act>::from_f32(acc[q]);
-      ((uint4*)F.y)[(size_t)t * nvec + v] = o;
     }
+  }
+}
+
+template <class Act>
+__device__ void combine_tokens(const Fwd& F, int cb) {
+  switch (F.k) {
+    case 1: combine_tokens_k<Act, 1>(F, cb); break;
+    case 2: combine_tokens_k<Act, 2>(F, cb); break;
+    case 4: combine_tokens_k<Act, 4>(F, cb); break;
+    case 6: combine_tokens_k<Act, 6>(F, cb); break;
+    case 8: combine_tokens_k<Act, 8>(F, cb); break;
+    default: combine_tokens_k<Act, 0>(F, cb); break;
   }
 }
 
