@@ -366,13 +366,14 @@ __device__ __forceinline__ void tile_visit_pairs(const f32x16_t (&acc)[TL::MI][T
 
 // ---------------------------------------------------------------- stream
 // nc output tiles that share their A rows, each over nk K-stages, run as one
-// stream of nc * nk steps (step j = column tile j / nk, stage j % nk): the
-// two-stage prefetch runs across tile boundaries, so the next tile's loads
-// overlap this tile's MFMAs and stores.  After the last stage of column tile
-// c, epi(c, acc) writes the tile and the accumulators restart from zero.
-// The loaders' prep(j) must map the step to (c, stage) (KCols::nk_).
+// stream of nc * nk steps (step j = column tile c = j / nk, stage s =
+// j % nk, both advanced without division): the register prefetch runs
+// across tile boundaries, so the next tile's loads overlap this tile's
+// MFMAs and stores.  After the last stage of column tile c, epi(c, acc)
+// writes the tile and the accumulators restart from zero.  The loaders'
+// prep(j) must map the step to (c, stage) (KCols::nk_).
 template <int CUR, class TL, class LA, class LB, class EPI>
-__device__ __forceinline__ void stream_step(int j, int nk, int last, bf16_t* As, bf16_t* Bs,
+__device__ __forceinline__ void stream_step(int j, int s, int c, int nk, int last, bf16_t* As, bf16_t* Bs,
                                             f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B, EPI& epi) {
   constexpr int RB = kPrefetch == 2 ? CUR : 0;
   constexpr int SB = kPrefetch == 2 ? (CUR ^ 1) : 0;
@@ -385,8 +386,8 @@ __device__ __forceinline__ void stream_step(int j, int nk, int last, bf16_t* As,
   __builtin_amdgcn_sched_barrier(0);
   A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
   B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);
-  if ((j + 1) % nk == 0) {
-    epi(j / nk, acc);
+  if (s == nk - 1) {
+    epi(c, acc);
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
@@ -399,6 +400,7 @@ __device__ __forceinline__ void stream_step(int j, int nk, int last, bf16_t* As,
 
 template <class TL, class LA, class LB, class EPI>
 __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A, LB& B, EPI epi) {
+  static_assert(!TL::kMX, "bf16 tiles");
   f32x16_t acc[TL::MI][TL::NJ];
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i)
@@ -412,12 +414,20 @@ __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A,
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
   mainloop_prologue(last, As, Bs, A, B);
-  int j = 0;
+  int j = 0, s = 0, c = 0;
+  auto advance = [&] {
+    if (++s == nk) {
+      s = 0;
+      ++c;
+    }
+  };
   for (; j + 1 < total; j += 2) {
-    stream_step<0, TL>(j, nk, last, As, Bs, acc, A, B, epi);
-    stream_step<1, TL>(j + 1, nk, last, As, Bs, acc, A, B, epi);
+    stream_step<0, TL>(j, s, c, nk, last, As, Bs, acc, A, B, epi);
+    advance();
+    stream_step<1, TL>(j + 1, s, c, nk, last, As, Bs, acc, A, B, epi);
+    advance();
   }
-  if (j < total) stream_step<0, TL>(j, nk, last, As, Bs, acc, A, B, epi);
+  if (j < total) stream_step<0, TL>(j, s, c, nk, last, As, Bs, acc, A, B, epi);
 }
 
 // Writes a tile whose rows are all valid as bf16 straight from registers,
