@@ -59,6 +59,7 @@ static_assert(kPrefetch == 1 || kPrefetch == 2, "prefetch distance 1 or 2");
 template <int BM_, int BN_>
 struct Tile {
   static constexpr bool kMX = false;
+  static constexpr bool kDMA = false;
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NJ = WN / 32;

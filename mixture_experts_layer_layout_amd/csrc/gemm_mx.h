@@ -34,6 +34,7 @@ namespace moe {
 template <int BM_, int BN_>
 struct TileMX {
   static constexpr bool kMX = true;
+  static constexpr bool kDMA = false;
   static constexpr int BM = BM_, BN = BN_;
   static_assert(BM + BN == kThreads, "one scale row per thread");
   static constexpr int WM = BM / 2, WN = BN / 2;

@@ -54,8 +54,11 @@ int make_plan(const moe_desc* D, Plan* p) {
     p->nN2 = d / 64;
   } else {
     p->BM = D->stage_rows ? D->stage_rows : 128;
-    p->nN1 = I / (TileB128::BN / 2);
-    p->nN2 = d / TileB128::BN;
+    // column tiles: the bf16 forward with 128-row tiles uses the 256-wide
+    // direct-to-LDS tile, the others 128-wide tiles
+    const int bn = (!p->mxfp8 && p->BM == 128) ? TileD256::BN : TileB128::BN;
+    p->nN1 = I / (bn / 2);
+    p->nN2 = d / bn;
   }
   p->nC = cdiv(T, kCombTok);
   // row tiles of the forward (BM rows) and of the backward (TileDH::BM rows)
@@ -182,6 +185,14 @@ __global__ void k_zero(int* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// Workgroups per CU a tile's kernel is compiled for: two for the 128-row
+// register-staged tiles, one for 256-row tiles and for the direct-to-LDS
+// ring (its LDS holds one).
+template <class TL>
+constexpr int tile_occupancy() {
+  return (TL::BM == 128 && !TL::kDMA) ? 2 : 1;
+}
+
 // Spreads consecutive logical tiles over one XCD: hardware dispatches
 // workgroup b to XCD b % 8, so logical tile ranges stay in one L2.
 __device__ __forceinline__ int xcd_remap(int b, int n) {
@@ -238,7 +249,7 @@ __device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* sme
 __global__ void __launch_bounds__(256) k_quant_tokens(Fwd F) { quant_tokens(F, blockIdx.x); }
 
 template <class Act, class TL>
-__global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g1(Fwd F) {
+__global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_g1(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= *F.s.n_mtiles * F.nN1) return;
@@ -248,7 +259,7 @@ __global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g1(Fwd F) {
 }
 
 template <class Act, class TL>
-__global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_g2(Fwd F) {
+__global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_g2(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   if (id >= *F.s.n_mtiles * F.nN2) return;
@@ -270,7 +281,7 @@ __global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F,
 // that reads them runs in this launch (MASK); readers in later launches see
 // them through the kernel boundary.
 template <class Act, class TL, unsigned MASK>
-__global__ void __launch_bounds__(256, TL::BM == 128 ? 2 : 1) k_fused_fwd(Fwd F) {
+__global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   __shared__ Claim c;
   __shared__ int s_flag;
@@ -771,7 +782,7 @@ int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float
   }
   if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st);
   if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st);
-  return forward_impl<bf16_t, TileB128>(p, desc, F, st);
+  return forward_impl<bf16_t, TileD256>(p, desc, F, st);
 }
 
 int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_weights* w, const moe_saved* saved,

@@ -21,8 +21,11 @@
 //   combine         weighted merge back into token order (§01, §03)
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_bf16.h"
+#include "gemm_dma.h"
 #include "gemm_f32.h"
 
 namespace moe {
@@ -32,8 +35,9 @@ constexpr int kCombTok = 8;    // tokens per combine task
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 
-typedef Tile<128, 128> TileB128;  // 64 KB of LDS: two workgroups per CU
+typedef Tile<128, 128> TileB128;   // 64 KB of LDS: two workgroups per CU
 typedef Tile<256, 128> TileB256;
+typedef TileD<128, 256> TileD256;  // direct-to-LDS ring, 144 KB: one workgroup per CU
 
 struct Sync {
   int* queue;    // start of the counter region
@@ -425,8 +429,10 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const bf16_t* W1 = (const bf16_t*)F.w1 + (size_t)e * I * d;
   const bf16_t* W3 = (const bf16_t*)F.w3 + (size_t)e * I * d;
   const int c0 = nt * (TL::BN / 2);
-  KRows<TL::BM> la;
-  KRows<TL::BN> lb;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BM>, KRows<TL::BM>> LA;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BN>, KRows<TL::BN>> LB;
+  LA la;
+  LB lb;
   // rows past the tile's n repeat its last row (their outputs are dropped)
   if (F.direct) {
     const bf16_t* X = (const bf16_t*)F.x;
@@ -441,7 +447,10 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
     return (which ? W3 : W1) + (size_t)(c0 + col) * d;
   });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(d / 64, smem, acc, la, lb);
+  if constexpr (TL::kDMA)
+    tile_mainloop_dma<TL>(d / 64, smem, acc, la, lb);
+  else
+    tile_mainloop<TL>(d / 64, smem, acc, la, lb);
   // H (then the saved pre-activations) staged in LDS, stored 16 bytes a lane
   typedef Staged<TL::BM, TL::BN / 2> St;
   static_assert(St::bytes <= TL::smem_bytes, "SwiGLU staging fits the tile's LDS");
@@ -470,12 +479,17 @@ __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const bf16_t* W2 = (const bf16_t*)F.w2 + (size_t)e * d * I;
   const bf16_t* H = (const bf16_t*)F.h;
   const int c0 = nt * TL::BN;
-  KRows<TL::BM> la;
-  KRows<TL::BN> lb;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BM>, KRows<TL::BM>> LA;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BN>, KRows<TL::BN>> LB;
+  LA la;
+  LB lb;
   la.init([&](int r) -> const bf16_t* { return H + (size_t)(r0 + min(r, n - 1)) * I; });
   lb.init([&](int nr) -> const bf16_t* { return W2 + (size_t)(c0 + nr) * I; });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(I / 64, smem, acc, la, lb);
+  if constexpr (TL::kDMA)
+    tile_mainloop_dma<TL>(I / 64, smem, acc, la, lb);
+  else
+    tile_mainloop<TL>(I / 64, smem, acc, la, lb);
   bf16_t* YP = (bf16_t*)F.yp;
   const Staged<TL::BM, TL::BN> st{smem};
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
