@@ -87,7 +87,8 @@ typedef struct moe_desc {
   int32_t fused;         /* 1: persistent launches driven by device-side
                             ready counters; 0: one launch per step          */
   int32_t stage_rows;    /* rows per ready counter (the minibatch handed to
-                            the expert GEMM): 0 = auto, else 128 or 256     */
+                            the expert GEMM): 0 = auto, else 128 or 256
+                            (MXFP8 experts: 0 or 128)                      */
   int32_t n_workgroups;  /* persistent grid size, 0 = auto (all CUs)       */
   uint32_t flags;        /* MOE_FLAG_* below                                */
 } moe_desc;

@@ -56,6 +56,7 @@ int make_plan(const moe_desc* D, Plan* p) {
     p->BM = D->stage_rows ? D->stage_rows : 128;
     // column tiles: the bf16 forward with 128-row tiles uses the 256-wide
     // direct-to-LDS tile, the others 128-wide tiles
+    if (p->mxfp8 && p->BM != 128) return MOE_ERR_UNSUPPORTED;  // MXFP8 tiles have 128 rows
     const int bn = (!p->mxfp8 && p->BM == 128) ? TileD256::BN : TileB128::BN;
     p->nN1 = I / (bn / 2);
     p->nN2 = d / bn;

@@ -69,9 +69,11 @@ def test_workspace_size_and_validation(lib):
     small = ctypes.c_size_t(0)
     assert lib.moe_workspace_size(ctypes.byref(_desc(T=64, d=256, E=8, k=2, I=128)), ctypes.byref(small)) == 0
     assert 0 < small.value < n.value
-    # invalid descriptors: k > E, k = 0, E too large, bad dtype, bf16 d not a multiple of 256
+    # invalid descriptors: k > E, k = 0, E too large, bad dtype, bf16 d not a multiple of 256,
+    # MXFP8 experts with 256-row stages
     for bad, code in ((dict(k=9, E=8), -1), (dict(k=0), -1), (dict(E=5000), -1), (dict(act_dtype=7), -1),
-                      (dict(d=7000), -2), (dict(stage_rows=64), -2), (dict(act_dtype=0, expert_dtype=1), -2)):
+                      (dict(d=7000), -2), (dict(stage_rows=64), -2), (dict(act_dtype=0, expert_dtype=1), -2),
+                      (dict(expert_dtype=2, stage_rows=256), -2)):
         assert lib.moe_workspace_size(ctypes.byref(_desc(**bad)), ctypes.byref(n)) == code, bad
     assert lib.moe_workspace_size(None, ctypes.byref(n)) == -1
     assert lib.moe_workspace_size(ctypes.byref(_desc()), None) == -1
