@@ -38,6 +38,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// A pointer that is the same in every lane of the wave, moved to scalar
+// registers (the compiler cannot prove it uniform when it derives from
+// values loaded from memory).
+__device__ __forceinline__ void* wave_uniform(void* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer descriptor for raw (untyped) buffer accesses from base: no stride,
+// 2^31 - 1 bytes in range, word 3 = 32-bit data format as gfx9-family
+// parts expect for raw buffer instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+}
+
 // The value of the neighbouring lane (lane ^ 1) through a DPP quad
 // permutation [1,0,3,2] (one VALU instruction, no LDS round trip).
 __device__ __forceinline__ float swap_lane_pair(float v) {

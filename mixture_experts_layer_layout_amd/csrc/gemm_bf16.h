@@ -109,7 +109,7 @@ struct KRows {
 //   half_off  extra element offset for the second half of the tile's rows
 //             (two column ranges of one stored row, e.g. the dA and dB
 //             halves of [dA | dB]); 0 when the rows are contiguous
-template <int ROWS, bool SCALED, class P, class S>
+template <int ROWS, bool SCALED, class P, class S, int NBUF = kPrefetch>
 struct KCols {
   static constexpr int KK = ROWS >= 256 ? 8 : 4;
   static constexpr int KG = 64 / KK;
@@ -122,8 +122,8 @@ struct KCols {
   // ps_ (prep is called with steps that grow by 0 or 1 at a time)
   int pj_ = -1, pc_ = 0, ps_ = -1;
   const bf16_t* p[KK];
-  float s[KK], sl[kPrefetch][KK];
-  uint4 v[kPrefetch][KK];
+  float s[KK], sl[NBUF][KK];
+  uint4 v[NBUF][KK];
   __device__ __forceinline__ KCols(P kp, S ks, int half_off) : kptr(kp), kscale(ks) {
     const int nb = threadIdx.x / KG;
     coff = nb * 8 + (nb >= ROWS / 16 ? half_off : 0);
@@ -204,6 +204,11 @@ struct NoScale {
 template <int ROWS, class P>
 __device__ __forceinline__ KCols<ROWS, false, P, NoScale> kcols(P kptr, int half_off = 0) {
   return KCols<ROWS, false, P, NoScale>(kptr, NoScale(), half_off);
+}
+// the same with two register buffers (tile_band's streamed operand)
+template <int ROWS, class P>
+__device__ __forceinline__ KCols<ROWS, false, P, NoScale, 2> kcols2(P kptr, int half_off = 0) {
+  return KCols<ROWS, false, P, NoScale, 2>(kptr, NoScale(), half_off);
 }
 template <int ROWS, class P, class S>
 __device__ __forceinline__ KCols<ROWS, true, P, S> kcols_scaled(P kptr, S kscale, int half_off = 0) {
@@ -431,31 +436,129 @@ __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A,
   if (j < total) stream_step<0, TL>(j, s, c, nk, last, As, Bs, acc, A, B, epi);
 }
 
+// ---------------------------------------------------------------- band
+// The nc output tiles of a band that share their A rows, when K is only
+// NK = 1 or 2 stages (the weight gradients of experts with at most 128
+// rows): A is loaded into LDS once and stays there, and only B streams,
+// two stages ahead in registers.  Each tile's output is written at the end
+// of its last stage.
+//
+// The point is the order of memory operations.  vmcnt counts loads and
+// stores together, in issue order, so waiting for a load also waits for
+// every store issued before it.  Here the B stage stored to LDS in step j
+// was loaded at the top of step j-1, before that step's output stores, so
+// the wait for it leaves those stores in flight; they have until the wait
+// of step j+1 to complete.  For the compiler to count this exactly, every
+// path into a step must have issued the same operations: the epilogue sits
+// at a fixed place in the unrolled loop, and the steps before the repeating
+// pattern (one step for NK = 1, one tile for NK = 2) are peeled.
+template <int CUR, int S, bool EPI_NOW, class TL, class LB, class EPI>
+__device__ __forceinline__ void band_step(int j, int c, int last, const bf16_t* As, bf16_t* Bs,
+                                          f32x16_t (&acc)[TL::MI][TL::NJ], LB& B, EPI& epi) {
+  B.template load<CUR>(min(j + 2, last));
+  B.prep(min(j + 3, last));
+  __builtin_amdgcn_sched_barrier(0);
+  TL::stage(As + S * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  B.template store<CUR ^ 1>(Bs + (CUR ^ 1) * TL::LDS_B);
+  if (EPI_NOW) {
+    epi(c, acc);
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TL::NJ; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+  }
+  __syncthreads();
+}
+
+// A: the loader of the shared rows (prep(s) with s < NK gives stage s);
+// B: a two-buffer loader (kcols2) whose prep(j) maps step j to column tile
+// j / NK, stage j % NK.  LDS: NK stages of A, then two B stages.
+template <class TL, int NK, class LA, class LB, class EPI>
+__device__ __forceinline__ void tile_band(int nc, bf16_t* smem, LA& A, LB& B, EPI epi) {
+  static_assert(!TL::kMX && !TL::kDMA, "register-staged bf16 tiles");
+  static_assert(NK == 1 || NK == 2, "one or two resident stages");
+  static_assert((size_t)(NK * TL::LDS_A + 2 * TL::LDS_B) * sizeof(bf16_t) <= TL::smem_bytes, "band fits the LDS");
+  f32x16_t acc[TL::MI][TL::NJ];
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int total = nc * NK;
+  if (total <= 0) return;
+  const int last = total - 1;
+  bf16_t* As = smem;
+  bf16_t* Bs = smem + NK * TL::LDS_A;
+  // the LDS may still be read by the previous user
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    A.prep(s);
+    A.template load<0>(s);
+    A.template store<0>(As + s * TL::LDS_A);
+  }
+  B.prep(0);
+  B.template load<0>(0);
+  B.prep(min(1, last));
+  B.template load<1>(min(1, last));
+  B.prep(min(2, last));
+  B.template store<0>(Bs);
+  __syncthreads();
+  if (NK == 1) {
+    band_step<0, 0, true, TL>(0, 0, last, As, Bs, acc, B, epi);
+    int j = 1;
+    for (; j + 1 < total; j += 2) {
+      band_step<1, 0, true, TL>(j, j, last, As, Bs, acc, B, epi);
+      band_step<0, 0, true, TL>(j + 1, j + 1, last, As, Bs, acc, B, epi);
+    }
+    if (j < total) band_step<1, 0, true, TL>(j, j, last, As, Bs, acc, B, epi);
+  } else {
+    band_step<0, 0, false, TL>(0, 0, last, As, Bs, acc, B, epi);
+    band_step<1, 1, true, TL>(1, 0, last, As, Bs, acc, B, epi);
+    for (int c = 1; c < nc; ++c) {
+      band_step<0, 0, false, TL>(2 * c, c, last, As, Bs, acc, B, epi);
+      band_step<1, 1, true, TL>(2 * c + 1, c, last, As, Bs, acc, B, epi);
+    }
+  }
+}
+
 // Writes a tile whose rows are all valid as bf16 straight from registers,
 // two columns per 4-byte store: lane pairs swap values (DPP) so the even
 // lane of a pair stores (row of r, its two columns) and the odd lane (row of
 // r+1, the same two columns); one store instruction then covers 64
-// contiguous bytes of each of 4 rows.  No per-row test and one address
-// computation per lane: wave row block wm (tile rows wm * WM ..) starts at
-// base(wm), consecutive rows ld elements apart.  (Storing the tile
+// contiguous bytes of each of 4 rows.  No per-row test.  The stores are
+// buffer stores: the wave's base in a buffer descriptor (scalar registers),
+// the row offset of each store in a scalar register and the lane's offset
+// in one VGPR, so no 64-bit address is formed per store (and none can be
+// hoisted out of a loop that stores a tile every step).  Wave row block wm
+// (tile rows wm * WM ..) starts at base(wm), rows ld elements apart; the
+// tile's extent (128 * ld * 2 bytes) stays below 2^31.  (Storing the tile
 // transposed in registers, 8 bytes per lane over 32 rows per instruction,
 // measured slower: the write path prefers fewer, longer row segments.)
 template <class TL, class BASE>
 __device__ __forceinline__ void tile_store_full(const f32x16_t (&acc)[TL::MI][TL::NJ], BASE base, size_t ld) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int odd = lane & 1;
-  bf16_t* p = base(wm) + (size_t)(4 * (lane >> 5) + odd) * ld + wn * TL::WN + (lane & 30);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wave_uniform(base(wm)));
+  const int ldb = (int)ld * 2;
+  const int vo = (4 * (lane >> 5) + odd) * ldb + (wn * TL::WN + (lane & 30)) * 2;
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      bf16_t* q = p + (size_t)(32 * i + 8 * (r >> 2) + (r & 3)) * ld;
+      const int so = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
 #pragma unroll
       for (int j = 0; j < TL::NJ; ++j) {
         const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
         const float o0 = swap_lane_pair(v0), o1 = swap_lane_pair(v1);
-        *(uint32_t*)(q + 32 * j) = odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0);
+        __builtin_amdgcn_raw_buffer_store_b32(odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0), rs, vo + 64 * j, so,
+                                              0);
       }
     }
 }

@@ -222,6 +222,24 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
   st.flush(n, [&](int row) { return B.dxp + (size_t)(r0 + row) * d + c0; });
 }
 
+// A weight-gradient band: experts with at most 128 rows keep the band's A
+// stages in LDS (tile_band), larger ones stream both operands.
+template <class TL, class LA, class BP, class EPI>
+__device__ __forceinline__ void wgrad_band(int nc, int nk, bf16_t* smem, LA& la, BP bptr, EPI& epi) {
+  if (nk <= 2) {
+    auto lb = kcols2<TL::BN>(bptr);
+    lb.nk_ = nk;
+    if (nk == 1)
+      tile_band<TL, 1>(nc, smem, la, lb, epi);
+    else
+      tile_band<TL, 2>(nc, smem, la, lb, epi);
+  } else {
+    auto lb = kcols<TL::BN>(bptr);
+    lb.nk_ = nk;
+    tile_stream<TL>(nc, nk, smem, la, lb, epi);
+  }
+}
+
 // ---------------------------------------------------------------- dw2
 // dW2_e[n0 .. +128, i0 .. +128] = sum over the expert's rows r of
 // gG[r, n] H[r, i] (gG pulled by rowprep): K = the expert's rows, k past
@@ -247,13 +265,12 @@ __device__ void bwd_dw2_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   }
   auto la = kcols<TL::BM>(
       [&](int kk, int) -> const bf16_t* { return kk < M ? B.gg + (size_t)(off + kk) * d + n0 : B.zrow; });
-  auto lb = kcols<TL::BN>([&](int kk, int c) -> const bf16_t* {
+  auto bptr = [&](int kk, int c) -> const bf16_t* {
     return kk < M ? B.h + (size_t)(off + kk) * I + (cb + c) * TL::BN : B.zrow;
-  });
+  };
   const int nk = cdiv(M, 64);
   la.nk_ = nk;
-  lb.nk_ = nk;
-  tile_stream<TL>(nc, nk, smem, la, lb, epi);
+  wgrad_band<TL>(nc, nk, smem, la, bptr, epi);
 }
 
 // ---------------------------------------------------------------- dw13
@@ -283,13 +300,12 @@ __device__ void bwd_dw13_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   auto la = kcols<TL::BM>(
       [&](int kk, int) -> const bf16_t* { return kk < M ? B.dab + (size_t)(off + kk) * 2 * I + i0 : B.zrow; },
       I - TL::BM / 2);
-  auto lb = kcols<TL::BN>([&](int kk, int c) -> const bf16_t* {
+  auto bptr = [&](int kk, int c) -> const bf16_t* {
     return kk < M ? B.xp + (size_t)(off + kk) * d + (cb + c) * TL::BN : B.zrow;
-  });
+  };
   const int nk = cdiv(M, 64);
   la.nk_ = nk;
-  lb.nk_ = nk;
-  tile_stream<TL>(nc, nk, smem, la, lb, epi);
+  wgrad_band<TL>(nc, nk, smem, la, bptr, epi);
 }
 
 // ---------------------------------------------------------------- dx
