@@ -526,39 +526,57 @@ __device__ __forceinline__ void tile_band(int nc, bf16_t* smem, LA& A, LB& B, EP
   }
 }
 
-// Writes a tile whose rows are all valid as bf16 straight from registers,
-// two columns per 4-byte store: lane pairs swap values (DPP) so the even
-// lane of a pair stores (row of r, its two columns) and the odd lane (row of
-// r+1, the same two columns); one store instruction then covers 64
-// contiguous bytes of each of 4 rows.  No per-row test.  The stores are
-// buffer stores: the wave's base in a buffer descriptor (scalar registers),
-// the row offset of each store in a scalar register and the lane's offset
-// in one VGPR, so no 64-bit address is formed per store (and none can be
-// hoisted out of a loop that stores a tile every step).  Wave row block wm
-// (tile rows wm * WM ..) starts at base(wm), rows ld elements apart; the
-// tile's extent (128 * ld * 2 bytes) stays below 2^31.  (Storing the tile
-// transposed in registers, 8 bytes per lane over 32 rows per instruction,
-// measured slower: the write path prefers fewer, longer row segments.)
+// Writes a tile whose rows are all valid as bf16 with 16-byte stores, each
+// covering 8 rows x 128 contiguous bytes (one wave's 64 columns).  The
+// accumulators hold one column per lane, so each wave regroups its 64 x 64
+// block through its own 2 KB of LDS (stage: 4 waves x 2 KB, used by no one
+// else, so no barrier), 16 rows at a time: lane pairs swap values (DPP) so
+// the even lane of a pair holds two columns of row r and the odd lane the
+// same two columns of row r+1, each lane writes those words, and reads back
+// 16-byte row chunks.  Four times fewer store instructions than storing
+// the word pairs directly, whose 64 addresses per instruction kept the
+// texture unit's address queue full.  The stores are buffer stores (the
+// wave's base in a scalar descriptor, row offsets in scalar registers, one
+// VGPR of lane offset).  Wave row block wm (tile rows wm * WM ..) starts at
+// base(wm), rows ld elements apart; 128 * ld * 2 bytes stay below 2^31.
+// LDS layout of a wave's 16 x 64 block: 32 dwords a row, the row's 16-byte
+// chunk c at c ^ (4 * ((row >> 2) & 1)): conflict-free for the word writes
+// (rows r, r+1, r+4, r+5 together) and the chunk reads (8 lanes a row).
+constexpr int kWgradStageBytes = 4 * 2048;
 template <class TL, class BASE>
-__device__ __forceinline__ void tile_store_full(const f32x16_t (&acc)[TL::MI][TL::NJ], BASE base, size_t ld) {
+__device__ __forceinline__ void tile_store_staged(const f32x16_t (&acc)[TL::MI][TL::NJ], BASE base, size_t ld,
+                                                  bf16_t* stage) {
+  static_assert(TL::WN == 64 && TL::NJ == 2 && TL::WM == 32 * TL::MI, "64-column wave blocks");
+  typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int odd = lane & 1;
+  uint32_t* st = (uint32_t*)stage + wave * 512;
+  auto sidx = [](int row, int dw) { return row * 32 + ((((dw >> 2) ^ (((row >> 2) & 1) << 2)) << 2) | (dw & 3)); };
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wave_uniform(base(wm)));
   const int ldb = (int)ld * 2;
-  const int vo = (4 * (lane >> 5) + odd) * ldb + (wn * TL::WN + (lane & 30)) * 2;
+  const int rrow = lane >> 3, rch = lane & 7;
+  const int vo = rrow * ldb + (wn * TL::WN + 8 * rch) * 2;
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int so = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
+    for (int h = 0; h < 2; ++h) {
+      // accumulator entries 8h .. 8h+7: rows 16h .. 16h+15 of block i
 #pragma unroll
-      for (int j = 0; j < TL::NJ; ++j) {
-        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-        const float o0 = swap_lane_pair(v0), o1 = swap_lane_pair(v1);
-        __builtin_amdgcn_raw_buffer_store_b32(odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0), rs, vo + 64 * j, so,
-                                              0);
+      for (int r = 8 * h; r < 8 * h + 8; r += 2) {
+        const int row = 8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3) + odd;
+#pragma unroll
+        for (int j = 0; j < TL::NJ; ++j) {
+          const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+          const float o0 = swap_lane_pair(v0), o1 = swap_lane_pair(v1);
+          st[sidx(row, 16 * j + ((lane & 30) >> 1))] = odd ? pack_bf16x2(o1, v1) : pack_bf16x2(v0, o0);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const u32x4_t q = *(const u32x4_t*)(st + sidx(8 * g + rrow, 4 * rch));
+        __builtin_amdgcn_raw_buffer_store_b128(q, rs, vo, (32 * i + 16 * h + 8 * g) * ldb, 0);
       }
     }
 }

@@ -631,9 +631,12 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, B.s.queue, (int)p.n_ctr);
   const int nz = (int)(((size_t)2 * p.I + p.d + 256) / 2);
   hipLaunchKernelGGL(k_zero, dim3(cdiv(nz, 256)), dim3(256), 0, st, at<int>(ws, p.o_zero), nz);
-  const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes;
+  // weight-gradient tiles: their main loop's LDS plus the store staging
+  const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes + kWgradStageBytes;
   if (D->fused) {
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
+    static_assert(2 * (TileDW::smem_bytes + kWgradStageBytes + 1024) <= 160 * 1024,
+                  "two weight-gradient workgroups per CU, with their static LDS");
     // By default one persistent launch per phase (setup and row pulls
     // together): no phase reads what another phase of its launch writes, so
     // no task needs the agent-scope release, and each launch's registers
@@ -642,10 +645,10 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     // runs it anyway).
     if (!(D->flags & (MOE_FLAG_PERSISTENT_SINGLE | MOE_FLAG_PERSISTENT_WGRAD_APART))) {
       int rc = launch_fused_bwd<0x03u>(D, B, smem, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, smem, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, smem, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x10u>(D, B, smem, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, sm_dh, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x10u>(D, B, sm_dh, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x40u>(D, B, smem, st);
       return rc;
     }

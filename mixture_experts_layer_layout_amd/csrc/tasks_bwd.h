@@ -256,7 +256,8 @@ __device__ void bwd_dw2_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   const int off = B.offsets[e], M = B.offsets[e + 1] - off;
   bf16_t* out = B.dw2 + (size_t)e * d * I + (size_t)n0 * I;
   auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
-    tile_store_full<TL>(acc, [&](int wm) { return out + (size_t)(wm * TL::WM) * I + (cb + c) * TL::BN; }, I);
+    tile_store_staged<TL>(acc, [&](int wm) { return out + (size_t)(wm * TL::WM) * I + (cb + c) * TL::BN; }, I,
+                          smem + TL::smem_bytes / sizeof(bf16_t));
   };
   if (M == 0) {
     f32x16_t zero[TL::MI][TL::NJ] = {};
@@ -290,7 +291,8 @@ __device__ void bwd_dw13_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   // wave row block 0 holds the dW1 rows, block 1 the dW3 rows
   static_assert(TL::WM == TL::BM / 2, "one wave row block per gradient");
   auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
-    tile_store_full<TL>(acc, [&](int wm) { return (wm ? o3 : o1) + (cb + c) * TL::BN; }, d);
+    tile_store_staged<TL>(acc, [&](int wm) { return (wm ? o3 : o1) + (cb + c) * TL::BN; }, d,
+                          smem + TL::smem_bytes / sizeof(bf16_t));
   };
   if (M == 0) {
     f32x16_t zero[TL::MI][TL::NJ] = {};
