@@ -70,11 +70,11 @@ struct Tile {
 
 // ---------------------------------------------------------------- loaders
 // Rows with k contiguous.  Thread t handles chunk t%8 of rows t/8 + 32*i.
-template <int ROWS>
+template <int ROWS, int NBUF = kPrefetch>
 struct KRows {
   static constexpr int PER = ROWS / 32;
   const bf16_t* row[PER];
-  uint4 v[kPrefetch][PER];
+  uint4 v[NBUF][PER];
   // rowptr(r) -> pointer to element k=0 of tile row r; must be readable
   // for every r (clamp rows past the operand to a real one).
   template <class F>
@@ -205,10 +205,11 @@ template <int ROWS, class P>
 __device__ __forceinline__ KCols<ROWS, false, P, NoScale> kcols(P kptr, int half_off = 0) {
   return KCols<ROWS, false, P, NoScale>(kptr, NoScale(), half_off);
 }
-// the same with two register buffers (tile_band's streamed operand)
-template <int ROWS, class P>
-__device__ __forceinline__ KCols<ROWS, false, P, NoScale, 2> kcols2(P kptr, int half_off = 0) {
-  return KCols<ROWS, false, P, NoScale, 2>(kptr, NoScale(), half_off);
+// the same with NBUF register buffers (a deeper prefetch; tile_band's
+// streamed operand)
+template <int ROWS, int NBUF, class P>
+__device__ __forceinline__ KCols<ROWS, false, P, NoScale, NBUF> kcols_n(P kptr, int half_off = 0) {
+  return KCols<ROWS, false, P, NoScale, NBUF>(kptr, NoScale(), half_off);
 }
 template <int ROWS, class P, class S>
 __device__ __forceinline__ KCols<ROWS, true, P, S> kcols_scaled(P kptr, S kscale, int half_off = 0) {
@@ -270,15 +271,15 @@ __device__ __forceinline__ void Tile<BM_, BN_>::stage(const bf16_t* As, const bf
 // (stage kt lives in LDS buffer CUR, stage kt+1 in register buffer CUR ^ 1)
 // and receives stage kt+2.  kPrefetch = 1: one register buffer, which
 // receives stage kt+1 while stage kt feeds the MFMAs.
-template <int CUR, class TL, class LA, class LB>
+template <int CUR, class TL, int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16_t* Bs,
                                               f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B) {
-  constexpr int RB = kPrefetch == 2 ? CUR : 0;        // register buffer loaded now
-  constexpr int SB = kPrefetch == 2 ? (CUR ^ 1) : 0;  // register buffer stored now
-  A.template load<RB>(min(kt + kPrefetch, last));
-  B.template load<RB>(min(kt + kPrefetch, last));
-  A.prep(min(kt + kPrefetch + 1, last));
-  B.prep(min(kt + kPrefetch + 1, last));
+  constexpr int RB = PF == 2 ? CUR : 0;        // register buffer loaded now
+  constexpr int SB = PF == 2 ? (CUR ^ 1) : 0;  // register buffer stored now
+  A.template load<RB>(min(kt + PF, last));
+  B.template load<RB>(min(kt + PF, last));
+  A.prep(min(kt + PF + 1, last));
+  B.prep(min(kt + PF + 1, last));
   // keep the scheduler from sinking these loads below the LDS stores of
   // the previous stage (which wait for their own loads)
   __builtin_amdgcn_sched_barrier(0);
@@ -290,7 +291,7 @@ __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16
 }
 
 // Loads the first stages and stores stage 0 into LDS buffer 0.
-template <class LA, class LB>
+template <int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* Bs, LA& A, LB& B) {
   A.prep(0);
   B.prep(0);
@@ -298,7 +299,7 @@ __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* 
   B.template load<0>(0);
   A.prep(min(1, last));
   B.prep(min(1, last));
-  if (kPrefetch == 2) {
+  if constexpr (PF == 2) {
     A.template load<1>(min(1, last));
     B.template load<1>(min(1, last));
     A.prep(min(2, last));
@@ -310,7 +311,8 @@ __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* 
   __syncthreads();
 }
 
-template <class TL, class LA, class LB>
+// PF: stages loaded ahead into registers (the loaders need PF buffers).
+template <class TL, int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&acc)[TL::MI][TL::NJ], LA& A,
                                               LB& B) {
 #pragma unroll
@@ -323,13 +325,13 @@ __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&a
   const int last = nk - 1;
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
-  mainloop_prologue(last, As, Bs, A, B);
+  mainloop_prologue<PF>(last, As, Bs, A, B);
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    mainloop_step<0, TL>(kt, last, As, Bs, acc, A, B);
-    mainloop_step<1, TL>(kt + 1, last, As, Bs, acc, A, B);
+    mainloop_step<0, TL, PF>(kt, last, As, Bs, acc, A, B);
+    mainloop_step<1, TL, PF>(kt + 1, last, As, Bs, acc, A, B);
   }
-  if (kt < nk) mainloop_step<0, TL>(kt, last, As, Bs, acc, A, B);
+  if (kt < nk) mainloop_step<0, TL, PF>(kt, last, As, Bs, acc, A, B);
 }
 
 // Visits every accumulator: f(tile_row, tile_col, value).
@@ -474,7 +476,7 @@ __device__ __forceinline__ void band_step(int j, int c, int last, const bf16_t* 
 }
 
 // A: the loader of the shared rows (prep(s) with s < NK gives stage s);
-// B: a two-buffer loader (kcols2) whose prep(j) maps step j to column tile
+// B: a two-buffer loader (kcols_n<.., 2>) whose prep(j) maps step j to column tile
 // j / NK, stage j % NK.  LDS: NK stages of A, then two B stages.
 template <class TL, int NK, class LA, class LB, class EPI>
 __device__ __forceinline__ void tile_band(int nc, bf16_t* smem, LA& A, LB& B, EPI epi) {

@@ -412,9 +412,10 @@ __global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockI
 
 // The persistent backward: phases setup | rowprep | dh | dw2 | dxp | dw13
 // | dx through the per-XCD phase queues (dh and dxp tiles in the grouped
-// raster, 64 per queue block; the weight-gradient tiles of the expert of
-// load rank q -> queue q % 8, one band of kWgradPerTicket column tiles per
-// claim).
+// raster, 64 per queue block; the weight-gradient bands of each expert cut
+// into 8 slices of consecutive bands, slice x on queue x, experts in order
+// of decreasing load on every queue; one band of kWgradPerTicket column
+// tiles per claim).
 // Workgroups per CU the persistent backward asks the compiler to fit: two
 // where the phases' registers allow it without spilling, else one.
 constexpr int bwd_occupancy(unsigned mask) {
@@ -443,8 +444,8 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
         if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
         if (ph == 0) { groups = 1; return true; }
         if (ph == 1) { groups = B.nRP; return true; }
-        if (ph == 3) { groups = B.E; per = g2; return true; }
-        if (ph == 5) { groups = B.E; per = g13; return true; }
+        if (ph == 3) { groups = 8 * B.E; per = cdiv(g2, 8); return true; }
+        if (ph == 5) { groups = 8 * B.E; per = cdiv(g13, 8); return true; }
         if (c.nmt < 0) {
           if (!thread_wait_geq(B.s.scan_done, 1 + B.nRP, W)) return false;
           c.nmt = load_relaxed(B.s.n_mtiles);
@@ -472,15 +473,16 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
     } else if ((MASK & 0x28u) && (ph == 3 || ph == 5)) {
       // the expert order comes from setup
       if (!wait_geq(B.s.scan_done, 1 + B.nRP, W, &s_flag)) continue;
-      const int per = ph == 3 ? g2 : g13;
-      const int rank = t / per;
+      const int per = ph == 3 ? g2 : g13, span = 8 * cdiv(per, 8);
+      const int rank = t / span, band = t % span;
+      if (band >= per) continue;  // the last slice's padding
       if ((MASK & 8u) && ph == 3) {
-        bwd_dw2_band(B, rank, t % per, (bf16_t*)smem);
+        bwd_dw2_band(B, rank, band, (bf16_t*)smem);
       } else if (MASK & 0x20u) {
         const int e = B.eorder[rank];
         const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
         if (wait_geq(&B.s.aux1[e], need, W, &s_flag))
-          bwd_dw13_band(B, rank, t % per, (bf16_t*)smem);
+          bwd_dw13_band(B, rank, band, (bf16_t*)smem);
       }
     } else if ((MASK & 4u) && ph == 2) {
       if (t >= s_nmt * B.nNdh) continue;

@@ -42,6 +42,10 @@ typedef Tile<128, 128> TileDH;  // row tiles: dh, dxp
 typedef Tile<128, 128> TileDW;  // weight-gradient tiles: dw2, dw13
 constexpr int kRowPrep = 32;    // rows per rowprep (pull) task
 constexpr int kWgradPerTicket = 8;  // column tiles per weight-gradient task (one band)
+#ifndef MOE_DGRAD_AHEAD
+#define MOE_DGRAD_AHEAD 2
+#endif
+constexpr int kDgradAhead = MOE_DGRAD_AHEAD;  // stages in registers ahead in dh and dxp
 
 struct Bwd {
   int T, d, E, k, I, R, BM;
@@ -149,12 +153,12 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
   const int d = B.d, I = B.I;
   const bf16_t* W2 = B.w2 + (size_t)e * d * I;
   const int c0 = nt * TL::BN;
-  KRows<TL::BM> la;
+  KRows<TL::BM, kDgradAhead> la;
   // rows past n repeat the last row (their outputs are dropped)
   la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)B.src[r0 + min(r, n - 1)] * d; });
-  auto lb = kcols<TL::BN>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
+  auto lb = kcols_n<TL::BN, kDgradAhead>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(d / 64, smem, acc, la, lb);
+  tile_mainloop<TL, kDgradAhead>(d / 64, smem, acc, la, lb);
 
   // dA staged in LDS (dB kept in the accumulators), then dB; the dgate
   // partial sums go through a small LDS area past the staging block
@@ -210,13 +214,13 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const bf16_t* W1 = B.w1 + (size_t)e * I * d;
   const bf16_t* W3 = B.w3 + (size_t)e * I * d;
   const int c0 = nt * TL::BN;
-  KRows<TL::BM> la;
+  KRows<TL::BM, kDgradAhead> la;
   la.init([&](int r) -> const bf16_t* { return B.dab + (size_t)(r0 + min(r, n - 1)) * 2 * I; });
-  auto lb = kcols<TL::BN>([&](int kk, int) -> const bf16_t* {
+  auto lb = kcols_n<TL::BN, kDgradAhead>([&](int kk, int) -> const bf16_t* {
     return (kk < I ? W1 + (size_t)kk * d : W3 + (size_t)(kk - I) * d) + c0;
   });
   f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL>(2 * I / 64, smem, acc, la, lb);
+  tile_mainloop<TL, kDgradAhead>(2 * I / 64, smem, acc, la, lb);
   const Staged<TL::BM, TL::BN> st{smem};
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
   st.flush(n, [&](int row) { return B.dxp + (size_t)(r0 + row) * d + c0; });
@@ -227,7 +231,7 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
 template <class TL, class LA, class BP, class EPI>
 __device__ __forceinline__ void wgrad_band(int nc, int nk, bf16_t* smem, LA& la, BP bptr, EPI& epi) {
   if (nk <= 2) {
-    auto lb = kcols2<TL::BN>(bptr);
+    auto lb = kcols_n<TL::BN, 2>(bptr);
     lb.nk_ = nk;
     if (nk == 1)
       tile_band<TL, 1>(nc, smem, la, lb, epi);
