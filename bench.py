@@ -266,8 +266,9 @@ def main():
     if saved["status"].item() != 0:
         raise RuntimeError("device status " + api.moe_status_string(saved["status"].item()))
 
-    # the standalone layout and pull gather (moe_layout, moe_gather) on this
-    # step's routing, timed with events on the same stream
+    # the standalone layout and gather (moe_layout, moe_gather: token-major
+    # by inv, and the pull by perm) on this step's routing, timed with events
+    # on the same stream
     side = {}
     if w.experts != "f32":
         gdesc = layer.desc_for(w, fused=False)
@@ -279,7 +280,10 @@ def main():
         reps = 20
         for name, fn in (("layout", lambda: api.moe_layout(gdesc, saved["topk_idx"], lay["counts"], lay["offsets"],
                                                            lay["perm"], lay["inv"], None, lws, stream)),
-                         ("gather", lambda: api.moe_gather(gdesc, dev["x"], saved["perm"], xq_, xs_, stream))):
+                         ("gather", lambda: api.moe_gather(gdesc, dev["x"], None, xq_, xs_, stream,
+                                                           inv=saved["inv"])),
+                         ("gather_pull", lambda: api.moe_gather(gdesc, dev["x"], saved["perm"], xq_, xs_,
+                                                                stream))):
             fn()
             a, b = ev(), ev()
             a.record(stream)
@@ -316,6 +320,7 @@ def main():
         phases["gather_ms"] = round(side["gather"], 4)
         phases["gather_gbs"] = round(gbytes / (side["gather"] * 1e-3) / 1e9, 1)
         phases["gather_hbm_frac"] = round(gbytes / (side["gather"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        phases["gather_pull_gbs"] = round(gbytes / (side["gather_pull"] * 1e-3) / 1e9, 1)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -183,15 +183,22 @@ MOE_API int moe_layout(const moe_desc* desc, const int32_t* topk_idx, int32_t* c
                int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Pull dispatch as a row gather (MoK flash §02: the receiver pulls each
- * token given only its source position and lays rows out itself).
- *   x   act [T, d] input;  perm int32 [R] from moe_layout;
- *   xp  act [R, d] output, xp[r] = x[perm[r] / k].
+/* Dispatch as a row gather (MoK flash §02: tokens are laid out in expert
+ * order so each expert's rows are contiguous for its GEMM).
+ *   x    act [T, d] input
+ *   perm int32 [R] from moe_layout, or NULL
+ *   inv  int32 [R] from moe_layout, or NULL (at least one of the two)
+ *   xp   act [R, d] output, xp[r] = x[perm[r] / k], i.e. xp[inv[t k + j]] = x[t]
+ * With inv the gather runs token-major: each token row is read once and
+ * written to its k rows.  With only perm it is the pull of MoK flash §02:
+ * each destination row reads its token given only the source position.
+ * Both write the same bytes.  Row indices outside [0, R) in inv are
+ * skipped; perm entries must lie in [0, R).
  * For desc->expert_dtype == MOE_MXFP8 the gather also quantises (MoK flash
  * §02, quantisation folded into the dispatch): xp receives E4M3 codes
  * uint8 [R, d] and xp_scale E8M0 codes uint8 [R, d/32]; else xp_scale is
  * ignored. */
-MOE_API int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm,
+MOE_API int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm, const int32_t* inv,
                void* xp, uint8_t* xp_scale, void* stream);
 
 /* MXFP8 quantisation of a [rows, K] bf16 matrix along K in blocks of 32

@@ -64,7 +64,7 @@ _lib.moe_workspace_size.argtypes = [_P(MoeDesc), _P(ctypes.c_size_t)]
 _lib.moe_route.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
 _lib.moe_layout.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_void_p, ctypes.c_size_t, c_void_p]
-_lib.moe_gather.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+_lib.moe_gather.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
 _lib.moe_quantize_mxfp8.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p,
                                     c_void_p, c_void_p]
 _lib.moe_forward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWeights),
@@ -131,8 +131,8 @@ def moe_layout(desc, topk_idx, counts, offsets, perm, inv, status, workspace, st
            "moe_layout")
 
 
-def moe_gather(desc, x, perm, xp, xp_scale=None, stream=None):
-    _check(_lib.moe_gather(ctypes.byref(desc), _p(x), _p(perm), _p(xp), _p(xp_scale),
+def moe_gather(desc, x, perm, xp, xp_scale=None, stream=None, inv=None):
+    _check(_lib.moe_gather(ctypes.byref(desc), _p(x), _p(perm), _p(inv), _p(xp), _p(xp_scale),
                            _stream(stream)), "moe_gather")
 
 

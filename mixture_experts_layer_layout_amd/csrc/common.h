@@ -183,6 +183,33 @@ struct CopyAsIs {
   __device__ __forceinline__ uint4 operator()(int, uint4 u) const { return u; }
 };
 
+// One wave writes one source row to k <= 64 destination rows, reading it
+// once: every lane loads up to kCopyUnroll vectors, then stores them to each
+// destination.  Lane j holds destination j's row index in lane_row (read
+// out with readlane, so no memory load sits between the stores: vmcnt
+// counts stores too, and a load there would wait for every store before
+// it); indices outside [0, R) are skipped.  f(j, u) may transform a vector
+// for destination j.
+template <class F>
+__device__ __forceinline__ void wave_push_row(const uint4* __restrict__ src, uint4* __restrict__ dst, int nvec,
+                                              int k, int R, int lane_row, F f) {
+  const int lane = threadIdx.x & 63;
+  for (int v0 = lane; v0 < nvec; v0 += 64 * kCopyUnroll) {
+    uint4 u[kCopyUnroll];
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q)
+      if (v0 + 64 * q < nvec) u[q] = src[v0 + 64 * q];
+    for (int j = 0; j < k; ++j) {
+      const int r = __builtin_amdgcn_readlane(lane_row, j);
+      if ((unsigned)r >= (unsigned)R) continue;
+      uint4* d = dst + (size_t)r * nvec;
+#pragma unroll
+      for (int q = 0; q < kCopyUnroll; ++q)
+        if (v0 + 64 * q < nvec) d[v0 + 64 * q] = f(j, u[q]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- misc
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }

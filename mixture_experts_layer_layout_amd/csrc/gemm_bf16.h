@@ -261,21 +261,20 @@ __device__ __forceinline__ void Tile<BM_, BN_>::stage(const bf16_t* As, const bf
 }
 
 // Runs the K loop over nk stages (nk may be 0: the tile is then zero).
-// Two stages are in flight while a third feeds the MFMAs: at step kt the
-// loads of stage kt+2 go out into the register buffer freed by step kt-1,
-// the MFMAs consume stage kt from LDS, and stage kt+1 (loaded a step
-// earlier) is written to the other LDS buffer.  Every load, prep and store
-// is unconditional -- past the last stage they repeat it -- so the only
-// waits the compiler emits are for the stage being stored.
-// One step of the K loop.  kPrefetch = 2: register buffer CUR is free
-// (stage kt lives in LDS buffer CUR, stage kt+1 in register buffer CUR ^ 1)
-// and receives stage kt+2.  kPrefetch = 1: one register buffer, which
-// receives stage kt+1 while stage kt feeds the MFMAs.
-template <int CUR, class TL, int PF = kPrefetch, class LA, class LB>
+// PF stages are in flight in registers while a third feeds the MFMAs from
+// LDS: at step kt the loads of stage kt+PF go into register buffer kt % PF
+// (stored to LDS a step earlier), the MFMAs consume stage kt from LDS
+// buffer kt % 2, and stage kt+1 (register buffer (kt+1) % PF) is written to
+// the other LDS buffer.  Every load, prep and store is unconditional --
+// past the last stage they repeat it -- so the only waits the compiler
+// emits are for the stage being stored.  STEP is kt modulo lcm(2, PF), so
+// both buffer indices are compile-time.
+template <int STEP, class TL, int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16_t* Bs,
                                               f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B) {
-  constexpr int RB = PF == 2 ? CUR : 0;        // register buffer loaded now
-  constexpr int SB = PF == 2 ? (CUR ^ 1) : 0;  // register buffer stored now
+  constexpr int CUR = STEP & 1;            // LDS buffer read now
+  constexpr int RB = STEP % PF;            // register buffer loaded now
+  constexpr int SB = (STEP + 1) % PF;      // register buffer stored now
   A.template load<RB>(min(kt + PF, last));
   B.template load<RB>(min(kt + PF, last));
   A.prep(min(kt + PF + 1, last));
@@ -290,7 +289,8 @@ __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16
   __syncthreads();
 }
 
-// Loads the first stages and stores stage 0 into LDS buffer 0.
+// Loads the first PF stages (stage s into register buffer s) and stores
+// stage 0 into LDS buffer 0.
 template <int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* Bs, LA& A, LB& B) {
   A.prep(0);
@@ -299,11 +299,23 @@ __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* 
   B.template load<0>(0);
   A.prep(min(1, last));
   B.prep(min(1, last));
-  if constexpr (PF == 2) {
+  if constexpr (PF >= 2) {
     A.template load<1>(min(1, last));
     B.template load<1>(min(1, last));
     A.prep(min(2, last));
     B.prep(min(2, last));
+  }
+  if constexpr (PF >= 3) {
+    A.template load<2>(min(2, last));
+    B.template load<2>(min(2, last));
+    A.prep(min(3, last));
+    B.prep(min(3, last));
+  }
+  if constexpr (PF >= 4) {
+    A.template load<3>(min(3, last));
+    B.template load<3>(min(3, last));
+    A.prep(min(4, last));
+    B.prep(min(4, last));
   }
   __syncthreads();
   A.template store<0>(As);
@@ -311,10 +323,35 @@ __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* 
   __syncthreads();
 }
 
-// PF: stages loaded ahead into registers (the loaders need PF buffers).
+// Steps STEP .. U-1 of one unrolled round of U steps, each only if its
+// stage exists.
+template <int STEP, int U, class TL, int PF, class LA, class LB>
+__device__ __forceinline__ void mainloop_tail(int kt, int nk, int last, bf16_t* As, bf16_t* Bs,
+                                              f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B) {
+  if constexpr (STEP < U) {
+    if (kt + STEP < nk) {
+      mainloop_step<STEP, TL, PF>(kt + STEP, last, As, Bs, acc, A, B);
+      mainloop_tail<STEP + 1, U, TL, PF>(kt, nk, last, As, Bs, acc, A, B);
+    }
+  }
+}
+
+template <int STEP, int U, class TL, int PF, class LA, class LB>
+__device__ __forceinline__ void mainloop_round(int kt, int last, bf16_t* As, bf16_t* Bs,
+                                               f32x16_t (&acc)[TL::MI][TL::NJ], LA& A, LB& B) {
+  if constexpr (STEP < U) {
+    mainloop_step<STEP, TL, PF>(kt + STEP, last, As, Bs, acc, A, B);
+    mainloop_round<STEP + 1, U, TL, PF>(kt, last, As, Bs, acc, A, B);
+  }
+}
+
+// PF: stages loaded ahead into registers, 1 to 4 (the loaders need PF
+// buffers).
 template <class TL, int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&acc)[TL::MI][TL::NJ], LA& A,
                                               LB& B) {
+  static_assert(PF >= 1 && PF <= 4, "register prefetch depth 1..4");
+  constexpr int U = PF % 2 ? 2 * PF : PF;  // lcm(2, PF)
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
@@ -327,11 +364,8 @@ __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&a
   bf16_t* Bs = smem + 2 * TL::LDS_A;
   mainloop_prologue<PF>(last, As, Bs, A, B);
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    mainloop_step<0, TL, PF>(kt, last, As, Bs, acc, A, B);
-    mainloop_step<1, TL, PF>(kt + 1, last, As, Bs, acc, A, B);
-  }
-  if (kt < nk) mainloop_step<0, TL, PF>(kt, last, As, Bs, acc, A, B);
+  for (; kt + U <= nk; kt += U) mainloop_round<0, U, TL, PF>(kt, last, As, Bs, acc, A, B);
+  mainloop_tail<0, U, TL, PF>(kt, nk, last, As, Bs, acc, A, B);
 }
 
 // Visits every accumulator: f(tile_row, tile_col, value).
@@ -545,6 +579,12 @@ __device__ __forceinline__ void tile_band(int nc, bf16_t* smem, LA& A, LB& B, EP
 // chunk c at c ^ (4 * ((row >> 2) & 1)): conflict-free for the word writes
 // (rows r, r+1, r+4, r+5 together) and the chunk reads (8 lanes a row).
 constexpr int kWgradStageBytes = 4 * 2048;
+// The weight-gradient stores carry the non-temporal hint (cache policy
+// bit 1): 22.5 GB of dW written once at the DeepSeek-V3 shape would
+// otherwise displace the band's inputs from the L2, and the data gradient
+// the next launch reads.  Measured: dW1/dW3 5.66 -> 5.48 ms, the dX
+// gather-sum after them 156 -> 109 us.
+constexpr int kWgradStorePolicy = 2;
 template <class TL, class BASE>
 __device__ __forceinline__ void tile_store_staged(const f32x16_t (&acc)[TL::MI][TL::NJ], BASE base, size_t ld,
                                                   bf16_t* stage) {
@@ -578,7 +618,7 @@ __device__ __forceinline__ void tile_store_staged(const f32x16_t (&acc)[TL::MI][
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const u32x4_t q = *(const u32x4_t*)(st + sidx(8 * g + rrow, 4 * rch));
-        __builtin_amdgcn_raw_buffer_store_b128(q, rs, vo, (32 * i + 16 * h + 8 * g) * ldb, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(q, rs, vo, (32 * i + 16 * h + 8 * g) * ldb, kWgradStorePolicy);
       }
     }
 }

@@ -179,9 +179,9 @@ __device__ __forceinline__ uint32_t mx_quant32(const float (&v)[32], uint32_t (&
   return sc;
 }
 
-// Quantises block b of a bf16 row at src into codes (32 bytes at dst) and
-// its scale code.
-__device__ __forceinline__ void mx_quant_bf16_block(const bf16_t* src, uint8_t* dst, uint8_t* scale) {
+// Quantises 32 bf16 values at src: the 32 codes packed into w, the scale
+// code returned.
+__device__ __forceinline__ uint8_t mx_quant_bf16_words(const bf16_t* src, uint32_t (&w)[8]) {
   uint4 in[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) in[i] = ((const uint4*)src)[i];
@@ -192,8 +192,14 @@ __device__ __forceinline__ void mx_quant_bf16_block(const bf16_t* src, uint8_t* 
     v[2 * i] = __uint_as_float(iw[i] << 16);
     v[2 * i + 1] = __uint_as_float(iw[i] & 0xffff0000u);
   }
+  return (uint8_t)mx_quant32(v, w);
+}
+
+// Quantises block b of a bf16 row at src into codes (32 bytes at dst) and
+// its scale code.
+__device__ __forceinline__ void mx_quant_bf16_block(const bf16_t* src, uint8_t* dst, uint8_t* scale) {
   uint32_t w[8];
-  *scale = (uint8_t)mx_quant32(v, w);
+  *scale = mx_quant_bf16_words(src, w);
   ((uint4*)dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
   ((uint4*)dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }

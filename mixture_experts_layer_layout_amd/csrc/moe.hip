@@ -72,7 +72,7 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->nW2n = I / TileDW::BN;
   p->nW13m = I / (TileDW::BM / 2);
   p->nW13n = d / TileDW::BN;
-  p->nRP = cdiv(p->R, kRowPrep);
+  p->nRP = cdiv(T, kPrepTok);
 
   const size_t R = (size_t)p->R, es = p->act_es;
   size_t o = 0;
@@ -367,6 +367,22 @@ __global__ void __launch_bounds__(256) k_gather_perm(const Act* __restrict__ x, 
   const int nvec = d * (int)sizeof(Act) / 16;
   for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4)
     wave_copy_row((const uint4*)x + (size_t)(perm[r] / k) * nvec, (uint4*)xp + (size_t)r * nvec, nvec, CopyAsIs());
+}
+
+// Token-major gather: each wave reads one token row once and writes it to
+// the k rows the layout gave that token, xp[inv[t k + j]] = x[t].  Same
+// rows as the pull by perm, with x read once instead of k times.  A row
+// index outside [0, R) is skipped.  k <= 64 (the plan caps k at 16).
+template <class Act>
+__global__ void __launch_bounds__(256) k_gather_push(const Act* __restrict__ x, const int* __restrict__ inv,
+                                                     Act* __restrict__ xp, int T, int R, int d, int k) {
+  const int nvec = d * (int)sizeof(Act) / 16;
+  const int lane = threadIdx.x & 63;
+  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+    const int lane_row = lane < k ? inv[(size_t)t * k + lane] : -1;
+    wave_push_row((const uint4*)x + (size_t)t * nvec, (uint4*)xp, nvec, k, R, lane_row,
+                  [](int, uint4 u) { return u; });
+  }
 }
 
 // ------------------------------------------------------------------ backward
@@ -739,19 +755,30 @@ int moe_layout(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts, i
   return launch_status();
 }
 
-int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm, void* xp, uint8_t* xp_scale,
-               void* stream) {
+int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm, const int32_t* inv, void* xp,
+               uint8_t* xp_scale, void* stream) {
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
   if (p.R == 0) return MOE_OK;
-  if (!x || !perm || !xp) return MOE_ERR_INVALID_ARG;
+  if (!x || (!perm && !inv) || !xp) return MOE_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
-  const int grid = cdiv(p.R, 4) < 4096 ? cdiv(p.R, 4) : 4096;
   if (p.mxfp8) {
     if (!xp_scale) return MOE_ERR_INVALID_ARG;
-    return mxfp8_gather_perm((const bf16_t*)x, perm, (uint8_t*)xp, xp_scale, p.R, p.d, p.k, st);
+    return inv ? mxfp8_gather_push((const bf16_t*)x, inv, (uint8_t*)xp, xp_scale, p.T, p.R, p.d, p.k, st)
+               : mxfp8_gather_perm((const bf16_t*)x, perm, (uint8_t*)xp, xp_scale, p.R, p.d, p.k, st);
   }
+  if (inv) {
+    const int grid = cdiv(p.T, 4) < 4096 ? cdiv(p.T, 4) : 4096;
+    if (p.f32)
+      hipLaunchKernelGGL(k_gather_push<float>, dim3(grid), dim3(256), 0, st, (const float*)x, inv, (float*)xp, p.T,
+                         p.R, p.d, p.k);
+    else
+      hipLaunchKernelGGL(k_gather_push<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)x, inv, (bf16_t*)xp,
+                         p.T, p.R, p.d, p.k);
+    return launch_status();
+  }
+  const int grid = cdiv(p.R, 4) < 4096 ? cdiv(p.R, 4) : 4096;
   if (p.f32)
     hipLaunchKernelGGL(k_gather_perm<float>, dim3(grid), dim3(256), 0, st, (const float*)x, perm, (float*)xp, p.R,
                        p.d, p.k);

@@ -148,6 +148,37 @@ __global__ void __launch_bounds__(256) k_mx_quant_rows(const bf16_t* __restrict_
   }
 }
 
+// Token-major quantising gather: block b of token t is quantised once and
+// its codes and scale written to each of the token's k rows (rows outside
+// [0, R) skipped).  The same codes as quantising every gathered row, since
+// the 32-element blocks lie within a row.
+__global__ void __launch_bounds__(256) k_mx_quant_push(const bf16_t* __restrict__ x, const int* __restrict__ inv,
+                                                       int k, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales, int T, int R, int d) {
+  const int nbk = d / 32;
+  const int64_t total = (int64_t)T * nbk;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = i / nbk, b = i - t * nbk;
+    // every row index loaded before the first store (vmcnt counts stores
+    // too, so a load between them would wait for the stores before it)
+    int rows[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) rows[j] = j < k ? inv[t * k + j] : -1;
+    uint32_t w[8];
+    const uint8_t s = mx_quant_bf16_words(x + t * d + 32 * b, w);
+    const uint4 lo = make_uint4(w[0], w[1], w[2], w[3]), hi = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      const int r = rows[j];
+      if ((unsigned)r >= (unsigned)R) continue;
+      uint4* dst = (uint4*)(codes + (int64_t)r * d + 32 * b);
+      dst[0] = lo;
+      dst[1] = hi;
+      scales[(int64_t)r * nbk + b] = s;
+    }
+  }
+}
+
 static int mx_quant_grid(int64_t blocks) {
   const int64_t g = (blocks + kThreads - 1) / kThreads;
   return (int)(g < 8192 ? g : 8192);
@@ -158,6 +189,13 @@ static int mxfp8_gather_perm(const bf16_t* x, const int* perm, uint8_t* xq, uint
   const int64_t blocks = (int64_t)R * (d / 32);
   hipLaunchKernelGGL(k_mx_quant_rows<true>, dim3(mx_quant_grid(blocks)), dim3(kThreads), 0, st, x, perm, k, xq,
                      xs, (int64_t)R, (int64_t)d);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+static int mxfp8_gather_push(const bf16_t* x, const int* inv, uint8_t* xq, uint8_t* xs, int T, int R, int d, int k,
+                             hipStream_t st) {
+  const int64_t blocks = (int64_t)T * (d / 32);
+  hipLaunchKernelGGL(k_mx_quant_push, dim3(mx_quant_grid(blocks)), dim3(kThreads), 0, st, x, inv, k, xq, xs, T, R, d);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

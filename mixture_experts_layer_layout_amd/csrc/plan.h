@@ -25,7 +25,7 @@ struct Plan {
   int nNdx;        // column tiles of the dXp GEMM (over d)
   int nW2m, nW2n;  // dW2 tiles per expert: over d, over I
   int nW13m, nW13n;// dW1/dW3 tiles per expert: over I (half a tile of each), over d
-  int nRP;         // rowprep (pull) tasks
+  int nRP;         // row-preparation tasks (kPrepTok tokens each)
   // workspace carving (byte offsets)
   size_t o_ctr, n_ctr;
   size_t o_lpart, o_topk, o_gate, o_bmask, o_bcnt, o_bbase, o_counts, o_offsets;

@@ -40,12 +40,16 @@ namespace moe {
 
 typedef Tile<128, 128> TileDH;  // row tiles: dh, dxp
 typedef Tile<128, 128> TileDW;  // weight-gradient tiles: dw2, dw13
-constexpr int kRowPrep = 32;    // rows per rowprep (pull) task
+constexpr int kPrepTok = 8;     // tokens per row-preparation task
 constexpr int kWgradPerTicket = 8;  // column tiles per weight-gradient task (one band)
+// Stages in registers ahead in dh and dxp.  Measured at the DeepSeek-V3
+// Zipf step: 2 is best (dxp 5.8 ms); 3 and 4 cost the registers of a second
+// workgroup per CU (dxp 7.7 and 11.6 ms).
 #ifndef MOE_DGRAD_AHEAD
 #define MOE_DGRAD_AHEAD 2
 #endif
-constexpr int kDgradAhead = MOE_DGRAD_AHEAD;  // stages in registers ahead in dh and dxp
+constexpr int kDgradAhead = MOE_DGRAD_AHEAD;
+
 
 struct Bwd {
   int T, d, E, k, I, R, BM;
@@ -118,23 +122,28 @@ __device__ void bwd_setup(const Bwd& B, int* sh /* >= 2*kMaxE + 16 ints */) {
   }
 }
 
+// Token-major row preparation for kPrepTok tokens: each token's x and dY
+// rows are read once and written to its k expert rows, dY scaled by the
+// slot's gate (Xp[r] = x[t], G[r] = g dY[t] for r = inv[t k + j]); the row's
+// source token and gate are recorded.
 __device__ void bwd_rowprep(const Bwd& B, int task) {
-  const int r0 = task * kRowPrep, n = min(kRowPrep, B.R - r0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvec = B.d / 8;
-  for (int i = wave; i < n; i += 4) {
-    const int r = r0 + i;
-    const int a = B.perm[r];
-    const int t = a / B.k;
-    const float g = B.gate[a];
-    if (lane == 0) {
-      B.src[r] = t;
-      B.grow[r] = g;
+  const int k = B.k;
+  for (int tt = wave; tt < kPrepTok; tt += 4) {
+    const int t = task * kPrepTok + tt;
+    if (t >= B.T) break;
+    // lane j < k holds slot j's row and gate
+    const int lane_row = lane < k ? B.inv[(size_t)t * k + lane] : -1;
+    const float lane_g = lane < k ? B.gate[(size_t)t * k + lane] : 0.0f;
+    if (lane < k && (unsigned)lane_row < (unsigned)B.R) {
+      B.src[lane_row] = t;
+      B.grow[lane_row] = lane_g;
     }
-    const uint4* xs = (const uint4*)(B.x + (size_t)t * B.d);
-    const uint4* ys = (const uint4*)(B.dy + (size_t)t * B.d);
-    wave_copy_row(xs, (uint4*)(B.xp + (size_t)r * B.d), nvec, CopyAsIs());
-    wave_copy_row(ys, (uint4*)(B.gg + (size_t)r * B.d), nvec, [&](int, uint4 u) {
+    wave_push_row((const uint4*)(B.x + (size_t)t * B.d), (uint4*)B.xp, nvec, k, B.R, lane_row,
+                  [](int, uint4 u) { return u; });
+    wave_push_row((const uint4*)(B.dy + (size_t)t * B.d), (uint4*)B.gg, nvec, k, B.R, lane_row, [&](int j, uint4 u) {
+      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_g), j));
       uint32_t* w = (uint32_t*)&u;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -329,29 +338,41 @@ __device__ void bwd_dx_tokens_k(const Bwd& B, int cb) {
     int rows[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) rows[j] = j < k ? B.inv[(size_t)t * k + j] : 0;
-    if (lane < k) {
-      int mine = 0;
-#pragma unroll
-      for (int j = 0; j < NR; ++j)
-        if (j == lane) mine = rows[j];
+    {
+      // dgate[t, j]: slot j's column-tile partials summed by a group of G
+      // lanes (G the largest power of two with G k <= 64), each lane a
+      // strided part, then a butterfly inside the group: a fixed order, and
+      // the partial loads are issued by all lanes at once
+      int G = 64;
+      while (G * k > 64) G >>= 1;
+      const int j = lane / G, q = lane - (lane / G) * G;
       float s = 0.0f;
-      for (int p = 0; p < B.nNdh; ++p) s += B.dgp[(size_t)p * B.R + mine];
-      B.dgate[(size_t)t * k + lane] = s;
+      if (j < k) {
+        const int r = B.inv[(size_t)t * k + j];
+        for (int p = q; p < B.nNdh; p += G) s += B.dgp[(size_t)p * B.R + r];
+      }
+      for (int o = G >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (j < k && q == 0) B.dgate[(size_t)t * k + j] = s;
     }
     auto put = [&](int v, const float (&acc)[8]) {
       ((uint4*)B.dx)[(size_t)t * nvec + v] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
     };
-    // known k: two vectors per lane per iteration, all row loads up front
-    constexpr int VU = K ? 2 : 1;
-    for (int v0 = lane; v0 < nvec; v0 += 64 * VU) {
-      if constexpr (K != 0) {
-        uint4 u[VU][K];
+    // known k: kCombVec vectors per lane per step, the next step's row
+    // loads issued before this step's stores (as in combine_tokens_k)
+    constexpr int VU = K ? kCombVec : 1;
+    if constexpr (K != 0) {
+      uint4 u[VU][K], nx[VU][K];
+      auto load = [&](uint4 (&b)[VU][K], int v) {
 #pragma unroll
         for (int h = 0; h < VU; ++h)
 #pragma unroll
           for (int j = 0; j < K; ++j)
-            if (v0 + 64 * h < nvec) u[h][j] = ((const uint4*)B.dxp)[(size_t)rows[j] * nvec + v0 + 64 * h];
+            if (v + 64 * h < nvec) b[h][j] = ((const uint4*)B.dxp)[(size_t)rows[j] * nvec + v + 64 * h];
+      };
+      load(u, lane);
+      for (int v0 = lane; v0 < nvec; v0 += 64 * VU) {
+        if (v0 + 64 * VU < nvec) load(nx, v0 + 64 * VU);
 #pragma unroll
         for (int h = 0; h < VU; ++h) {
           if (v0 + 64 * h >= nvec) break;
@@ -366,7 +387,13 @@ __device__ void bwd_dx_tokens_k(const Bwd& B, int cb) {
           }
           put(v0 + 64 * h, acc);
         }
-      } else {
+#pragma unroll
+        for (int h = 0; h < VU; ++h)
+#pragma unroll
+          for (int j = 0; j < K; ++j) u[h][j] = nx[h][j];
+      }
+    } else {
+      for (int v0 = lane; v0 < nvec; v0 += 64) {
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.0f;

@@ -32,6 +32,7 @@ namespace moe {
 
 constexpr int kTokBlock = 64;  // tokens per routing block (one mask bit each)
 constexpr int kCombTok = 8;    // tokens per combine task
+constexpr int kCombVec = 2;    // 16-byte vectors per lane per step of a combine row (known k)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 
@@ -557,17 +558,23 @@ __device__ void combine_tokens_k(const Fwd& F, int cb) {
       rows[j] = j < k ? F.inv[(size_t)t * k + j] : 0;
       g[j] = j < k ? F.gate[(size_t)t * k + j] : 0.0f;
     }
-    // known k: two vectors per lane per iteration, all 2k row loads issued
-    // before the first is used
-    constexpr int VU = K ? 2 : 1;
-    for (int v0 = lane; v0 < nvec; v0 += 64 * VU) {
-      if constexpr (K != 0) {
-        uint4 u[VU][K];
+    // known k: kCombVec vectors per lane per step, every row load of a step
+    // issued before the first is used, and the next step's loads issued
+    // before this step's stores (vmcnt counts stores too: loads issued after
+    // the stores would wait for them)
+    constexpr int VU = K ? kCombVec : 1;
+    if constexpr (K != 0) {
+      uint4 u[VU][K], nx[VU][K];
+      auto load = [&](uint4 (&b)[VU][K], int v) {
 #pragma unroll
         for (int h = 0; h < VU; ++h)
 #pragma unroll
           for (int j = 0; j < K; ++j)
-            if (v0 + 64 * h < nvec) u[h][j] = ((const uint4*)F.yp)[(size_t)rows[j] * nvec + v0 + 64 * h];
+            if (v + 64 * h < nvec) b[h][j] = ((const uint4*)F.yp)[(size_t)rows[j] * nvec + v + 64 * h];
+      };
+      load(u, lane);
+      for (int v0 = lane; v0 < nvec; v0 += 64 * VU) {
+        if (v0 + 64 * VU < nvec) load(nx, v0 + 64 * VU);
 #pragma unroll
         for (int h = 0; h < VU; ++h) {
           if (v0 + 64 * h >= nvec) break;
@@ -586,8 +593,13 @@ __device__ void combine_tokens_k(const Fwd& F, int cb) {
           for (int q = 0; q < EPV; ++q) po[q] = Elem<Act>::from_f32(acc[q]);
           ((uint4*)F.y)[(size_t)t * nvec + v0 + 64 * h] = o;
         }
-      } else {
-        const int v = v0;
+#pragma unroll
+        for (int h = 0; h < VU; ++h)
+#pragma unroll
+          for (int j = 0; j < K; ++j) u[h][j] = nx[h][j];
+      }
+    } else {
+      for (int v = lane; v < nvec; v += 64) {
         float acc[EPV];
 #pragma unroll
         for (int q = 0; q < EPV; ++q) acc[q] = 0.0f;

@@ -61,7 +61,8 @@ def test_quantize_bit_exact(rows, K):
     assert np.array_equal(host(codes), want_c.astype(np.int64))
 
 
-def test_gather_quantises_bit_exact():
+@pytest.mark.parametrize("mode", ["pull", "push"])
+def test_gather_quantises_bit_exact(mode):
     w = synth.WORKLOADS["dsv3-mxfp8"].shrink(T=100, d=512, E=16, k=4, I=256)
     x = edge_matrix(w.T, w.d, 3)
     logits = synth.random_logits(w.T, w.E, 4)
@@ -77,7 +78,10 @@ def test_gather_quantises_bit_exact():
     api.moe_layout(d, idx, counts, offsets, perm, inv, None, ws)
     xq = torch.empty((w.R, w.d), dtype=torch.uint8, device="cuda")
     xs = torch.empty((w.R, w.d // 32), dtype=torch.uint8, device="cuda")
-    api.moe_gather(d, x.cuda(), perm, xq, xs)
+    if mode == "pull":
+        api.moe_gather(d, x.cuda(), perm, xq, xs)
+    else:
+        api.moe_gather(d, x.cuda(), None, xq, xs, inv=inv)
     torch.cuda.synchronize()
     src = host(perm) // w.k
     want_c, want_s = Q.quantize(x.double().numpy()[src])

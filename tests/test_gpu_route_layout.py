@@ -95,18 +95,40 @@ def test_layout_repeatable_and_invalid_route():
     assert st.item() == api.MOE_ERR_INVALID_ROUTE
 
 
+@pytest.mark.parametrize("mode", ["pull", "push"])
 @pytest.mark.parametrize("act,d", [("bf16", 7168), ("bf16", 256), ("f32", 128)])
-def test_gather_bitexact(act, d):
+def test_gather_bitexact(act, d, mode):
     T, E, k = 777, 32, 4
     idx = synth.random_topk(T, E, k, seed=11)
-    _, _, perm, _, src = M.layout(idx.numpy(), E)
+    _, _, perm, inv, src = M.layout(idx.numpy(), E)
     dt = torch.bfloat16 if act == "bf16" else torch.float32
     x = torch.randn((T, d), dtype=torch.float32).to(dt)
     desc = api.make_desc(T, d, E, k, 128, act=act, experts=act)
     xp = torch.empty((T * k, d), dtype=dt, device="cuda")
-    api.moe_gather(desc, x.cuda(), torch.from_numpy(perm.astype(np.int32)).cuda(), xp)
+    dev = lambda a: torch.from_numpy(a.astype(np.int32)).cuda()
+    if mode == "pull":
+        api.moe_gather(desc, x.cuda(), dev(perm), xp)
+    else:
+        api.moe_gather(desc, x.cuda(), None, xp, inv=dev(inv))
     torch.cuda.synchronize()
     assert torch.equal(xp.cpu(), x[torch.from_numpy(src)])
+
+
+def test_gather_push_skips_rows_out_of_range():
+    T, d, E, k = 130, 256, 16, 2
+    idx = synth.random_topk(T, E, k, seed=5)
+    _, _, _, inv, src = M.layout(idx.numpy(), E)
+    bad = inv.copy()
+    lost = [int(bad[3]), int(bad[100])]
+    bad[3], bad[100] = -1, T * k
+    x = torch.randn((T, d), dtype=torch.float32).to(torch.bfloat16)
+    desc = api.make_desc(T, d, E, k, 128)
+    xp = torch.full((T * k, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    api.moe_gather(desc, x.cuda(), None, xp, inv=torch.from_numpy(bad.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    want = x[torch.from_numpy(src)]
+    want[lost] = 7.0
+    assert torch.equal(xp.cpu(), want)
 
 
 def test_host_validation_errors():
