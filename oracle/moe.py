@@ -1,5 +1,6 @@
 """fp64 CPU oracle of the MoE layer: route, count, lay out, gather, expert
-SwiGLU FFN, weighted combine, and the backward of the expert path.
+SwiGLU FFN, weighted combine, the backward of the expert path, and the
+router backward through the gates.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Plain numpy, fp64 for
 every floating-point step; the one place where floating point decides an
@@ -291,6 +292,66 @@ def backward(dy, fwd, w1, w3, w2, k):
     dgate = dgate_row[inv].reshape(T, k)
     return dict(dx=dx, dw1=dW1, dw3=dW3, dw2=dW2, dgate=dgate,
                 G=G, dHu=dHu, dA=dA, dB=dB, dXp=dXp)
+
+
+# --------------------------------------------------------------------------
+# Router backward with the selection frozen.  MoK flash §01: the router
+# decides every step which experts a token goes to; training runs the layer
+# backwards, and the router's part of that is the gradient through the gates
+# (the choice itself is piecewise constant and passes no gradient).
+# --------------------------------------------------------------------------
+def gate_grad_to_logits(z, idx, dgate, score, renorm):
+    """dL/dz [T, E] from dL/dgate [T, k] for biased logits z [T, E].
+
+    Two chain-rule steps, gates -> scores -> logits:
+      softmax, renorm    : g = exp(z_sel) / sum exp(z_sel);
+                           dz_j = g_j (dg_j - sum_i g_i dg_i), chosen j only
+      softmax, no renorm : g_j = p(z)[e_j] with p the softmax over all E;
+                           dz_e = p_e ([e chosen] dg_e - sum_j g_j dg_j)
+      sigmoid, renorm    : g = s_sel / S, S = sum s_sel, s = sigmoid(z);
+                           dL/ds_j = (dg_j - sum_i g_i dg_i) / S,
+                           dz_j = dL/ds_j * s_j (1 - s_j)
+      sigmoid, no renorm : dz_j = dg_j s_j (1 - s_j)
+    """
+    z = _f64(z)
+    dg = _f64(dgate)
+    T, E = z.shape
+    k = idx.shape[1]
+    zsel = np.take_along_axis(z, idx, axis=1)
+    dz = np.zeros((T, E))
+    if score == SOFTMAX:
+        if renorm:
+            g = np.exp(zsel - zsel.max(axis=1, keepdims=True))
+            g = g / g.sum(axis=1, keepdims=True)
+            dsel = g * (dg - np.sum(g * dg, axis=1, keepdims=True))
+        else:
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            p = p / p.sum(axis=1, keepdims=True)
+            g = np.take_along_axis(p, idx, axis=1)
+            dp = np.zeros((T, E))
+            np.put_along_axis(dp, idx, dg, axis=1)
+            return p * (dp - np.sum(g * dg, axis=1, keepdims=True))
+    elif score == SIGMOID:
+        sv = sigmoid(zsel)
+        if renorm:
+            S = sv.sum(axis=1, keepdims=True)
+            g = sv / S
+            ds = (dg - np.sum(g * dg, axis=1, keepdims=True)) / S
+        else:
+            ds = dg
+        dsel = ds * sv * (1.0 - sv)
+    else:
+        raise ValueError(f"unknown score function {score!r}")
+    np.put_along_axis(dz, idx, dsel, axis=1)
+    return dz
+
+
+def router_backward(x, wr, z, idx, dgate, score, renorm):
+    """Gradients of the router for biased logits z = x wr^T + bias:
+    dz = gate_grad_to_logits(...), dwr = dz^T x, dbias = sum_t dz,
+    dx_router = dz wr (to be added to the expert path's dx)."""
+    dz = gate_grad_to_logits(z, idx, dgate, score, renorm)
+    return dict(dlogits=dz, dwr=dz.T @ _f64(x), dbias=dz.sum(axis=0), dx=dz @ _f64(wr))
 
 
 # --------------------------------------------------------------------------
