@@ -293,6 +293,28 @@ def main():
             torch.cuda.synchronize()
             side[name] = a.elapsed_time(b) / reps
         del xq_, xs_, lay, lws
+    if w.backward and not (w.score == "softmax" and not w.renorm):
+        # the router backward (moe_router_backward) after the step's
+        # backward, timed apart: it is not part of the measured step
+        rdesc = layer.desc_for(w, fused=fused)
+        rws = layer.workspace(rdesc)
+        rout = dict(dwr=torch.empty((w.E, w.d), dtype=y.dtype, device="cuda"),
+                    dbias=torch.empty((w.E,), dtype=torch.float32, device="cuda"),
+                    dlogits=torch.empty((w.T, w.E), dtype=torch.float32, device="cuda"))
+        dx_r = grads["dx"].clone()
+        rfn = lambda: api.moe_router_backward(rdesc, dev["x"], dev["wr"], dev["bias"], sv, grads["dgate"],
+                                              rout["dlogits"], rout["dwr"],
+                                              rout["dbias"] if dev["bias"] is not None else None, dx_r, rws,
+                                              stream)
+        rfn()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(10):
+            rfn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        side["router_backward"] = a.elapsed_time(b) / 10
+        del rws, rout, dx_r
     fwd_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
     bwd_ms = sum(b.elapsed_time(c) for _, b, c in marks) / args.steps if w.backward else 0.0
     ms_step = elapsed * 1e3 / args.steps
@@ -321,6 +343,8 @@ def main():
         phases["gather_gbs"] = round(gbytes / (side["gather"] * 1e-3) / 1e9, 1)
         phases["gather_hbm_frac"] = round(gbytes / (side["gather"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         phases["gather_pull_gbs"] = round(gbytes / (side["gather_pull"] * 1e-3) / 1e9, 1)
+    if "router_backward" in side:
+        phases["router_backward_ms"] = round(side["router_backward"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:

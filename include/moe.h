@@ -155,7 +155,7 @@ typedef struct moe_saved {
 } moe_saved;
 
 /* Bytes of workspace the calls below need for `desc` (covers moe_forward,
- * moe_backward, moe_layout and moe_gather).  Returns MOE_ERR_INVALID_ARG for
+ * moe_backward, moe_router_backward, moe_layout and moe_gather).  Returns MOE_ERR_INVALID_ARG for
  * an invalid descriptor.  Host only. */
 MOE_API int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 
@@ -247,6 +247,35 @@ MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
                  const moe_weights* w, const moe_saved* saved, void* dx,
                  void* dw1, void* dw3, void* dw2, float* dgate,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Router backward through the gates (the router step of MoK flash §01 run
+ * backwards; the selection is piecewise constant and passes no gradient).
+ * With the chosen experts frozen, dgate flows to the biased logits
+ * z = x Wr^T + bias of the chosen experts:
+ *   softmax, renorm: dz_j = g_j (dg_j - sum_i g_i dg_i)
+ *   sigmoid, renorm: dz_j = (dg_j - sum_i g_i dg_i) / S * s_j (1 - s_j),
+ *                    s = sigmoid(z), S = sum of the chosen s
+ *   sigmoid, plain : dz_j = dg_j s_j (1 - s_j)
+ * (softmax without renorm makes every logit's gradient nonzero:
+ * MOE_ERR_UNSUPPORTED), zero for the other logits, and then
+ *   dwr = dz^T x, dbias = sum over tokens of dz, dx += dz Wr.
+ *   x       act [T, d]   the forward's input
+ *   wr      act [E, d]   router weight (as in moe_forward)
+ *   bias    float [E] or NULL, the router bias of the forward
+ *   saved   the forward's logits, topk_idx, gate, offsets and perm (all
+ *           required); other fields ignored
+ *   dgate   float [T, k] gradient of the gates (moe_backward's output)
+ *   dlogits float [T, E] output or NULL: dL/dz
+ *   dwr     act [E, d]   output (fp32 accumulation, overwritten)
+ *   dbias   float [E] output or NULL
+ *   dx      act [T, d]   in/out: dz Wr is ADDED to it (pass the expert
+ *           path's dx from moe_backward to get the layer's full dx)
+ * Every sum runs in a fixed order: results are deterministic.  Uses the
+ * workspace of moe_workspace_size. */
+MOE_API int moe_router_backward(const moe_desc* desc, const void* x, const void* wr, const float* bias,
+                        const moe_saved* saved, const float* dgate, float* dlogits, void* dwr,
+                        float* dbias, void* dx, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Static description of a status code. */
 MOE_API const char* moe_status_string(int status);

@@ -72,14 +72,18 @@ _lib.moe_forward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWe
 _lib.moe_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, _P(MoeWeights), _P(MoeSaved),
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               ctypes.c_size_t, c_void_p]
+_lib.moe_router_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeSaved),
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     ctypes.c_size_t, c_void_p]
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_status_string.restype = ctypes.c_char_p
 for _f in ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather", "moe_quantize_mxfp8",
-           "moe_forward", "moe_backward"):
+           "moe_forward", "moe_backward", "moe_router_backward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather",
-           "moe_quantize_mxfp8", "moe_forward", "moe_backward", "moe_status_string")
+           "moe_quantize_mxfp8", "moe_forward", "moe_backward", "moe_router_backward",
+           "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -168,3 +172,11 @@ def moe_backward(desc, dy, x, weights: MoeWeights, saved: MoeSaved, dx, dw1, dw3
                              ctypes.byref(saved), _p(dx), _p(dw1), _p(dw3), _p(dw2), _p(dgate),
                              _p(workspace), 0 if workspace is None else workspace.numel(),
                              _stream(stream)), "moe_backward")
+
+
+def moe_router_backward(desc, x, wr, bias, saved: MoeSaved, dgate, dlogits, dwr, dbias, dx,
+                        workspace, stream=None):
+    _check(_lib.moe_router_backward(ctypes.byref(desc), _p(x), _p(wr), _p(bias), ctypes.byref(saved),
+                                    _p(dgate), _p(dlogits), _p(dwr), _p(dbias), _p(dx), _p(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(stream)),
+           "moe_router_backward")

@@ -18,6 +18,7 @@
 #include "tasks_bwd.h"
 #include "sched.h"
 #include "mxfp8.h"
+#include "router_bwd.h"
 
 namespace moe {
 
@@ -107,6 +108,9 @@ int make_plan(const moe_desc* D, Plan* p) {
     p->o_dab = take(R * 2 * I * 2);
     p->o_dgp = take((size_t)p->nNdh * R * 4);
   }
+  p->o_rdz = take(R * 4);
+  p->o_rpart = take((size_t)kRbSplits * E * d * 4);
+  p->o_rpbias = take((size_t)kRbSplits * E * 4);
   p->total = o;
   return MOE_OK;
 }
@@ -832,6 +836,45 @@ int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_
     return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   return backward_impl(p, desc, dy, x, w, saved, dx, dw1, dw3, dw2, dgate, workspace, (hipStream_t)stream);
+}
+
+int moe_router_backward(const moe_desc* desc, const void* x, const void* wr, const float* bias,
+                        const moe_saved* saved, const float* dgate, float* dlogits, void* dwr, float* dbias,
+                        void* dx, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (desc->score == MOE_SCORE_SOFTMAX && !desc->renorm) return MOE_ERR_UNSUPPORTED;
+  if (!saved || !wr || !dwr || !saved->offsets) return MOE_ERR_INVALID_ARG;
+  if (p.T > 0 && (!x || !dx || !dgate || !saved->logits || !saved->topk_idx || !saved->gate || !saved->perm))
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  RouterBwd P;
+  memset(&P, 0, sizeof(P));
+  P.T = p.T; P.d = p.d; P.E = p.E; P.k = p.k; P.R = p.R;
+  P.score = desc->score; P.renorm = desc->renorm ? 1 : 0;
+  P.x = x; P.wr = wr; P.bias = bias; P.logits = saved->logits; P.topk = saved->topk_idx;
+  P.gate = saved->gate; P.dgate = dgate; P.offsets = saved->offsets; P.perm = saved->perm;
+  P.dz = at<float>(workspace, p.o_rdz);
+  P.part = at<float>(workspace, p.o_rpart);
+  P.pbias = at<float>(workspace, p.o_rpbias);
+  P.dlogits = dlogits; P.dwr = dwr; P.dbias = dbias; P.dx = dx;
+  hipStream_t st = (hipStream_t)stream;
+  const int nvec = p.d * p.act_es / 16;
+  const int tgrid = cdiv(p.T, 4) < 4096 ? cdiv(p.T, 4) : 4096;
+  const int64_t nel = (int64_t)p.E * p.d;
+  const int fgrid = (int)(cdiv64(nel, 256) < 8192 ? cdiv64(nel, 256) : 8192);
+  const dim3 wgrid(p.E, cdiv(nvec, 64), kRbSplits);
+  if (p.f32) {
+    if (p.T > 0) hipLaunchKernelGGL(k_router_bwd_tokens<float>, dim3(tgrid), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_router_bwd_dwr<float>, wgrid, dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_router_bwd_final<float>, dim3(fgrid), dim3(256), 0, st, P);
+  } else {
+    if (p.T > 0) hipLaunchKernelGGL(k_router_bwd_tokens<bf16_t>, dim3(tgrid), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_router_bwd_dwr<bf16_t>, wgrid, dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_router_bwd_final<bf16_t>, dim3(fgrid), dim3(256), 0, st, P);
+  }
+  return launch_status();
 }
 
 const char* moe_status_string(int status) {

@@ -102,3 +102,21 @@ def backward(w, inp, saved, fused=True, ws=None, flags=0, n_workgroups=0, weight
     api.moe_backward(d, inp["dy"], inp["x"], weights, api.make_saved(**saved), out["dx"],
                      out["dw1"], out["dw3"], out["dw2"], out["dgate"], ws)
     return out
+
+
+def router_backward(w, inp, saved, dgate, dx, ws=None, dlogits=True):
+    """Runs moe_router_backward: adds the router's part into dx (in place)
+    and returns dict dwr, dbias (None without a bias) and dlogits (None when
+    not asked for)."""
+    dev = inp["x"].device
+    T = inp["x"].shape[0]
+    d = desc_for(w, True, T=T)
+    if ws is None:
+        ws = workspace(d, dev)
+    out = dict(dwr=torch.empty((w.E, w.d), dtype=_ACT[w.act], device=dev),
+               dbias=(torch.empty((w.E,), dtype=torch.float32, device=dev)
+                      if inp.get("bias") is not None else None),
+               dlogits=torch.empty((T, w.E), dtype=torch.float32, device=dev) if dlogits else None)
+    api.moe_router_backward(d, inp["x"], inp["wr"], inp.get("bias"), api.make_saved(**saved), dgate,
+                            out["dlogits"], out["dwr"], out["dbias"], dx, ws)
+    return out

@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_entry_points()
     for n in ("moe_route", "moe_layout", "moe_forward", "moe_backward", "moe_workspace_size",
-              "moe_status_string", "moe_gather"):
+              "moe_status_string", "moe_gather", "moe_router_backward"):
         assert n in names
 
 
@@ -95,6 +95,20 @@ def test_entry_points_reject_bad_arguments_before_launching(lib):
     # the backward is bf16 only
     assert lib.moe_backward(ctypes.byref(_desc(T=64, d=256, E=8, k=2, I=128, act_dtype=0, expert_dtype=0)),
                             None, None, None, None, None, None, None, None, None, None, 0, None) == -2
+
+
+def test_router_backward_rejects_bad_arguments_before_launching(lib):
+    vp = ctypes.c_void_p
+    lib.moe_router_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+    # softmax without renormalisation: every logit's gradient is nonzero
+    plain = _desc(T=64, d=256, E=8, k=2, I=128, score=0, renorm=0)
+    assert lib.moe_router_backward(ctypes.byref(plain), None, None, None, None, None, None, None, None,
+                                   None, None, 0, None) == -2
+    # a missing saved struct
+    d = _desc(T=64, d=256, E=8, k=2, I=128)
+    assert lib.moe_router_backward(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                                   None, None, 0, None) == -1
 
 
 def test_status_strings(lib):

@@ -1,0 +1,139 @@
+"""GPU parity of moe_router_backward against the fp64 oracle.
+
+Isolated: both sides take the same inputs -- the routing the GPU forward
+saved (fp32 logits, top-k, gates, layout) and one seeded dgate -- so the
+comparison covers the router backward alone.  dlogits and dbias are fp32 on
+the GPU against fp64 (max error relative to the tensor's max <= 1e-5); dWr
+per expert row and dx per token row, max row-relative error <= 1e-2 in bf16
+(one bf16 rounding of an fp32 sum) and 1e-5 in fp32.  dlogits must be exactly
+zero off the chosen experts, experts without rows get dWr = 0 exactly, and two
+calls give identical bits (every sum runs in a fixed order).
+
+Chained: moe_backward then moe_router_backward on a bf16 layer with a router
+bias, against the oracle's backward and router backward end to end."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as M
+from mixture_experts_layer_layout_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+api = pytest.importorskip("mixture_experts_layer_layout_amd.api")
+from mixture_experts_layer_layout_amd import layer  # noqa: E402
+from parity import host, row_rel_err  # noqa: E402
+
+CASES = {
+    "tiny-fp32": synth.WORKLOADS["tiny-fp32"],
+    "dsv3-zipf-small": synth.WORKLOADS["dsv3-fwdbwd-zipf"].shrink(T=777, d=512, E=64, I=256),
+    "mixtral-small": synth.WORKLOADS["mixtral-bf16"].shrink(T=300, d=512, I=512),
+    "k-equals-E": synth.WORKLOADS["dsv3-bf16"].shrink(T=129, d=256, E=8, k=8, I=256),
+    "sparse-experts": synth.WORKLOADS["dsv3-bf16"].shrink(T=40, d=256, E=64, k=2, I=256),
+    "sigmoid-plain": synth.WORKLOADS["dsv3-bf16"].shrink(T=200, d=256, E=16, k=4, I=256, renorm=False),
+    "k6": synth.WORKLOADS["dsv3-bf16"].shrink(T=150, d=256, E=32, k=6, I=256),
+}
+
+
+def _setup(w, seed):
+    inp = synth.make_inputs(w, seed)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    _, sv = layer.forward(w, dev)
+    g = torch.Generator().manual_seed(1000 + seed)
+    dgate = torch.randn((w.T, w.k), generator=g, dtype=torch.float32)
+    act = torch.float32 if w.act == "f32" else torch.bfloat16
+    dx0 = torch.randn((w.T, w.d), generator=g, dtype=torch.float32).to(act)
+    return inp, dev, sv, dgate, dx0
+
+
+def _oracle(w, inp, sv, dgate):
+    h = {k: (host(v) if v is not None else None) for k, v in inp.items()}
+    z = host(sv["logits"]) + (h["bias"][None, :] if h["bias"] is not None else 0.0)
+    idx = host(sv["topk_idx"])
+    return M.router_backward(h["x"], h["wr"], z, idx, host(dgate), w.score, w.renorm), idx
+
+
+def _tensor_rel(got, want):
+    return float(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_router_backward_matches_oracle(name):
+    w = CASES[name]
+    inp, dev, sv, dgate, dx0 = _setup(w, 3)
+    dx = dx0.cuda()
+    r = layer.router_backward(w, dev, sv, dgate.cuda(), dx)
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    o, idx = _oracle(w, inp, sv, dgate)
+    tol = 1e-5 if w.act == "f32" else 1e-2
+    got_dl = host(r["dlogits"])
+    chosen = np.zeros_like(got_dl, dtype=bool)
+    np.put_along_axis(chosen, idx, True, axis=1)
+    assert np.all(got_dl[~chosen] == 0.0), "dlogits nonzero off the chosen experts"
+    assert _tensor_rel(got_dl, o["dlogits"]) <= 1e-5
+    if r["dbias"] is not None:
+        assert _tensor_rel(host(r["dbias"]), o["dbias"]) <= 1e-5
+    counts = host(sv["counts"])
+    got_dwr = host(r["dwr"])
+    for e in range(w.E):
+        if counts[e] == 0:
+            assert np.all(got_dwr[e] == 0.0), f"dwr[{e}] of an expert without rows is not zero"
+        else:
+            err = row_rel_err(got_dwr[e:e + 1], o["dwr"][e:e + 1])
+            assert err <= tol, f"dwr[{e}] row-relative error {err:.3e} > {tol}"
+    want_dx = host(dx0) + o["dx"]
+    err = row_rel_err(host(dx), want_dx)
+    assert err <= tol, f"dx row-relative error {err:.3e} > {tol}"
+
+
+def test_router_backward_is_deterministic():
+    w = CASES["dsv3-zipf-small"]
+    inp, dev, sv, dgate, dx0 = _setup(w, 4)
+    outs = []
+    for _ in range(2):
+        dx = dx0.cuda()
+        r = layer.router_backward(w, dev, sv, dgate.cuda(), dx)
+        torch.cuda.synchronize()
+        outs.append((r["dwr"].cpu(), r["dbias"].cpu(), r["dlogits"].cpu(), dx.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_router_backward_without_optional_outputs():
+    w = CASES["mixtral-small"]
+    inp, dev, sv, dgate, dx0 = _setup(w, 5)
+    dx = dx0.cuda()
+    r = layer.router_backward(w, dev, sv, dgate.cuda(), dx, dlogits=False)
+    torch.cuda.synchronize()
+    o, _ = _oracle(w, inp, sv, dgate)
+    assert r["dlogits"] is None and r["dbias"] is None
+    assert row_rel_err(host(r["dwr"]), o["dwr"]) <= 1e-2
+
+
+def test_layer_gradients_end_to_end_bf16():
+    """moe_backward + moe_router_backward against the oracle's full dx, dWr,
+    dbias and dlogits (bf16 layer with a router bias).  The GPU's dgate comes
+    from bf16 operands, and dz = g (dg - sum g dg) can cancel within a token,
+    so dWr, dbias and dlogits are compared by the max error relative to the
+    tensor's max, at the bf16 bar of 2e-2; dx per token row."""
+    w = synth.WORKLOADS["dsv3-fwdbwd-zipf"].shrink(T=500, d=512, E=64, I=256)
+    inp = synth.make_inputs(w, 6, with_dy=True)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    _, sv = layer.forward(w, dev)
+    g = layer.backward(w, dev, sv)
+    r = layer.router_backward(w, dev, sv, g["dgate"], g["dx"])
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    h = {k: (host(v) if v is not None else None) for k, v in inp.items()}
+    logits = host(sv["logits"])
+    f = M.forward(h["x"], h["wr"], h["bias"], h["w1"], h["w3"], h["w2"], w.k, w.score, w.renorm,
+                  logits=logits)
+    assert np.array_equal(host(sv["topk_idx"]), f["topk_idx"])
+    b = M.backward(h["dy"], f, h["w1"], h["w3"], h["w2"], w.k)
+    z = logits + h["bias"][None, :]
+    o = M.router_backward(h["x"], h["wr"], z, f["topk_idx"], b["dgate"], w.score, w.renorm)
+    assert row_rel_err(host(g["dx"]), b["dx"] + o["dx"]) <= 2e-2
+    for n in ("dwr", "dbias", "dlogits"):
+        err = _tensor_rel(host(r[n]), o[n])
+        assert err <= 2e-2, f"{n}: {err:.3e}"
