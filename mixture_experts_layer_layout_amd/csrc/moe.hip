@@ -600,7 +600,7 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
       int rc = launch_fused_fwd<Act, TL, 0x0Fu>(D, F, smem, st);
       if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x10u>(D, F, smem, st);
       if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
-      if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, 0, st);
       return rc;
     }
     // Routing through the up projection in one launch (each up-projection
@@ -608,9 +608,12 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
     // the combine: a down-projection tile would need every up-projection
     // tile of its rows released at agent scope, an L2 write-back per tile,
     // which costs more on this chip than the launch boundary.
+    // The combine uses no dynamic LDS: its launch reserves none, so as many
+    // workgroups fit per CU as its registers allow (with the tile's LDS it
+    // ran one per CU).
     int rc = launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st);
     if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
-    if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, smem, st);
+    if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, 0, st);
     return rc;
   }
   hipLaunchKernelGGL(k_router_partial<Act>, dim3(p.nb * p.S), dim3(256), 0, st, F);
@@ -666,12 +669,15 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     // not fit two workgroups' registers per CU (MOE_FLAG_PERSISTENT_SINGLE
     // runs it anyway).
     if (!(D->flags & (MOE_FLAG_PERSISTENT_SINGLE | MOE_FLAG_PERSISTENT_WGRAD_APART))) {
-      int rc = launch_fused_bwd<0x03u>(D, B, smem, st);
+      // each launch reserves the LDS its own tasks use: the setup's scan
+      // area, the tiles' stages, none for the dX gather-sum
+      const size_t sm_setup = (2 * kMaxE + 16) * sizeof(int);
+      int rc = launch_fused_bwd<0x03u>(D, B, sm_setup, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, sm_dh, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x10u>(D, B, sm_dh, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x40u>(D, B, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x40u>(D, B, 0, st);
       return rc;
     }
     if (D->flags & MOE_FLAG_PERSISTENT_WGRAD_APART) {
