@@ -10,7 +10,9 @@ oracle where the oracle can follow:
     its own row, so the oracle forward/backward run on a subset of tokens
     gives those tokens' exact values;
   * dW1/dW3/dW2 of sampled experts from the oracle's per-expert backward
-    over exactly that expert's rows.
+    over exactly that expert's rows;
+  * the router backward over every token and expert, given the GPU's saved
+    routing and dgate.
 Expert weights are drawn on the device (as bench.py does); the oracle reads
 the experts it needs back one at a time."""
 import numpy as np
@@ -150,3 +152,31 @@ def test_fullsize_mxfp8():
     err = row_rel_err(host(y)[ts], f["y"])
     print(f"  y sampled max row-rel err {err:.2e}", flush=True)
     assert err <= 6e-2
+
+
+def test_fullsize_router_backward():
+    """moe_router_backward at the DeepSeek-V3 Zipf shape, fed the routing the
+    GPU forward saved and the dgate its backward produced; the oracle takes
+    the same routing and dgate.  dlogits and dbias over every token (fp32,
+    1e-5 of the tensor max), dWr per expert row and dx per token row (bf16,
+    1e-2), computed in full on the host."""
+    w = synth.WORKLOADS["dsv3-fwdbwd-zipf"]
+    print(f"\nfull-size router backward {w.name}: T={w.T} d={w.d} E={w.E} k={w.k}", flush=True)
+    inp, dev = full_inputs(w, 0)
+    _, sv = layer.forward(w, dev, fused=True)
+    g = layer.backward(w, dev, sv, fused=True)
+    dx_in = g["dx"].clone()
+    r = layer.router_backward(w, dev, sv, g["dgate"], g["dx"])
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    x = host(inp["x"])
+    wr = host(inp["wr"])
+    z = host(sv["logits"]) + inp["bias"].numpy().astype(np.float64)[None, :]
+    o = M.router_backward(x, wr, z, host(sv["topk_idx"]), host(g["dgate"]), w.score, w.renorm)
+    rel = lambda a, b: float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+    e1, e2 = rel(host(r["dlogits"]), o["dlogits"]), rel(host(r["dbias"]), o["dbias"])
+    e3 = max(row_rel_err(host(r["dwr"])[e:e + 1], o["dwr"][e:e + 1]) for e in range(w.E))
+    e4 = row_rel_err(host(g["dx"]), host(dx_in) + o["dx"])
+    print(f"  dlogits {e1:.2e} dbias {e2:.2e} dwr {e3:.2e} dx {e4:.2e}", flush=True)
+    assert e1 <= 1e-5 and e2 <= 1e-5
+    assert e3 <= 1e-2 and e4 <= 1e-2
