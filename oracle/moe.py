@@ -96,18 +96,60 @@ def gates_from_logits(logits, idx, score, renorm):
     raise ValueError(f"unknown score function {score!r}")
 
 
-def route(logits, k, score, renorm, bias=None):
+def select_grouped(keys, k, n_group, topk_group):
+    """Group-limited selection.  The E experts form n_group groups of E /
+    n_group consecutive ids; a group's score is the sum of its two largest
+    keys (its only key when a group holds one expert); the topk_group groups
+    with the largest scores are kept (ties to the lower group), and the k
+    largest keys among the kept experts are chosen (ties to the lower
+    expert), largest first."""
+    keys = np.asarray(keys)
+    T, E = keys.shape
+    if E % n_group or not (1 <= topk_group <= n_group) or k > topk_group * (E // n_group):
+        raise ValueError("bad grouping")
+    gs = E // n_group
+    grouped = keys.reshape(T, n_group, gs)
+    top = -np.sort(-grouped, axis=2)
+    gscore = top[:, :, 0] + (top[:, :, 1] if gs > 1 else 0.0)
+    kept = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, kept, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), keys, -np.inf)
+    return select_topk(masked, k)
+
+
+def route(logits, k, score, renorm, bias=None, select_only=False, n_group=0, topk_group=0,
+          routed_scale=1.0):
     """Top-k selection and gates from router logits.
 
     ``bias`` (if given) is added to the logits in the logits' own dtype
     before anything else, so an fp32 caller gets the same fp32 sums the
     kernel forms; selection then compares those values directly.
+
+    DeepSeek-V3-style options (sigmoid scores only):
+      select_only  the bias steers the selection only: the experts are
+                   ranked by sigmoid(logit) + bias and the gates come from
+                   the unbiased logits
+      n_group > 1  group-limited selection (select_grouped) over the keys
+                   sigmoid(z) + (bias if select_only), z the gate logits
+    With either option the keys live in score space; the plain path ranks
+    the (biased) logits themselves.  routed_scale multiplies every gate.
     """
     logits = np.asarray(logits)
-    if bias is not None:
-        logits = logits + np.asarray(bias, dtype=logits.dtype)[None, :]
-    idx = select_topk(logits, k)
-    gate = gates_from_logits(logits, idx, score, renorm)
+    keyed = select_only or n_group > 1
+    if keyed and score != SIGMOID:
+        raise ValueError("selection-only bias and grouped routing need sigmoid scores")
+    z = logits
+    if bias is not None and not select_only:
+        z = logits + np.asarray(bias, dtype=logits.dtype)[None, :]
+    if keyed:
+        keys = sigmoid(_f64(z))
+        if select_only and bias is not None:
+            keys = keys + _f64(bias)[None, :]
+        idx = select_grouped(keys, k, n_group, topk_group) if n_group > 1 else select_topk(keys, k)
+    else:
+        idx = select_topk(z, k)
+    gate = gates_from_logits(z, idx, score, renorm) * routed_scale
     return idx, gate
 
 
@@ -215,17 +257,18 @@ def combine(yp, gate, inv, T, k):
     return y
 
 
-def forward(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
+def forward(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None, **routing):
     """The whole forward.  Returns a dict of every intermediate.
 
     ``logits`` may be given to route on fixed logits (fp32 as the kernel
-    would form them); otherwise the fp64 router GEMM is used.
+    would form them); otherwise the fp64 router GEMM is used.  ``routing``
+    takes route()'s DeepSeek-V3-style options.
     """
     T = np.shape(x)[0]
     E = np.shape(w1)[0]
     if logits is None:
         logits = router_logits(x, wr, None)
-    idx, gate = route(logits, k, score, renorm, bias)
+    idx, gate = route(logits, k, score, renorm, bias, **routing)
     counts, offsets, perm, inv, src = layout(idx, E)
     xp = gather(_f64(x), src)
     A, B, H, Yp = grouped_ffn(xp, offsets, w1, w3, w2)
@@ -300,8 +343,10 @@ def backward(dy, fwd, w1, w3, w2, k):
 # backwards, and the router's part of that is the gradient through the gates
 # (the choice itself is piecewise constant and passes no gradient).
 # --------------------------------------------------------------------------
-def gate_grad_to_logits(z, idx, dgate, score, renorm):
-    """dL/dz [T, E] from dL/dgate [T, k] for biased logits z [T, E].
+def gate_grad_to_logits(z, idx, dgate, score, renorm, routed_scale=1.0):
+    """dL/dz [T, E] from dL/dgate [T, k] for the gate logits z [T, E] (the
+    logits the gates are computed from).  Gates scaled by routed_scale c pass
+    c dL/dgate to the unscaled gates g below.
 
     Two chain-rule steps, gates -> scores -> logits:
       softmax, renorm    : g = exp(z_sel) / sum exp(z_sel);
@@ -314,7 +359,7 @@ def gate_grad_to_logits(z, idx, dgate, score, renorm):
       sigmoid, no renorm : dz_j = dg_j s_j (1 - s_j)
     """
     z = _f64(z)
-    dg = _f64(dgate)
+    dg = _f64(dgate) * routed_scale
     T, E = z.shape
     k = idx.shape[1]
     zsel = np.take_along_axis(z, idx, axis=1)
@@ -346,12 +391,15 @@ def gate_grad_to_logits(z, idx, dgate, score, renorm):
     return dz
 
 
-def router_backward(x, wr, z, idx, dgate, score, renorm):
-    """Gradients of the router for biased logits z = x wr^T + bias:
-    dz = gate_grad_to_logits(...), dwr = dz^T x, dbias = sum_t dz,
-    dx_router = dz wr (to be added to the expert path's dx)."""
-    dz = gate_grad_to_logits(z, idx, dgate, score, renorm)
-    return dict(dlogits=dz, dwr=dz.T @ _f64(x), dbias=dz.sum(axis=0), dx=dz @ _f64(wr))
+def router_backward(x, wr, z, idx, dgate, score, renorm, routed_scale=1.0, select_only=False):
+    """Gradients of the router for the gate logits z = x wr^T (+ bias unless
+    the bias only steers the selection): dz = gate_grad_to_logits(...),
+    dwr = dz^T x, dbias = sum_t dz (zero for a selection-only bias, which the
+    gates never see), dx_router = dz wr (to be added to the expert path's
+    dx)."""
+    dz = gate_grad_to_logits(z, idx, dgate, score, renorm, routed_scale)
+    dbias = np.zeros(dz.shape[1]) if select_only else dz.sum(axis=0)
+    return dict(dlogits=dz, dwr=dz.T @ _f64(x), dbias=dbias, dx=dz @ _f64(wr))
 
 
 # --------------------------------------------------------------------------
