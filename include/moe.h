@@ -91,6 +91,20 @@ typedef struct moe_desc {
                             (MXFP8 experts: 0 or 128)                      */
   int32_t n_workgroups;  /* persistent grid size, 0 = auto (all CUs)       */
   uint32_t flags;        /* MOE_FLAG_* below                                */
+  /* DeepSeek-V3-style routing options (0 = off):
+   * n_group, topk_group: group-limited selection.  The E experts form
+   *   n_group groups of E / n_group consecutive ids (E % n_group == 0,
+   *   n_group <= 64); a group's score is the sum of its two largest keys;
+   *   the topk_group best groups are kept (ties to the lower group) and the
+   *   k experts are chosen among them (k <= topk_group * E / n_group).
+   * routed_scale: factor on every gate (0 means 1).
+   * With n_group > 1 or MOE_FLAG_BIAS_SELECT_ONLY the experts are ranked
+   * by the key sigmoid(z) (+ bias with MOE_FLAG_BIAS_SELECT_ONLY), z the
+   * gate logits; both need score MOE_SCORE_SIGMOID.  Without them the
+   * (biased) logits themselves are ranked. */
+  int32_t n_group;
+  int32_t topk_group;
+  float routed_scale;
 } moe_desc;
 
 /* Flags. */
@@ -106,6 +120,10 @@ typedef struct moe_desc {
                                       gradients after the rest           */
 #define MOE_FLAG_PERSISTENT_SINGLE 0x8u /* fused forward and backward: every
                                       phase in one persistent launch     */
+#define MOE_FLAG_BIAS_SELECT_ONLY 0x10u /* the router bias steers the
+                                      selection only: experts ranked by
+                                      sigmoid(logit) + bias, gates from the
+                                      unbiased logits, no bias gradient    */
 #define MOE_FLAG_SPIN_LIMIT_TINY 0x100u /* test only: bounded waits give up
                                       after a few polls (exercises the
                                       MOE_ERR_TIMEOUT path)                 */
@@ -270,6 +288,9 @@ MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
  *   dbias   float [E] output or NULL
  *   dx      act [T, d]   in/out: dz Wr is ADDED to it (pass the expert
  *           path's dx from moe_backward to get the layer's full dx)
+ * Gates scaled by desc->routed_scale c: the unscaled gate g / c receives
+ * c dgate.  With MOE_FLAG_BIAS_SELECT_ONLY the gate logits exclude the bias
+ * and dbias is written as zeros (the bias steers the selection only).
  * Every sum runs in a fixed order: results are deterministic.  Uses the
  * workspace of moe_workspace_size. */
 MOE_API int moe_router_backward(const moe_desc* desc, const void* x, const void* wr, const float* bias,

@@ -33,6 +33,7 @@ MOE_FLAG_DIRECT_PULL = 0x1
 MOE_FLAG_PERSISTENT_SPLIT = 0x2
 MOE_FLAG_PERSISTENT_WGRAD_APART = 0x4
 MOE_FLAG_PERSISTENT_SINGLE = 0x8
+MOE_FLAG_BIAS_SELECT_ONLY = 0x10
 MOE_FLAG_SPIN_LIMIT_TINY = 0x100
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
@@ -44,7 +45,8 @@ class MoeDesc(ctypes.Structure):
                 ("I", c_int32), ("act_dtype", c_int32), ("expert_dtype", c_int32),
                 ("score", c_int32), ("renorm", c_int32), ("fused", c_int32),
                 ("stage_rows", c_int32), ("n_workgroups", c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("n_group", c_int32), ("topk_group", c_int32),
+                ("routed_scale", ctypes.c_float)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -112,9 +114,11 @@ def _stream(stream):
 
 
 def make_desc(T, d, E, k, I, act="bf16", experts="bf16", score="sigmoid", renorm=True,
-              fused=True, stage_rows=0, n_workgroups=0, flags=0) -> MoeDesc:
+              fused=True, stage_rows=0, n_workgroups=0, flags=0, n_group=0, topk_group=0,
+              routed_scale=0.0) -> MoeDesc:
     return MoeDesc(T, d, E, k, I, _DT[act], _DT[experts], _SC[score], int(bool(renorm)),
-                   int(bool(fused)), stage_rows, n_workgroups, flags)
+                   int(bool(fused)), stage_rows, n_workgroups, flags, n_group, topk_group,
+                   routed_scale)
 
 
 def moe_workspace_size(desc: MoeDesc) -> int:

@@ -43,6 +43,14 @@ int make_plan(const moe_desc* D, Plan* p) {
     return MOE_ERR_INVALID_ARG;
   }
   if (D->stage_rows != 0 && D->stage_rows != 128 && D->stage_rows != 256) return MOE_ERR_UNSUPPORTED;
+  // routing options
+  if (D->n_group < 0 || D->topk_group < 0 || !(D->routed_scale >= 0.0f) || D->routed_scale > 3.0e38f)
+    return MOE_ERR_INVALID_ARG;
+  if (D->n_group > 1 && (D->n_group > 64 || E % D->n_group || D->topk_group < 1 || D->topk_group > D->n_group ||
+                         k > D->topk_group * (E / D->n_group)))
+    return MOE_ERR_INVALID_ARG;
+  if (((D->flags & MOE_FLAG_BIAS_SELECT_ONLY) || D->n_group > 1) && D->score != MOE_SCORE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
   p->T = T; p->d = d; p->E = E; p->k = k; p->I = I; p->R = T * k;
   p->f32 = f32;
   p->mxfp8 = D->expert_dtype == MOE_MXFP8;
@@ -142,9 +150,18 @@ static Sync make_sync(const Plan& p, void* ws, int32_t* status, uint32_t flags) 
   return s;
 }
 
+// The routing options of a descriptor (validated by make_plan).
+static void set_routing(Fwd& F, const moe_desc* D) {
+  F.select_only = (D->flags & MOE_FLAG_BIAS_SELECT_ONLY) ? 1 : 0;
+  F.n_group = D->n_group > 1 ? D->n_group : 0;
+  F.topk_group = D->n_group > 1 ? D->topk_group : 0;
+  F.scale = D->routed_scale > 0.0f ? D->routed_scale : 1.0f;
+}
+
 static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved* sv) {
   Fwd F;
   memset(&F, 0, sizeof(F));
+  set_routing(F, D);
   F.T = p.T; F.d = p.d; F.E = p.E; F.k = p.k; F.I = p.I; F.R = p.R;
   F.nb = p.nb; F.S = p.S; F.BM = p.BM; F.nN1 = p.nN1; F.nN2 = p.nN2; F.nC = p.nC;
   F.max_tiles = p.max_tiles;
@@ -731,6 +748,7 @@ int moe_route(const moe_desc* desc, const float* logits, const float* bias, int3
   memset(&F, 0, sizeof(F));
   F.T = p.T; F.E = p.E; F.k = p.k; F.S = 1;
   F.score = desc->score; F.renorm = desc->renorm ? 1 : 0;
+  set_routing(F, desc);
   F.lpart = (float*)logits;
   F.bias = bias;
   F.topk = topk_idx;
@@ -863,6 +881,8 @@ int moe_router_backward(const moe_desc* desc, const void* x, const void* wr, con
   memset(&P, 0, sizeof(P));
   P.T = p.T; P.d = p.d; P.E = p.E; P.k = p.k; P.R = p.R;
   P.score = desc->score; P.renorm = desc->renorm ? 1 : 0;
+  P.select_only = (desc->flags & MOE_FLAG_BIAS_SELECT_ONLY) ? 1 : 0;
+  P.scale = desc->routed_scale > 0.0f ? desc->routed_scale : 1.0f;
   P.x = x; P.wr = wr; P.bias = bias; P.logits = saved->logits; P.topk = saved->topk_idx;
   P.gate = saved->gate; P.dgate = dgate; P.offsets = saved->offsets; P.perm = saved->perm;
   P.dz = at<float>(workspace, p.o_rdz);

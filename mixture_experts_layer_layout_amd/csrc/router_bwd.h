@@ -3,7 +3,9 @@
 // MoK flash §01: the router re-decides every step which experts a token goes
 // to.  The choice is piecewise constant, so in training the gradient reaches
 // the router only through the gates of the chosen experts.  With the choice
-// frozen, for the biased logits z = x Wr^T + bias:
+// frozen, for the gate logits z = x Wr^T + bias (no bias when it steers the
+// selection only; it then gets no gradient), and gates divided by the routed
+// scale c with c dgate as their gradient:
 //   softmax, renormalised : dz_j = g_j (dg_j - sum_i g_i dg_i)
 //   sigmoid, renormalised : dz_j = (dg_j - sum_i g_i dg_i) / S * s_j (1 - s_j),
 //                           s = sigmoid(z), S = sum of the chosen s
@@ -26,6 +28,8 @@ constexpr int kRbSplits = 8;  // row splits per expert in the dWr sum
 
 struct RouterBwd {
   int T, d, E, k, R, score, renorm;
+  int select_only;      // the bias steered the selection only: z excludes it, no dbias
+  float scale;          // routed scaling factor of the gates
   const void* x;        // act [T, d]
   const void* wr;       // act [E, d]
   const float* bias;    // [E] or null
@@ -57,9 +61,10 @@ __device__ void router_bwd_token(const RouterBwd& P, int t) {
   float g = 0.0f, dg = 0.0f, z = 0.0f;
   if (mine) {
     e = P.topk[(size_t)t * k + lane];
-    g = P.gate[(size_t)t * k + lane];
-    dg = P.dgate[(size_t)t * k + lane];
-    z = P.logits[(size_t)t * P.E + e] + (P.bias ? P.bias[e] : 0.0f);
+    // the unscaled gate and the gradient it receives
+    g = P.gate[(size_t)t * k + lane] / P.scale;
+    dg = P.dgate[(size_t)t * k + lane] * P.scale;
+    z = P.logits[(size_t)t * P.E + e] + (P.bias && !P.select_only ? P.bias[e] : 0.0f);
   }
   const float gdg = wave_sum(g * dg);
   float dzj;
@@ -208,7 +213,7 @@ __global__ void __launch_bounds__(256) k_router_bwd_final(RouterBwd P) {
       const int e = (int)(i / P.d);
       float b = 0.0f;
       for (int s = 0; s < kRbSplits; ++s) b += P.pbias[(size_t)s * P.E + e];
-      P.dbias[e] = b;
+      P.dbias[e] = P.select_only ? 0.0f : b;
     }
   }
 }

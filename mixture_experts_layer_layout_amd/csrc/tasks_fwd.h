@@ -63,6 +63,10 @@ struct Sync {
 struct Fwd {
   int T, d, E, k, I, R, nb, S, BM, nN1, nN2, nC, max_tiles;
   int score, renorm, direct;
+  // routing options: bias for selection only, group-limited selection
+  // (n_group > 1), factor on the gates
+  int select_only, n_group, topk_group;
+  float scale;
   const void* x;
   const void* wr;
   const float* bias;
@@ -164,20 +168,55 @@ __device__ void router_partial<float>(const Fwd& F, int task) {
   }
 }
 
-// Top-k of one token, one wave, from its E biased logits in LDS.  Lane l
-// owns experts l + 64 q.  Largest value first; equal values go to the lower
-// expert index.  Lane j < k returns the j-th choice and its gate.
-__device__ __forceinline__ void wave_topk_gates(const float* row, int E, int k, int score, int renorm,
+// Top-k of one token, one wave.  key (LDS) holds the E values ranked: the
+// gate logits themselves, or score-space keys sigmoid(z) (+ a selection-only
+// bias); row (LDS) holds the gate logits z.  Lane l owns experts l + 64 q.
+// Largest key first; equal keys go to the lower expert index.  With
+// n_group > 1 only experts of the topk_group best groups compete: lane g
+// scores group g by the sum of its two largest keys, and the groups are
+// taken best first (ties to the lower group).  Lane j < k returns the j-th
+// choice and its gate (times scale).
+__device__ __forceinline__ void wave_topk_gates(const float* row, const float* key, int E, int k, int score,
+                                                int renorm, int n_group, int topk_group, float scale,
                                                 int& sel_e, float& sel_g) {
   const int lane = threadIdx.x & 63;
+  unsigned long long kept = ~0ull;  // groups whose experts compete
+  int gs = E;
+  if (n_group > 1) {
+    gs = E / n_group;
+    float gsc = -INFINITY;
+    if (lane < n_group) {
+      float t1 = -INFINITY, t2 = -INFINITY;
+      for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+        const float v = key[e];
+        if (v > t1) { t2 = t1; t1 = v; } else if (v > t2) { t2 = v; }
+      }
+      gsc = gs > 1 ? t1 + t2 : t1;
+    }
+    kept = 0ull;
+    for (int j = 0; j < topk_group; ++j) {
+      float bv = ((kept >> lane) & 1ull) || lane >= n_group ? -INFINITY : gsc;
+      int bi = lane < n_group && !((kept >> lane) & 1ull) ? lane : 0x7fffffff;
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (bi < 64) kept |= 1ull << bi;
+    }
+  }
+  // experts of groups not kept start out as taken
   uint32_t taken = 0;
+  if (n_group > 1)
+    for (int e = lane, q = 0; e < E; e += 64, ++q)
+      if (!((kept >> (e / gs)) & 1ull)) taken |= 1u << q;
   float sv = -INFINITY;
   sel_e = -1;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int e = lane, q = 0; e < E; e += 64, ++q) {
-      const float v = row[e];
+      const float v = key[e];
       if (!((taken >> q) & 1u) && (v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -186,9 +225,10 @@ __device__ __forceinline__ void wave_topk_gates(const float* row, int E, int k, 
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { sel_e = bi; sv = bv; }
+    if (lane == j) sel_e = bi;
   }
   const bool mine = lane < k;
+  if (mine) sv = row[sel_e];  // the chosen gate logit
   float g;
   if (score == MOE_SCORE_SOFTMAX) {
     const float m = __shfl(sv, 0);  // the largest logit
@@ -204,12 +244,13 @@ __device__ __forceinline__ void wave_topk_gates(const float* row, int E, int k, 
     const float sg = mine ? 1.0f / (1.0f + expf(-sv)) : 0.0f;
     g = renorm ? sg / wave_sum(sg) : sg;
   }
-  sel_g = g;
+  sel_g = g * scale;
 }
 
 constexpr int kTopkChunk = 8;   // tokens whose logits are staged in LDS at once
-// LDS of router_topk: block masks (kMaxE u64) + a chunk of logits
-constexpr size_t kTopkSmem = kMaxE * 8 + (size_t)kTopkChunk * kMaxE * 4;
+// LDS of router_topk: block masks (kMaxE u64) + a chunk of logits + one
+// row of score-space keys per wave
+constexpr size_t kTopkSmem = kMaxE * 8 + (size_t)kTopkChunk * kMaxE * 4 + 4 * (size_t)kMaxE * 4;
 
 // Sums the slices, adds the bias, selects, writes idx/gates and the block's
 // expert bitmasks.  The logits of 8 tokens at a time are summed into LDS by
@@ -220,6 +261,8 @@ template <bool MASKS>
 __device__ void router_topk(const Fwd& F, int b, char* smem) {
   unsigned long long* smask = (unsigned long long*)smem;
   float* sv = (float*)(smem + kMaxE * 8);
+  float* skey = sv + kTopkChunk * kMaxE + (threadIdx.x >> 6) * kMaxE;  // this wave's keys
+  const bool keyed = F.select_only || F.n_group > 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = F.E;
   if (MASKS)
@@ -234,7 +277,7 @@ __device__ void router_topk(const Fwd& F, int b, char* smem) {
       float v = 0.0f;
       for (int s = 0; s < F.S; ++s) v += F.lpart[((size_t)s * F.T + t) * E + e];
       if (F.logits) F.logits[(size_t)t * E + e] = v;
-      if (F.bias) v += F.bias[e];
+      if (F.bias && !F.select_only) v += F.bias[e];
       sv[p] = v;
     }
     __syncthreads();
@@ -243,7 +286,18 @@ __device__ void router_topk(const Fwd& F, int b, char* smem) {
       if (t >= F.T) break;
       int se;
       float sg;
-      wave_topk_gates(sv + tt * E, E, F.k, F.score, F.renorm, se, sg);
+      const float* row = sv + tt * E;
+      if (keyed) {
+        // score-space keys sigmoid(z) (+ the selection-only bias); the
+        // wave's own LDS row, written and read by this wave only
+        for (int e = lane; e < E; e += 64)
+          skey[e] = 1.0f / (1.0f + expf(-row[e])) + (F.select_only && F.bias ? F.bias[e] : 0.0f);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      wave_topk_gates(row, keyed ? skey : row, E, F.k, F.score, F.renorm, F.n_group, F.topk_group, F.scale,
+                      se, sg);
       if (lane < F.k) {
         F.topk[(size_t)t * F.k + lane] = se;
         F.gate[(size_t)t * F.k + lane] = sg;

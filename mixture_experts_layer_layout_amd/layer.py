@@ -14,9 +14,13 @@ _ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 def desc_for(w, fused=True, stage_rows=0, n_workgroups=0, flags=0, T=None):
     """moe_desc of a synth.Workload."""
+    if w.select_only:
+        flags |= api.MOE_FLAG_BIAS_SELECT_ONLY
     return api.make_desc(w.T if T is None else T, w.d, w.E, w.k, w.I, act=w.act,
                          experts=w.experts, score=w.score, renorm=w.renorm, fused=fused,
-                         stage_rows=stage_rows, n_workgroups=n_workgroups, flags=flags)
+                         stage_rows=stage_rows, n_workgroups=n_workgroups, flags=flags,
+                         n_group=w.n_group, topk_group=w.topk_group,
+                         routed_scale=0.0 if w.routed_scale == 1.0 else w.routed_scale)
 
 
 def workspace(desc, device="cuda"):

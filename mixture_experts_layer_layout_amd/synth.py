@@ -52,6 +52,12 @@ class Workload:
     w2_std: float | None = None
     zipf_s: float | None = None
     backward: bool = False
+    # DeepSeek-V3-style routing options (see moe_desc): selection-only
+    # bias, group-limited selection, routed scaling factor
+    select_only: bool = False
+    n_group: int = 0
+    topk_group: int = 0
+    routed_scale: float = 1.0
 
     @property
     def R(self):

@@ -49,12 +49,16 @@ def test_library_exports_every_declared_symbol(lib):
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "E", "k", "I", "act_dtype", "expert_dtype",
                                               "score", "renorm", "fused", "stage_rows",
-                                              "n_workgroups")] + [("flags", ctypes.c_uint32)]
+                                              "n_workgroups")] + [("flags", ctypes.c_uint32),
+                                                                  ("n_group", ctypes.c_int32),
+                                                                  ("topk_group", ctypes.c_int32),
+                                                                  ("routed_scale", ctypes.c_float)]
 
 
 def _desc(**kw):
     base = dict(T=4096, d=7168, E=256, k=8, I=2048, act_dtype=1, expert_dtype=1, score=1, renorm=1,
-                fused=1, stage_rows=0, n_workgroups=0, flags=0)
+                fused=1, stage_rows=0, n_workgroups=0, flags=0, n_group=0, topk_group=0,
+                routed_scale=0.0)
     base.update(kw)
     return Desc(**base)
 
@@ -109,6 +113,21 @@ def test_router_backward_rejects_bad_arguments_before_launching(lib):
     d = _desc(T=64, d=256, E=8, k=2, I=128)
     assert lib.moe_router_backward(ctypes.byref(d), None, None, None, None, None, None, None, None,
                                    None, None, 0, None) == -1
+
+
+def test_routing_options_are_validated(lib):
+    lib.moe_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+    n = ctypes.c_size_t(0)
+    ok = lambda **kw: lib.moe_workspace_size(ctypes.byref(_desc(**kw)), ctypes.byref(n))
+    assert ok(n_group=8, topk_group=4, flags=0x10, routed_scale=2.5) == 0
+    assert ok(n_group=8, topk_group=4, score=0) == -2          # grouped needs sigmoid
+    assert ok(flags=0x10, score=0) == -2                        # so does a selection-only bias
+    assert ok(n_group=7, topk_group=4) == -1                    # E % n_group
+    assert ok(n_group=8, topk_group=9) == -1
+    assert ok(n_group=128, topk_group=4) == -1                  # at most 64 groups
+    assert ok(n_group=64, topk_group=1, k=8) == -1              # k > kept experts (4)
+    assert ok(routed_scale=-1.0) == -1
+    assert ok(routed_scale=float("nan")) == -1
 
 
 def test_status_strings(lib):
