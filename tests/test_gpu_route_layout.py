@@ -136,3 +136,36 @@ def test_host_validation_errors():
     with pytest.raises(api.MoeError) as e:
         api.moe_route(d, None, None, None, None)
     assert e.value.code == api.MOE_ERR_INVALID_ARG
+
+
+def test_route_layout_at_the_maximum_expert_count_and_k():
+    """E = 1024 experts and k = 16 (the library's limits): routing and layout
+    bit-exact against the oracle."""
+    T, E, k = 300, 1024, 16
+    lg = synth.random_logits(T, E, 21, ties=True)
+    d = api.make_desc(T, 256, E, k, 128)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    api.moe_route(d, lg.cuda(), None, idx, gate)
+    ws = torch.empty(api.moe_workspace_size(d), dtype=torch.uint8, device="cuda")
+    bufs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.moe_layout(d, idx, *bufs, st, ws)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    want_idx, want_g = M.route(lg.numpy(), k, "sigmoid", True)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    assert np.max(np.abs(gate.cpu().numpy() - want_g)) < 2e-6
+    counts, offsets, perm, inv, _ = M.layout(want_idx, E)
+    for got, want in zip(bufs, (counts, offsets, perm, inv)):
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_gather_push_of_an_empty_batch_is_a_no_op():
+    desc = api.make_desc(0, 256, 8, 2, 128)
+    xp = torch.full((4, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    inv = torch.empty((0,), dtype=torch.int32, device="cuda")
+    api.moe_gather(desc, x, None, xp, inv=inv)
+    torch.cuda.synchronize()
+    assert torch.all(xp == 3.0)

@@ -137,3 +137,45 @@ def test_layer_gradients_end_to_end_bf16():
     for n in ("dwr", "dbias", "dlogits"):
         err = _tensor_rel(host(r[n]), o[n])
         assert err <= 2e-2, f"{n}: {err:.3e}"
+
+
+def test_router_backward_of_an_empty_batch_zeroes_dwr():
+    w = CASES["dsv3-zipf-small"].shrink(T=0)
+    inp = synth.make_inputs(w, 7)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    _, sv = layer.forward(w, dev)
+    dx = torch.empty((0, w.d), dtype=torch.bfloat16, device="cuda")
+    dgate = torch.empty((0, w.k), dtype=torch.float32, device="cuda")
+    r = layer.router_backward(w, dev, sv, dgate, dx)
+    torch.cuda.synchronize()
+    assert torch.all(r["dwr"] == 0) and torch.all(r["dbias"] == 0)
+
+
+def test_layer_and_router_gradients_at_the_maximum_expert_count():
+    """E = 1024, k = 16, 64 groups of 16 with 8 kept and a selection-only
+    bias: forward, backward and router backward against the oracle."""
+    w = synth.WORKLOADS["dsv3-bf16"].shrink(T=257, d=256, E=1024, k=16, I=128, backward=True,
+                                            select_only=True, n_group=64, topk_group=8, routed_scale=2.5)
+    inp = synth.make_inputs(w, 8, with_dy=True)
+    inp["bias"] = torch.from_numpy((np.random.default_rng(8).standard_normal(w.E) * 0.05).astype(np.float32))
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    y, sv = layer.forward(w, dev)
+    g = layer.backward(w, dev, sv)
+    r = layer.router_backward(w, dev, sv, g["dgate"], g["dx"])
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    h = {k: (host(v) if v is not None else None) for k, v in inp.items()}
+    logits = host(sv["logits"])
+    opts = dict(select_only=True, n_group=64, topk_group=8, routed_scale=2.5)
+    f = M.forward(h["x"], h["wr"], h["bias"], h["w1"], h["w3"], h["w2"], w.k, w.score, w.renorm,
+                  logits=logits, **opts)
+    same = np.all(host(sv["topk_idx"]) == f["topk_idx"], axis=1)
+    assert (~same).sum() <= 3, f"{(~same).sum()} tokens routed differently (near ties)"
+    assert row_rel_err(host(y)[same], f["y"][same]) <= 2e-2
+    if same.all():
+        b = M.backward(h["dy"], f, h["w1"], h["w3"], h["w2"], w.k)
+        o = M.router_backward(h["x"], h["wr"], logits, f["topk_idx"], b["dgate"], w.score, w.renorm,
+                              2.5, True)
+        assert row_rel_err(host(g["dx"]), b["dx"] + o["dx"]) <= 2e-2
+        assert _tensor_rel(host(r["dwr"]), o["dwr"]) <= 2e-2
+        assert np.all(host(r["dbias"]) == 0.0)
