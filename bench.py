@@ -186,6 +186,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0, help="override the workload's T")
+    ap.add_argument("--macro-tokens", type=int, default=0,
+                    help="forward in macrobatches of this many tokens (forward-only workloads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -196,11 +199,19 @@ def main():
         copy_calibration()
         return
 
+    import numpy as np
     import torch
     from mixture_experts_layer_layout_amd import api, layer, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import dataclasses
     w = synth.WORKLOADS[args.workload]
+    if args.tokens:
+        w = dataclasses.replace(w, T=args.tokens)
+    if args.macro_tokens:
+        if w.backward:
+            sys.exit("--macro-tokens: macrobatches are a forward-only mode")
+        w = dataclasses.replace(w, macro_tokens=args.macro_tokens)
     t_gen = time.perf_counter()
     # x, router and bias on the host (shared with the CPU baseline), expert
     # weights and dY drawn on the device
@@ -270,7 +281,7 @@ def main():
     # by inv, and the pull by perm) on this step's routing, timed with events
     # on the same stream
     side = {}
-    if w.experts != "f32":
+    if w.experts != "f32" and "perm" in saved:
         gdesc = layer.desc_for(w, fused=False)
         xq_ = torch.empty((w.R, w.d), dtype=torch.uint8 if w.experts == "mxfp8" else torch.bfloat16,
                           device="cuda")
@@ -318,7 +329,10 @@ def main():
     fwd_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / args.steps
     bwd_ms = sum(b.elapsed_time(c) for _, b, c in marks) / args.steps if w.backward else 0.0
     ms_step = elapsed * 1e3 / args.steps
-    counts = saved["counts"].cpu().numpy()
+    counts = saved["counts"].cpu().numpy() if "counts" in saved else None
+    if counts is None:
+        # macrobatches: the per-expert loads from the saved routing
+        counts = np.bincount(saved["topk_idx"].cpu().numpy().reshape(-1), minlength=w.E)
 
     part = "backward" if w.backward else "forward"
     kern_ms = bwd_ms if w.backward else fwd_ms
@@ -334,7 +348,9 @@ def main():
                                          / MFMA_PEAK_TFS[w.experts], 4),
               "forward_hbm_frac": round(algorithmic_bytes(w, counts, "forward") / (fwd_ms * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
-              "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())}
+              "workspace_mb": round(ws.numel() / 1e6, 1)}
+    phases["max_rows_per_expert"] = int(counts.max())
+    phases["min_rows_per_expert"] = int(counts.min())
     if side:
         # gather: X read once, the routed rows written (MXFP8: codes + scales)
         gbytes = w.T * w.d * 2 + (w.R * w.d * (1 + 1 / 32) if w.experts == "mxfp8" else w.R * w.d * 2)
@@ -356,7 +372,8 @@ def main():
             "data": "synthetic (seeded; random-init expert weights)",
             "config": {"workload": w.name + (" fwd+bwd" if w.backward else " fwd"), "T": w.T, "d": w.d,
                        "E": w.E, "k": w.k, "I": w.I, "score": w.score, "fused": fused,
-                       "stage_rows": args.stage_rows, "flags": args.flags},
+                       "stage_rows": args.stage_rows, "flags": args.flags,
+                       "macro_tokens": args.macro_tokens},
             "roofline": roof, "cpu_baseline": cpu, "phases": phases,
             "input_gen_s": round(t_gen, 1), "source_sha256": source_digest()}
     print(json.dumps(line), flush=True)

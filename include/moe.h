@@ -105,6 +105,16 @@ typedef struct moe_desc {
   int32_t n_group;
   int32_t topk_group;
   float routed_scale;
+  /* macro_tokens > 0 (and < T): moe_forward walks the tokens in macrobatches
+   * of this many tokens (the last one ragged), every macrobatch reusing one
+   * workspace sized for a macrobatch (moe_workspace_size returns that size):
+   * the staging rows are a fixed pool reused batch after batch, so memory
+   * stays bounded for any T.  Outputs are identical to one call over all T.
+   * The saved layout (counts, offsets, perm, inv) and activations (a, b, h)
+   * describe one layout over all T and must be NULL; logits, topk_idx, gate
+   * and status are written.  The other calls return MOE_ERR_UNSUPPORTED
+   * for such a descriptor. */
+  int32_t macro_tokens;
 } moe_desc;
 
 /* Flags. */

@@ -46,7 +46,7 @@ class MoeDesc(ctypes.Structure):
                 ("score", c_int32), ("renorm", c_int32), ("fused", c_int32),
                 ("stage_rows", c_int32), ("n_workgroups", c_int32),
                 ("flags", ctypes.c_uint32), ("n_group", c_int32), ("topk_group", c_int32),
-                ("routed_scale", ctypes.c_float)]
+                ("routed_scale", ctypes.c_float), ("macro_tokens", c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -115,10 +115,10 @@ def _stream(stream):
 
 def make_desc(T, d, E, k, I, act="bf16", experts="bf16", score="sigmoid", renorm=True,
               fused=True, stage_rows=0, n_workgroups=0, flags=0, n_group=0, topk_group=0,
-              routed_scale=0.0) -> MoeDesc:
+              routed_scale=0.0, macro_tokens=0) -> MoeDesc:
     return MoeDesc(T, d, E, k, I, _DT[act], _DT[experts], _SC[score], int(bool(renorm)),
                    int(bool(fused)), stage_rows, n_workgroups, flags, n_group, topk_group,
-                   routed_scale)
+                   routed_scale, macro_tokens)
 
 
 def moe_workspace_size(desc: MoeDesc) -> int:

@@ -27,8 +27,11 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int make_plan(const moe_desc* D, Plan* p) {
   if (!D || !p) return MOE_ERR_INVALID_ARG;
   memset(p, 0, sizeof(*p));
-  const int T = D->T, d = D->d, E = D->E, k = D->k, I = D->I;
-  if (T < 0 || d <= 0 || E <= 0 || k <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (D->T < 0 || D->macro_tokens < 0) return MOE_ERR_INVALID_ARG;
+  const bool macro = D->macro_tokens > 0 && D->macro_tokens < D->T;
+  // with macrobatches every size below is that of one macrobatch
+  const int T = macro ? D->macro_tokens : D->T, d = D->d, E = D->E, k = D->k, I = D->I;
+  if (d <= 0 || E <= 0 || k <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
   if (E > kMaxE || k > kMaxK || k > E) return MOE_ERR_INVALID_ARG;
   if ((int64_t)T * k > (int64_t)1 << 30) return MOE_ERR_INVALID_ARG;
   if (D->score != MOE_SCORE_SOFTMAX && D->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
@@ -52,6 +55,8 @@ int make_plan(const moe_desc* D, Plan* p) {
   if (((D->flags & MOE_FLAG_BIAS_SELECT_ONLY) || D->n_group > 1) && D->score != MOE_SCORE_SIGMOID)
     return MOE_ERR_UNSUPPORTED;
   p->T = T; p->d = d; p->E = E; p->k = k; p->I = I; p->R = T * k;
+  p->macro = macro;
+  p->T_full = D->T;
   p->f32 = f32;
   p->mxfp8 = D->expert_dtype == MOE_MXFP8;
   p->act_es = f32 ? 4 : 2;
@@ -742,6 +747,7 @@ int moe_route(const moe_desc* desc, const float* logits, const float* bias, int3
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
+  if (p.macro) return MOE_ERR_UNSUPPORTED;
   if (p.T > 0 && (!logits || !topk_idx || !gate)) return MOE_ERR_INVALID_ARG;
   if (p.T == 0) return MOE_OK;
   Fwd F;
@@ -763,6 +769,7 @@ int moe_layout(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts, i
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
+  if (p.macro) return MOE_ERR_UNSUPPORTED;
   if (!counts || !offsets || (p.R > 0 && (!topk_idx || !perm || !inv))) return MOE_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   moe_saved sv;
@@ -792,6 +799,7 @@ int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm, const i
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
+  if (p.macro) return MOE_ERR_UNSUPPORTED;
   if (p.R == 0) return MOE_OK;
   if (!x || (!perm && !inv) || !xp) return MOE_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
@@ -827,20 +835,10 @@ int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* codes,
   return mxfp8_quantize_rows((const bf16_t*)src, rows, K, codes, scales, (hipStream_t)stream);
 }
 
-int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float* bias, const moe_weights* w,
-                void* y, const moe_saved* saved, void* workspace, size_t workspace_bytes, void* stream) {
-  Plan p;
-  int rc = make_plan(desc, &p);
-  if (rc != MOE_OK) return rc;
-  if (!w || (p.T > 0 && (!x || !wr || !y || !w->w1 || !w->w3 || !w->w2))) return MOE_ERR_INVALID_ARG;
-  if (p.mxfp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
-  if (p.f32 && saved && (saved->a || saved->b)) {
-    // fp32 layer: a/b are written as fp32 (act dtype)
-  }
+static int forward_call(const Plan& p, const moe_desc* desc, const void* x, const void* wr, const float* bias,
+                        const moe_weights* w, void* y, const moe_saved* saved, void* workspace, hipStream_t st) {
   Fwd F = make_fwd(p, desc, workspace, saved);
   F.x = x; F.wr = wr; F.bias = bias; F.w1 = w->w1; F.w3 = w->w3; F.w2 = w->w2; F.y = y;
-  hipStream_t st = (hipStream_t)stream;
   if (p.mxfp8) {
     F.w1s = w->w1_scale; F.w3s = w->w3_scale; F.w2s = w->w2_scale;
     return forward_impl<bf16_t, TileMX128>(p, desc, F, st);
@@ -850,12 +848,50 @@ int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float
   return forward_impl<bf16_t, TileD256>(p, desc, F, st);
 }
 
+int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float* bias, const moe_weights* w,
+                void* y, const moe_saved* saved, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p);
+  if (rc != MOE_OK) return rc;
+  if (!w || (p.T > 0 && (!x || !wr || !y || !w->w1 || !w->w3 || !w->w2))) return MOE_ERR_INVALID_ARG;
+  if (p.mxfp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (!p.macro) return forward_call(p, desc, x, wr, bias, w, y, saved, workspace, st);
+  // Macrobatches: the same call over consecutive token ranges, reusing the
+  // workspace (stream order keeps each macrobatch after the previous one).
+  if (saved && (saved->counts || saved->offsets || saved->perm || saved->inv || saved->a || saved->b || saved->h))
+    return MOE_ERR_INVALID_ARG;
+  const size_t es = p.act_es;
+  for (int t0 = 0; t0 < p.T_full; t0 += p.T) {
+    moe_desc md = *desc;
+    md.T = p.T_full - t0 < p.T ? p.T_full - t0 : p.T;
+    md.macro_tokens = 0;
+    Plan pm;
+    rc = make_plan(&md, &pm);
+    if (rc != MOE_OK) return rc;
+    moe_saved sm;
+    memset(&sm, 0, sizeof(sm));
+    if (saved) {
+      sm.logits = saved->logits ? saved->logits + (size_t)t0 * p.E : nullptr;
+      sm.topk_idx = saved->topk_idx ? saved->topk_idx + (size_t)t0 * p.k : nullptr;
+      sm.gate = saved->gate ? saved->gate + (size_t)t0 * p.k : nullptr;
+      sm.status = saved->status;
+    }
+    rc = forward_call(pm, &md, (const char*)x + (size_t)t0 * p.d * es, wr, bias, w,
+                      (char*)y + (size_t)t0 * p.d * es, saved ? &sm : nullptr, workspace, st);
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
+}
+
 int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_weights* w, const moe_saved* saved,
                  void* dx, void* dw1, void* dw3, void* dw2, float* dgate, void* workspace, size_t workspace_bytes,
                  void* stream) {
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
+  if (p.macro) return MOE_ERR_UNSUPPORTED;
   if (!p.bwd_ok) return MOE_ERR_UNSUPPORTED;
   if (!w || !saved) return MOE_ERR_INVALID_ARG;
   if (!saved->offsets || !dw1 || !dw3 || !dw2 || !w->w1 || !w->w3 || !w->w2) return MOE_ERR_INVALID_ARG;
@@ -872,6 +908,7 @@ int moe_router_backward(const moe_desc* desc, const void* x, const void* wr, con
   Plan p;
   int rc = make_plan(desc, &p);
   if (rc != MOE_OK) return rc;
+  if (p.macro) return MOE_ERR_UNSUPPORTED;
   if (desc->score == MOE_SCORE_SOFTMAX && !desc->renorm) return MOE_ERR_UNSUPPORTED;
   if (!saved || !wr || !dwr || !saved->offsets) return MOE_ERR_INVALID_ARG;
   if (p.T > 0 && (!x || !dx || !dgate || !saved->logits || !saved->topk_idx || !saved->gate || !saved->perm))

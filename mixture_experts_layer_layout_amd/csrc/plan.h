@@ -10,7 +10,9 @@
 namespace moe {
 
 struct Plan {
-  int T, d, E, k, I, R;
+  int T, d, E, k, I, R;  // T: tokens of one call (of one macrobatch when macro)
+  bool macro;      // moe_forward runs macrobatches of T tokens over T_full
+  int T_full;
   int nb;          // token blocks of 64
   int S;           // router k-slices
   int BM;          // rows per row tile (= rows per ready counter)

@@ -20,7 +20,8 @@ def desc_for(w, fused=True, stage_rows=0, n_workgroups=0, flags=0, T=None):
                          experts=w.experts, score=w.score, renorm=w.renorm, fused=fused,
                          stage_rows=stage_rows, n_workgroups=n_workgroups, flags=flags,
                          n_group=w.n_group, topk_group=w.topk_group,
-                         routed_scale=0.0 if w.routed_scale == 1.0 else w.routed_scale)
+                         routed_scale=0.0 if w.routed_scale == 1.0 else w.routed_scale,
+                         macro_tokens=w.macro_tokens)
 
 
 def workspace(desc, device="cuda"):
@@ -64,6 +65,11 @@ def alloc_saved(w, device="cuda", full=True, T=None):
         inv=torch.empty((R,), **i32),
         status=torch.zeros((1,), **i32),
     )
+    if w.macro_tokens and w.macro_tokens < T:
+        # macrobatches: per-token outputs only (no layout over all T)
+        for n in ("counts", "offsets", "perm", "inv"):
+            del out[n]
+        return out
     if full:
         act = _ACT[w.act]
         for n in ("a", "b", "h"):

@@ -58,6 +58,8 @@ class Workload:
     n_group: int = 0
     topk_group: int = 0
     routed_scale: float = 1.0
+    # forward in macrobatches of this many tokens (0: one call over all T)
+    macro_tokens: int = 0
 
     @property
     def R(self):

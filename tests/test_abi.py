@@ -52,13 +52,14 @@ class Desc(ctypes.Structure):
                                               "n_workgroups")] + [("flags", ctypes.c_uint32),
                                                                   ("n_group", ctypes.c_int32),
                                                                   ("topk_group", ctypes.c_int32),
-                                                                  ("routed_scale", ctypes.c_float)]
+                                                                  ("routed_scale", ctypes.c_float),
+                                                                  ("macro_tokens", ctypes.c_int32)]
 
 
 def _desc(**kw):
     base = dict(T=4096, d=7168, E=256, k=8, I=2048, act_dtype=1, expert_dtype=1, score=1, renorm=1,
                 fused=1, stage_rows=0, n_workgroups=0, flags=0, n_group=0, topk_group=0,
-                routed_scale=0.0)
+                routed_scale=0.0, macro_tokens=0)
     base.update(kw)
     return Desc(**base)
 
@@ -128,6 +129,21 @@ def test_routing_options_are_validated(lib):
     assert ok(n_group=64, topk_group=1, k=8) == -1              # k > kept experts (4)
     assert ok(routed_scale=-1.0) == -1
     assert ok(routed_scale=float("nan")) == -1
+
+
+def test_macrobatches_bound_the_workspace_and_other_calls_refuse_them(lib):
+    lib.moe_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+    full, part = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(_desc(T=65536)), ctypes.byref(full)) == 0
+    assert lib.moe_workspace_size(ctypes.byref(_desc(T=65536, macro_tokens=4096)), ctypes.byref(part)) == 0
+    assert part.value * 8 < full.value * 1.01  # about a sixteenth, plus the per-expert parts
+    assert lib.moe_workspace_size(ctypes.byref(_desc(macro_tokens=-1)), ctypes.byref(part)) == -1
+    vp = ctypes.c_void_p
+    lib.moe_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    m = _desc(T=8192, macro_tokens=4096)
+    assert lib.moe_backward(ctypes.byref(m), None, None, None, None, None, None, None, None, None, None,
+                            0, None) == -2
 
 
 def test_status_strings(lib):

@@ -123,3 +123,31 @@ def test_forward_persistent_variants_equal_unfused(flags):
     assert torch.equal(y1, y2)
     for n in ("topk_idx", "counts", "offsets", "perm", "inv", "h", "a", "b"):
         assert torch.equal(s1[n], s2[n]), n
+
+
+MACRO = {
+    "dsv3-zipf-bf16": (synth.WORKLOADS["dsv3-fwdbwd-zipf"].shrink(T=300, d=512, E=64, I=256, backward=False), 96),
+    "mixtral-bf16": (synth.WORKLOADS["mixtral-bf16"].shrink(T=300, d=512, I=512), 128),
+    "dsv3-mxfp8": (synth.WORKLOADS["dsv3-mxfp8"].shrink(T=200, d=512, E=16, k=4, I=256), 64),
+    "tiny-fp32": (synth.WORKLOADS["tiny-fp32"], 24),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MACRO))
+def test_macrobatched_forward_equals_one_call(name):
+    """moe_forward in macrobatches (the last one ragged) writes the same bits
+    as one call over all tokens, from a workspace sized for a macrobatch."""
+    import dataclasses
+    w, tm = MACRO[name]
+    wm = dataclasses.replace(w, macro_tokens=tm)
+    inp = synth.make_inputs(w, 5)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    y0, s0 = layer.forward(w, dev)
+    y1, s1 = layer.forward(wm, dev)
+    torch.cuda.synchronize()
+    assert s0["status"].item() == 0 and s1["status"].item() == 0
+    assert "perm" not in s1
+    for n in ("logits", "topk_idx", "gate"):
+        assert torch.equal(s0[n], s1[n]), n
+    assert torch.equal(y0, y1)
+    assert api.moe_workspace_size(layer.desc_for(wm)) < api.moe_workspace_size(layer.desc_for(w))
