@@ -99,9 +99,9 @@ struct KRows {
 };
 
 // k is the row index of the stored operand; the tile's ROWS rows are
-// contiguous within each stored row.  Thread t covers k-group t % KG (KK
-// consecutive k) and tile rows 8*(t/KG) .. +7, with KK = 8 for 256-row
-// tiles and 4 for 128-row tiles, so all 256 threads take part.
+// contiguous within each stored row.  Each thread covers one k-group (KK
+// consecutive k) and 8 tile rows (kgroup(), cblock()), with KK = 8 for
+// 256-row tiles and 4 for 128-row tiles, so all 256 threads take part.
 //   kptr(k, c) pointer to the stored row holding k, at the tile's first
 //             row; never null (k past the operand -> a zero row).  c is the
 //             column tile of a stream (tile_stream), 0 otherwise
@@ -124,8 +124,23 @@ struct KCols {
   const bf16_t* p[KK];
   float s[KK], sl[NBUF][KK];
   uint4 v[NBUF][KK];
+  // thread -> (k-group, 8-column block), so that every load instruction of
+  // a wave reads whole 128-byte lines: 8 k-rows x 8 column blocks.  With
+  // KG = 16 (128-row tiles) wave w takes k-groups 8 (w >> 1) .. +7 and
+  // column blocks 8 (w & 1) .. +7 (the split t % KG, t / KG read 16 k-rows x
+  // 64 bytes a wave, half lines: the backward took 17.25 ms against 16.16
+  // ms at the DeepSeek-V3 Zipf shape); with KG = 8 that split already
+  // reads 8 k-rows x 128 bytes.
+  __device__ static __forceinline__ int kgroup() {
+    if (KG == 16) return 8 * (threadIdx.x >> 7) + ((threadIdx.x & 63) >> 3);
+    return threadIdx.x % KG;
+  }
+  __device__ static __forceinline__ int cblock() {
+    if (KG == 16) return 8 * ((threadIdx.x >> 6) & 1) + (threadIdx.x & 7);
+    return threadIdx.x / KG;
+  }
   __device__ __forceinline__ KCols(P kp, S ks, int half_off) : kptr(kp), kscale(ks) {
-    const int nb = threadIdx.x / KG;
+    const int nb = cblock();
     coff = nb * 8 + (nb >= ROWS / 16 ? half_off : 0);
   }
   __device__ __forceinline__ void prep(int kt) {
@@ -143,7 +158,7 @@ struct KCols {
     }
     pj_ = kt;
     const int c = pc_;
-    const int k0 = ps_ * 64 + (threadIdx.x % KG) * KK;
+    const int k0 = ps_ * 64 + kgroup() * KK;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       p[kk] = kptr(k0 + kk, c);
@@ -169,7 +184,7 @@ struct KCols {
           w[kk * 4 + q] = pack_bf16x2(bf16_to_f32((bf16_t)(w[kk * 4 + q] & 0xffff)) * sl[BUF][kk],
                                       bf16_to_f32((bf16_t)(w[kk * 4 + q] >> 16)) * sl[BUF][kk]);
     }
-    const int kg = threadIdx.x % KG, nb = threadIdx.x / KG;
+    const int kg = kgroup(), nb = cblock();
     // lanes of odd nb walk their 8 rows in the order 1,0,3,2,...: the two
     // lane groups written together then target rows of opposite parity,
     // i.e. opposite halves of the 256-byte bank row
