@@ -51,25 +51,41 @@ struct TileMX {
 // KRows, one 16-byte chunk of 16 codes per lane and row, plus the stage's
 // scale word of row t of [A rows | B rows] for thread t (scale rows are
 // [rows, K/32] bytes, 4-byte aligned).  Operand B's codes use KRows as is.
+//
+// A stage needs one scale word from each of 256 rows, 256 different lines.
+// With wide rows (a multiple of 4 words, 16-byte aligned: K % 512 == 0)
+// each thread reads its row's words of 4 consecutive stages at once, every
+// fourth stage, so a scale line is touched a quarter as often and the
+// expert weights streaming through the L2 between stages evict it less.
+// The loads come in stage order from 0 (the main loop's order).
 template <int ROWS, int BROWS>
 struct KRowsMX {
   static_assert(ROWS + BROWS == kThreads, "one scale row per thread");
   KRows<ROWS> codes;
   const uint32_t* srow;
   uint32_t sv[kPrefetch];
+  uint4 s4;   // words of stages 4g .. 4g+3 (wide rows)
+  bool wide;
   // rowptr(r): first code byte of A row r; ascale(r), bscale(r): first
   // scale byte of A row r / B row r.  All must be readable for every row.
   template <class F, class GA, class GB>
-  __device__ __forceinline__ void init(F rowptr, GA ascale, GB bscale) {
+  __device__ __forceinline__ void init(F rowptr, GA ascale, GB bscale, bool wide_rows) {
     codes.init([&](int r) { return (const bf16_t*)rowptr(r); });
     const int t = threadIdx.x;
     srow = t < ROWS ? (const uint32_t*)ascale(t) : (const uint32_t*)bscale(t - ROWS);
+    wide = wide_rows;
   }
   __device__ __forceinline__ void prep(int) {}
   template <int BUF>
   __device__ __forceinline__ void load(int kt) {
     codes.template load<BUF>(kt);
-    sv[BUF] = srow[kt];
+    if (wide) {
+      const int q = kt & 3;
+      if (q == 0) s4 = *(const uint4*)(srow + kt);
+      sv[BUF] = q == 0 ? s4.x : q == 1 ? s4.y : q == 2 ? s4.z : s4.w;
+    } else {
+      sv[BUF] = srow[kt];
+    }
   }
   template <int BUF>
   __device__ __forceinline__ void store(bf16_t* lds) const {

@@ -841,6 +841,9 @@ static int forward_call(const Plan& p, const moe_desc* desc, const void* x, cons
   F.x = x; F.wr = wr; F.bias = bias; F.w1 = w->w1; F.w3 = w->w3; F.w2 = w->w2; F.y = y;
   if (p.mxfp8) {
     F.w1s = w->w1_scale; F.w3s = w->w3_scale; F.w2s = w->w2_scale;
+    auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    F.mx_wide1 = p.d % 512 == 0 && al16(F.xs) && al16(F.w1s) && al16(F.w3s);
+    F.mx_wide2 = p.I % 512 == 0 && al16(F.hs) && al16(F.w2s);
     return forward_impl<bf16_t, TileMX128>(p, desc, F, st);
   }
   if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st);

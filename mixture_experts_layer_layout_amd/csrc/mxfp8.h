@@ -56,7 +56,7 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   // rows past the tile's n repeat its last row (their outputs are dropped)
   la.init([&](int r) { return F.xq + (size_t)F.src[r0 + min(r, n - 1)] * d; },
           [&](int r) { return F.xs + (size_t)F.src[r0 + min(r, n - 1)] * ds; },
-          [&](int nr) { return wrow(nr, true); });
+          [&](int nr) { return wrow(nr, true); }, F.mx_wide1 != 0);
   lb.init([&](int nr) { return (const bf16_t*)wrow(nr, false); });
   f32x16_t acc[TL::MI][TL::NJ];
   tile_mainloop<TL>(d / 128, smem, acc, la, lb);
@@ -124,7 +124,7 @@ __device__ void g2_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   KRows<TL::BN> lb;
   la.init([&](int r) { return F.hq + (size_t)(r0 + min(r, n - 1)) * I; },
           [&](int r) { return F.hs + (size_t)(r0 + min(r, n - 1)) * is; },
-          [&](int nr) { return S2 + (size_t)(c0 + nr) * is; });
+          [&](int nr) { return S2 + (size_t)(c0 + nr) * is; }, F.mx_wide2 != 0);
   lb.init([&](int nr) { return (const bf16_t*)(W2 + (size_t)(c0 + nr) * I); });
   f32x16_t acc[TL::MI][TL::NJ];
   tile_mainloop<TL>(I / 128, smem, acc, la, lb);

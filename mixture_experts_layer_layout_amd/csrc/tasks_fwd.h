@@ -105,6 +105,9 @@ struct Fwd {
   uint8_t* xs;         // [T, d/32]
   uint8_t* hq;         // [R, I]
   uint8_t* hs;         // [R, I/32]
+  // scale rows of the up / down projection read 16 bytes every 4 stages
+  // (K % 512 == 0 and 16-byte aligned scale arrays)
+  int mx_wide1, mx_wide2;
   Sync s;
 };
 
