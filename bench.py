@@ -183,6 +183,7 @@ def main():
     ap.add_argument("--unfused", action="store_true", help="one launch per step instead of the persistent kernel")
     ap.add_argument("--stage-rows", type=int, default=0)
     ap.add_argument("--flags", type=lambda v: int(v, 0), default=0, help="moe_desc.flags (MOE_FLAG_*)")
+    ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: occupancy limit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -229,11 +230,12 @@ def main():
     fused = not args.unfused
     weights, keep = layer.weights_of(w, dev)
     saved = layer.alloc_saved(w, "cuda", full=w.backward)
-    desc = layer.desc_for(w, fused=fused, stage_rows=args.stage_rows, flags=args.flags)
+    desc = layer.desc_for(w, fused=fused, stage_rows=args.stage_rows, flags=args.flags,
+                          n_workgroups=args.workgroups)
     ws = layer.workspace(desc)
     y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if w.act == "bf16" else torch.float32, device="cuda")
     if w.backward:
-        bdesc = layer.desc_for(w, fused=fused, flags=args.flags)
+        bdesc = layer.desc_for(w, fused=fused, flags=args.flags, n_workgroups=args.workgroups)
         bws = layer.workspace(bdesc)
         act = y.dtype
         grads = dict(dx=torch.empty((w.T, w.d), dtype=act, device="cuda"),
@@ -372,7 +374,7 @@ def main():
             "data": "synthetic (seeded; random-init expert weights)",
             "config": {"workload": w.name + (" fwd+bwd" if w.backward else " fwd"), "T": w.T, "d": w.d,
                        "E": w.E, "k": w.k, "I": w.I, "score": w.score, "fused": fused,
-                       "stage_rows": args.stage_rows, "flags": args.flags,
+                       "stage_rows": args.stage_rows, "flags": args.flags, "workgroups": args.workgroups,
                        "macro_tokens": args.macro_tokens},
             "roofline": roof, "cpu_baseline": cpu, "phases": phases,
             "input_gen_s": round(t_gen, 1), "source_sha256": source_digest()}
