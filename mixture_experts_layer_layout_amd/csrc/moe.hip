@@ -97,7 +97,6 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_topk = take(R * 4);
   p->o_gate = take(R * 4);
   p->o_bmask = take((size_t)p->nb * E * 8);
-  p->o_bcnt = take((size_t)p->nb * E * 4);
   p->o_bbase = take((size_t)p->nb * E * 4);
   p->o_counts = take((size_t)E * 4);
   p->o_offsets = take((size_t)(E + 1) * 4);
@@ -178,7 +177,6 @@ static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved*
   F.topk = (sv && sv->topk_idx) ? sv->topk_idx : at<int>(ws, p.o_topk);
   F.gate = (sv && sv->gate) ? sv->gate : at<float>(ws, p.o_gate);
   F.bmask = at<unsigned long long>(ws, p.o_bmask);
-  F.bcnt = at<int>(ws, p.o_bcnt);
   F.bbase = at<int>(ws, p.o_bbase);
   F.counts = (sv && sv->counts) ? sv->counts : at<int>(ws, p.o_counts);
   F.offsets = (sv && sv->offsets) ? sv->offsets : at<int>(ws, p.o_offsets);
@@ -327,7 +325,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         groups = 0;
         if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
         if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0); return true; }
-        if (ph == 1) { groups = F.nb; return true; }
+        if (ph == 1) { groups = F.nb * kTopkChunks; return true; }
         if (ph == 2) { groups = 1; return true; }
         if (c.nmt < 0) {
           if (!thread_wait_geq(F.s.scan_done, 1, W)) return false;
@@ -356,10 +354,10 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         signal_add<(MASK & 2u) != 0>(&F.s.r1_cnt[t / F.S], 1);
       }
     } else if ((MASK & 2u) && ph == 1) {
-      if (wait_geq(&F.s.r1_cnt[t], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
+      if (wait_geq(&F.s.r1_cnt[t / kTopkChunks], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
       signal_add<(MASK & 0x4Cu) != 0>(F.s.r2_done, 1);  // read by scan, gather, combine
     } else if ((MASK & 4u) && ph == 2) {
-      if (wait_geq(F.s.r2_done, F.nb, W, &s_flag)) layout_scan(F, (int*)smem);
+      if (wait_geq(F.s.r2_done, F.nb * kTopkChunks, W, &s_flag)) layout_scan(F, (int*)smem);
       signal_add<(MASK & 0x78u) != 0>(F.s.scan_done, 1);
     } else if ((MASK & 8u) && ph == 3) {
       // MXFP8: a row tile is ready once the codes of x are complete too
@@ -642,7 +640,7 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   }
   hipLaunchKernelGGL(k_router_partial<Act>, dim3(p.nb * p.S), dim3(256), 0, st, F);
   if (!set_smem(k_router_topk<true>, kTopkSmem)) return MOE_ERR_HIP;
-  hipLaunchKernelGGL(k_router_topk<true>, dim3(p.nb), dim3(256), kTopkSmem, st, F);
+  hipLaunchKernelGGL(k_router_topk<true>, dim3(p.nb * kTopkChunks), dim3(256), kTopkSmem, st, F);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
   if (TL::kMX) hipLaunchKernelGGL(k_quant_tokens, dim3(p.nb), dim3(256), 0, st, F);
   if (F.direct)
@@ -760,7 +758,8 @@ int moe_route(const moe_desc* desc, const float* logits, const float* bias, int3
   F.topk = topk_idx;
   F.gate = gate;
   if (!set_smem(k_router_topk<false>, kTopkSmem)) return MOE_ERR_HIP;
-  hipLaunchKernelGGL(k_router_topk<false>, dim3(p.nb), dim3(256), kTopkSmem, (hipStream_t)stream, F);
+  hipLaunchKernelGGL(k_router_topk<false>, dim3(p.nb * kTopkChunks), dim3(256), kTopkSmem, (hipStream_t)stream,
+                     F);
   return launch_status();
 }
 

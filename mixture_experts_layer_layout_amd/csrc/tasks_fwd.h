@@ -79,7 +79,6 @@ struct Fwd {
   int* topk;         // [T, k]
   float* gate;       // [T, k]
   unsigned long long* bmask;  // [nb, E]
-  int* bcnt;         // [nb, E]
   int* bbase;        // [nb, E]
   int* counts;       // [E]
   int* offsets;      // [E+1]
@@ -250,30 +249,32 @@ __device__ __forceinline__ void wave_topk_gates(const float* row, const float* k
   sel_g = g * scale;
 }
 
-constexpr int kTopkChunk = 8;   // tokens whose logits are staged in LDS at once
-// LDS of router_topk: block masks (kMaxE u64) + a chunk of logits + one
-// row of score-space keys per wave
+constexpr int kTopkChunk = 8;   // tokens of one top-k task (staged in LDS at once)
+constexpr int kTopkChunks = 64 / kTopkChunk;  // top-k tasks per 64-token block
+// LDS of router_topk: the chunk's choices (within the first kMaxE u64) + a
+// chunk of logits + one row of score-space keys per wave
 constexpr size_t kTopkSmem = kMaxE * 8 + (size_t)kTopkChunk * kMaxE * 4 + 4 * (size_t)kMaxE * 4;
 
-// Sums the slices, adds the bias, selects, writes idx/gates and the block's
-// expert bitmasks.  The logits of 8 tokens at a time are summed into LDS by
-// the whole workgroup (coalesced, independent loads), then each wave selects
-// for 2 of them.  With S == 1 and lpart == the caller's logits this is also
-// the standalone route step.
+// One task per chunk of kTopkChunk tokens (kTopkChunks tasks per 64-token
+// block): sums the slices, adds the bias, selects, writes idx/gates and
+// (MASKS) its byte of every expert's block bitmask -- bits 8c .. 8c+7 of
+// bmask[b, e] for chunk c, zeros included, so no task needs the mask
+// cleared first and no two tasks write the same byte.  The logits of the
+// chunk's tokens are summed into LDS by the whole workgroup (coalesced,
+// independent loads), then each wave selects for 2 of them.  With S == 1
+// and lpart == the caller's logits this is also the standalone route step.
 template <bool MASKS>
-__device__ void router_topk(const Fwd& F, int b, char* smem) {
-  unsigned long long* smask = (unsigned long long*)smem;
+__device__ void router_topk(const Fwd& F, int task, char* smem) {
+  int* ssel = (int*)smem;  // [kTopkChunk][kMaxK] chosen experts of the chunk
   float* sv = (float*)(smem + kMaxE * 8);
   float* skey = sv + kTopkChunk * kMaxE + (threadIdx.x >> 6) * kMaxE;  // this wave's keys
   const bool keyed = F.select_only || F.n_group > 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = F.E;
-  if (MASKS)
-    for (int e = threadIdx.x; e < E; e += kThreads) smask[e] = 0ull;
-  for (int c0 = 0; c0 < kTokBlock; c0 += kTopkChunk) {
-    const int t0 = b * kTokBlock + c0;
-    if (t0 >= F.T) break;
-    __syncthreads();
+  const int b = task / kTopkChunks, c = task - b * kTopkChunks;
+  const int t0 = b * kTokBlock + c * kTopkChunk;
+  __syncthreads();
+  if (t0 < F.T) {
     for (int p = threadIdx.x; p < kTopkChunk * E; p += kThreads) {
       const int t = t0 + p / E, e = p % E;
       if (t >= F.T) break;
@@ -304,16 +305,19 @@ __device__ void router_topk(const Fwd& F, int b, char* smem) {
       if (lane < F.k) {
         F.topk[(size_t)t * F.k + lane] = se;
         F.gate[(size_t)t * F.k + lane] = sg;
-        if (MASKS) atomicOr(&smask[se], 1ull << (c0 + tt));
+        if (MASKS) ssel[tt * kMaxK + lane] = se;
       }
     }
   }
   if (MASKS) {
     __syncthreads();
+    const int nt = max(0, min(kTopkChunk, F.T - t0));  // tokens of this chunk
     for (int e = threadIdx.x; e < E; e += kThreads) {
-      const unsigned long long m = smask[e];
-      F.bmask[(size_t)b * E + e] = m;
-      F.bcnt[(size_t)b * E + e] = __popcll(m);
+      unsigned int byte = 0;
+      for (int tt = 0; tt < nt; ++tt)
+        for (int j = 0; j < F.k; ++j)
+          if (ssel[tt * kMaxK + j] == e) byte |= 1u << tt;
+      ((uint8_t*)(F.bmask + (size_t)b * E + e))[c] = (uint8_t)byte;
     }
   }
 }
@@ -338,7 +342,6 @@ __device__ void build_masks(const Fwd& F, int b, unsigned long long* smask) {
   for (int e = threadIdx.x; e < F.E; e += kThreads) {
     const unsigned long long m = smask[e];
     F.bmask[(size_t)b * F.E + e] = m;
-    F.bcnt[(size_t)b * F.E + e] = __popcll(m);
   }
 }
 
@@ -383,7 +386,7 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   __syncthreads();
   for (int e = threadIdx.x; e < F.E; e += kThreads) {
     int tot = 0;
-    for (int b = 0; b < F.nb; ++b) tot += F.bcnt[(size_t)b * F.E + e];
+    for (int b = 0; b < F.nb; ++b) tot += __popcll(F.bmask[(size_t)b * F.E + e]);
     scnt[e] = tot;
     stile[e] = cdiv(tot, F.BM);
     F.counts[e] = tot;
@@ -398,7 +401,7 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
     int run = off;
     for (int b = 0; b < F.nb; ++b) {
       F.bbase[(size_t)b * F.E + e] = run;
-      run += F.bcnt[(size_t)b * F.E + e];
+      run += __popcll(F.bmask[(size_t)b * F.E + e]);
     }
     const int cnt = run - off;
     for (int mt = 0, id = stile[e]; mt * F.BM < cnt; ++mt, ++id) {
