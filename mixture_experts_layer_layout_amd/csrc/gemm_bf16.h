@@ -6,7 +6,7 @@
 // stages and two register stages, so the global loads of two stages are in
 // flight while a third feeds the MFMAs; one barrier per step.  LDS holds
 // both operands k-contiguous: a row of 64 bf16 is 8 chunks of 16 bytes and
-// chunk c of row r is stored at chunk c ^ ((r >> 1) & 7) (lds_idx), so the
+// chunk c of row r is stored at chunk c ^ lds_key(r) (lds_idx), so the
 // 16-byte reads and writes of 16 lanes at a time hit 16 different bank
 // groups.
 //
@@ -34,13 +34,29 @@
 
 namespace moe {
 
+// The XOR key of tile row `row`.  The LDS serves 256 bytes (64 banks) per
+// cycle, i.e. one 16-byte access for each of 16 lanes, or one 8-byte access
+// for each of 32.  (row >> 1) & 7 places the same chunk of 16 consecutive
+// rows (two rows per 256 bytes) in 16 different slots, and the 8 chunks of
+// one row in 8 different slots: the fragment reads (16 aligned consecutive
+// rows, one chunk) and the row-wise stores need no more.  HI adds the term
+// (row >> 4) << 1, constant over 16 aligned rows, for the K-major loader's
+// 8-byte stores: a 32-lane group writes one row of each of 8 column blocks
+// (rows 8 apart) for 4 k-groups, and without the term column blocks of
+// equal parity share slots.  Measured on the backward's register-staged
+// tiles it takes 15-26% of the LDS instruction cycles off (the K-major
+// tiles run 4-6% faster); on the direct-to-LDS forward tile it raised the
+// bank-conflict count by two orders of magnitude and cost 1.5%, so that tile keeps the
+// plain key (Tile::kKeyHi / TileD::kKeyHi).
+template <bool HI>
+__device__ __forceinline__ int lds_key(int row) {
+  return HI ? ((row >> 1) ^ ((row >> 4) << 1)) & 7 : (row >> 1) & 7;
+}
+
 // Element index of 16-byte chunk `chunk` of tile row `row` in an LDS stage.
-// The LDS serves 256 bytes (64 banks) per cycle, i.e. one 16-byte access
-// for each of 16 lanes: the XOR key (row >> 1) & 7 places the same chunk of
-// 16 consecutive rows (two rows per 256 bytes) in 16 different slots, and
-// the 8 chunks of one row in 8 different slots.
+template <bool HI>
 __device__ __forceinline__ int lds_idx(int row, int chunk) {
-  return (row << 6) + (((chunk ^ (row >> 1)) & 7) << 3);
+  return (row << 6) + ((chunk ^ lds_key<HI>(row)) << 3);
 }
 
 // Stages whose global loads are in flight while one stage feeds the MFMAs
@@ -60,6 +76,7 @@ template <int BM_, int BN_>
 struct Tile {
   static constexpr bool kMX = false;
   static constexpr bool kDMA = false;
+  static constexpr bool kKeyHi = true;  // lds_key<true>
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NJ = WN / 32;
@@ -90,11 +107,11 @@ struct KRows {
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[BUF][i] = *(const uint4*)(row[i] + kt * 64 + ch * 8);
   }
-  template <int BUF>
+  template <int BUF, bool HI>
   __device__ __forceinline__ void store(bf16_t* lds) const {
     const int r0 = threadIdx.x >> 3, ch = threadIdx.x & 7;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) *(uint4*)(lds + lds_idx(r0 + 32 * i, ch)) = v[BUF][i];
+    for (int i = 0; i < PER; ++i) *(uint4*)(lds + lds_idx<HI>(r0 + 32 * i, ch)) = v[BUF][i];
   }
 };
 
@@ -173,7 +190,7 @@ struct KCols {
       if (SCALED) sl[BUF][kk] = s[kk];
     }
   }
-  template <int BUF>
+  template <int BUF, bool HI>
   __device__ __forceinline__ void store(bf16_t* lds) {
     uint32_t* w = (uint32_t*)v[BUF];  // w[kk*4 + q] = elements 2q, 2q+1 of k-row kk
     if (SCALED) {
@@ -201,12 +218,12 @@ struct KCols {
         o.y = __builtin_amdgcn_perm(w[3 * 4 + q], w[2 * 4 + q], sel);
         o.z = __builtin_amdgcn_perm(w[5 * 4 + q], w[4 * 4 + q], sel);
         o.w = __builtin_amdgcn_perm(w[7 * 4 + q], w[6 * 4 + q], sel);
-        *(uint4*)(lds + lds_idx(nb * 8 + mm, kg)) = o;
+        *(uint4*)(lds + lds_idx<HI>(nb * 8 + mm, kg)) = o;
       } else {
         uint2 o;
         o.x = __builtin_amdgcn_perm(w[1 * 4 + q], w[0 * 4 + q], sel);
         o.y = __builtin_amdgcn_perm(w[3 * 4 + q], w[2 * 4 + q], sel);
-        *(uint2*)(lds + lds_idx(nb * 8 + mm, kg >> 1) + (kg & 1) * 4) = o;
+        *(uint2*)(lds + lds_idx<HI>(nb * 8 + mm, kg >> 1) + (kg & 1) * 4) = o;
       }
     }
   }
@@ -245,10 +262,10 @@ __device__ __forceinline__ void tile_compute(const bf16_t* As, const bf16_t* Bs,
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
-      fa[i] = *(const bf16x8_t*)(As + lds_idx(wm * TL::WM + 32 * i + (lane & 31), ch));
+      fa[i] = *(const bf16x8_t*)(As + lds_idx<TL::kKeyHi>(wm * TL::WM + 32 * i + (lane & 31), ch));
 #pragma unroll
     for (int j = 0; j < TL::NJ; ++j)
-      fb[j] = *(const bf16x8_t*)(Bs + lds_idx(wn * TL::WN + 32 * j + (lane & 31), ch));
+      fb[j] = *(const bf16x8_t*)(Bs + lds_idx<TL::kKeyHi>(wn * TL::WN + 32 * j + (lane & 31), ch));
   };
   frags(0, a[0], b[0]);
 #pragma unroll
@@ -299,14 +316,14 @@ __device__ __forceinline__ void mainloop_step(int kt, int last, bf16_t* As, bf16
   __builtin_amdgcn_sched_barrier(0);
   TL::stage(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
-  A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
-  B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);
+  A.template store<SB, TL::kKeyHi>(As + (CUR ^ 1) * TL::LDS_A);
+  B.template store<SB, TL::kKeyHi>(Bs + (CUR ^ 1) * TL::LDS_B);
   __syncthreads();
 }
 
 // Loads the first PF stages (stage s into register buffer s) and stores
 // stage 0 into LDS buffer 0.
-template <int PF = kPrefetch, class LA, class LB>
+template <class TL, int PF = kPrefetch, class LA, class LB>
 __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* Bs, LA& A, LB& B) {
   A.prep(0);
   B.prep(0);
@@ -333,8 +350,8 @@ __device__ __forceinline__ void mainloop_prologue(int last, bf16_t* As, bf16_t* 
     B.prep(min(4, last));
   }
   __syncthreads();
-  A.template store<0>(As);
-  B.template store<0>(Bs);
+  A.template store<0, TL::kKeyHi>(As);
+  B.template store<0, TL::kKeyHi>(Bs);
   __syncthreads();
 }
 
@@ -377,7 +394,7 @@ __device__ __forceinline__ void tile_mainloop(int nk, bf16_t* smem, f32x16_t (&a
   const int last = nk - 1;
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
-  mainloop_prologue<PF>(last, As, Bs, A, B);
+  mainloop_prologue<TL, PF>(last, As, Bs, A, B);
   int kt = 0;
   for (; kt + U <= nk; kt += U) mainloop_round<0, U, TL, PF>(kt, last, As, Bs, acc, A, B);
   mainloop_tail<0, U, TL, PF>(kt, nk, last, As, Bs, acc, A, B);
@@ -441,8 +458,8 @@ __device__ __forceinline__ void stream_step(int j, int s, int c, int nk, int las
   __builtin_amdgcn_sched_barrier(0);
   TL::stage(As + CUR * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
-  A.template store<SB>(As + (CUR ^ 1) * TL::LDS_A);
-  B.template store<SB>(Bs + (CUR ^ 1) * TL::LDS_B);
+  A.template store<SB, TL::kKeyHi>(As + (CUR ^ 1) * TL::LDS_A);
+  B.template store<SB, TL::kKeyHi>(Bs + (CUR ^ 1) * TL::LDS_B);
   if (s == nk - 1) {
     epi(c, acc);
 #pragma unroll
@@ -470,7 +487,7 @@ __device__ __forceinline__ void tile_stream(int nc, int nk, bf16_t* smem, LA& A,
   const int last = total - 1;
   bf16_t* As = smem;
   bf16_t* Bs = smem + 2 * TL::LDS_A;
-  mainloop_prologue(last, As, Bs, A, B);
+  mainloop_prologue<TL>(last, As, Bs, A, B);
   int j = 0, s = 0, c = 0;
   auto advance = [&] {
     if (++s == nk) {
@@ -511,7 +528,7 @@ __device__ __forceinline__ void band_step(int j, int c, int last, const bf16_t* 
   __builtin_amdgcn_sched_barrier(0);
   TL::stage(As + S * TL::LDS_A, Bs + CUR * TL::LDS_B, acc);
   __builtin_amdgcn_sched_barrier(0);
-  B.template store<CUR ^ 1>(Bs + (CUR ^ 1) * TL::LDS_B);
+  B.template store<CUR ^ 1, TL::kKeyHi>(Bs + (CUR ^ 1) * TL::LDS_B);
   if (EPI_NOW) {
     epi(c, acc);
 #pragma unroll
@@ -550,14 +567,14 @@ __device__ __forceinline__ void tile_band(int nc, bf16_t* smem, LA& A, LB& B, EP
   for (int s = 0; s < NK; ++s) {
     A.prep(s);
     A.template load<0>(s);
-    A.template store<0>(As + s * TL::LDS_A);
+    A.template store<0, TL::kKeyHi>(As + s * TL::LDS_A);
   }
   B.prep(0);
   B.template load<0>(0);
   B.prep(min(1, last));
   B.template load<1>(min(1, last));
   B.prep(min(2, last));
-  B.template store<0>(Bs);
+  B.template store<0, TL::kKeyHi>(Bs);
   __syncthreads();
   if (NK == 1) {
     band_step<0, 0, true, TL>(0, 0, last, As, Bs, acc, B, epi);

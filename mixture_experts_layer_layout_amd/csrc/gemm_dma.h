@@ -10,7 +10,7 @@
 // (lds_idx), so tile_compute reads it unchanged.  A DMA instruction writes
 // 64 lanes x 16 bytes to consecutive LDS bytes; lane i of the instruction
 // that fills tile rows 8m .. 8m+7 lands at row 8m + i/8, slot i%8, and so
-// loads the row's logical 16-byte chunk (i%8) ^ ((row >> 1) & 7).
+// loads the row's logical 16-byte chunk (i%8) ^ lds_key<false>(row).
 //
 // Waiting: the DMA loads count in vmcnt like any vector load, and their LDS
 // writes are complete when the count drops past them.  At the top of each
@@ -32,6 +32,7 @@ template <int BM_, int BN_>
 struct TileD {
   static constexpr bool kMX = false;
   static constexpr bool kDMA = true;
+  static constexpr bool kKeyHi = false;  // lds_key<false>
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NJ = WN / 32;
@@ -56,7 +57,7 @@ struct DmaRows {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int row = 8 * (4 * q + w) + (lane >> 3);
-      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+      const int chunk = (lane & 7) ^ lds_key<false>(row);  // TileD::kKeyHi
       src[q] = (const char*)rowptr(row) + chunk * 16;
     }
   }

@@ -35,6 +35,7 @@ template <int BM_, int BN_>
 struct TileMX {
   static constexpr bool kMX = true;
   static constexpr bool kDMA = false;
+  static constexpr bool kKeyHi = false;  // lds_key<false>
   static constexpr int BM = BM_, BN = BN_;
   static_assert(BM + BN == kThreads, "one scale row per thread");
   static constexpr int WM = BM / 2, WN = BN / 2;
@@ -87,9 +88,10 @@ struct KRowsMX {
       sv[BUF] = srow[kt];
     }
   }
-  template <int BUF>
+  template <int BUF, bool HI>
   __device__ __forceinline__ void store(bf16_t* lds) const {
-    codes.template store<BUF>(lds);
+    static_assert(!HI, "the MX tile reads with lds_key<false>");
+    codes.template store<BUF, HI>(lds);
     ((uint32_t*)(lds + ROWS * 64))[threadIdx.x] = sv[BUF];
   }
 };
@@ -112,8 +114,8 @@ __device__ __forceinline__ void tile_compute_mx(const bf16_t* As, const bf16_t* 
   const uint32_t* sa = (const uint32_t*)(As + TL::BM * 64);
   const uint32_t* sb = sa + TL::BM;
   auto frag = [&](const bf16_t* base, int row, int s) -> i32x8_t {
-    const uint4 lo = *(const uint4*)(base + lds_idx(row, 4 * s + h));
-    const uint4 hi = *(const uint4*)(base + lds_idx(row, 4 * s + 2 + h));
+    const uint4 lo = *(const uint4*)(base + lds_idx<TL::kKeyHi>(row, 4 * s + h));
+    const uint4 hi = *(const uint4*)(base + lds_idx<TL::kKeyHi>(row, 4 * s + 2 + h));
     i32x8_t v;
     v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
     v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
