@@ -202,14 +202,78 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
     I = np.shape(w1)[1]
     d = np.shape(w1)[2]
     R = perm.shape[0]
+    A = np.zeros((R, I))
+    B = np.zeros((R, I))
     H = np.zeros((R, I))
     Yp = np.zeros((R, d))
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        _, _, H[lo:hi], Yp[lo:hi] = expert_ffn_mxfp8(xp[lo:hi], w1[e], w3[e], w2[e])
+        A[lo:hi], B[lo:hi], H[lo:hi], Yp[lo:hi] = expert_ffn_mxfp8(xp[lo:hi], w1[e], w3[e], w2[e])
     y = M.combine(Yp, gate, inv, T, k)
     return dict(logits=logits, topk_idx=idx, gate=gate, counts=counts,
-                offsets=offsets, perm=perm, inv=inv, src=src, H=H, Yp=Yp,
+                offsets=offsets, perm=perm, inv=inv, src=src, A=A, B=B, H=H, Yp=Yp,
                 y=y)
+
+
+def backward_mxfp8(dy, x, fwd, w1, w3, w2, k):
+    """The backward of the expert path (routing frozen) with the two data
+    gradient GEMMs in MXFP8 and the weight gradients in high precision.
+
+    MoK flash §03 quotes the backward in MXFP8 but does not say which
+    products are quantised.  Reading taken: the data gradients dHu = G W2
+    and dXp = dA W1 + dB W3 run in MXFP8, each operand quantised along that
+    product's contraction axis -- the upstream rows G along d and W2 as
+    [I, d] (W2^T) along d; [dA | dB] along I and W1, W3 as [d, I] (W^T)
+    along I -- while the weight gradients take the unquantised operands (G,
+    the forward's H, dA, dB and the gathered x rows).  The steps are those
+    of moe.backward; fwd holds the forward's gate, layout and A, B, H.
+    """
+    from . import moe as M
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    T, d = dy.shape
+    E, I, _ = np.shape(w1)
+    offsets, perm, inv, src = fwd["offsets"], fwd["perm"], fwd["inv"], fwd["src"]
+    gate = np.asarray(fwd["gate"], dtype=np.float64)
+    A, B, H = fwd["A"], fwd["B"], fwd["H"]
+    R = perm.shape[0]
+    g_row = gate.reshape(-1)[perm]
+    G = dy[src]                                    # pull reverse-combine
+    Gq = fake_quant(dy)[src]                       # rows quantised along d
+    xp = x[src]
+    dHu = np.zeros((R, I))
+    dW1 = np.zeros((E, I, d))
+    dW3 = np.zeros((E, I, d))
+    dW2 = np.zeros((E, d, I))
+    dXp = np.zeros((R, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        w2t = fake_quant(np.asarray(w2[e], dtype=np.float64).T)      # [I, d] along d
+        dHu[lo:hi] = Gq[lo:hi] @ w2t.T
+        dW2[e] = (g_row[lo:hi, None] * G[lo:hi]).T @ H[lo:hi]
+    dgate_row = np.sum(dHu * H, axis=1)
+    dH = g_row[:, None] * dHu
+    sA = M.sigmoid(A)
+    dA = dH * B * sA * (1.0 + A * (1.0 - sA))
+    dB = dH * M.silu(A)
+    dAq = fake_quant(dA)                           # along I
+    dBq = fake_quant(dB)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        w1t = fake_quant(np.asarray(w1[e], dtype=np.float64).T)      # [d, I] along I
+        w3t = fake_quant(np.asarray(w3[e], dtype=np.float64).T)
+        dXp[lo:hi] = dAq[lo:hi] @ w1t.T + dBq[lo:hi] @ w3t.T
+        dW1[e] = dA[lo:hi].T @ xp[lo:hi]
+        dW3[e] = dB[lo:hi].T @ xp[lo:hi]
+    dx = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            dx[t] += dXp[inv[t * k + j]]
+    dgate = dgate_row[inv].reshape(T, k)
+    return dict(dx=dx, dw1=dW1, dw3=dW3, dw2=dW2, dgate=dgate, dHu=dHu, dA=dA, dB=dB, dXp=dXp)
