@@ -236,6 +236,18 @@ MOE_API int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm,
 MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K,
                        uint8_t* codes, uint8_t* scales, void* stream);
 
+/* MXFP8 quantisation of the transpose of each bf16 matrix of a batch (the
+ * backward's weights, MoK flash §03: the data gradients contract W1, W3
+ * over I and W2 over d, the axes their forward does not block along).
+ *   src    bf16  [batch, rows, cols]
+ *   codes  uint8 [batch, cols, rows]      E4M3 codes of src^T
+ *   scales uint8 [batch, cols, rows/32]   E8M0 codes, blocks of 32 along rows
+ * rows % 32 == 0 (else MOE_ERR_INVALID_ARG); batch <= 65535, rows/32 <=
+ * 65535 and cols <= 2^30 (else MOE_ERR_UNSUPPORTED).  The same encoding as
+ * moe_quantize_mxfp8. */
+MOE_API int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                 uint8_t* codes, uint8_t* scales, void* stream);
+
 /* The whole forward layer (MoK flash §03: schedule, dispatch, expert FFN,
  * combine and the final weighted merge).
  *   x     act [T, d];  wr act [E, d] (row e scores expert e);
@@ -269,8 +281,17 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
  * dW1/dW3, dX) run through the persistent scheduler, one launch per phase
  * (setup and pulls together) unless MOE_FLAG_PERSISTENT_SINGLE or
  * MOE_FLAG_PERSISTENT_WGRAD_APART is set;
- * with fused = 0 each phase is an ordinary grid.  Needs bf16 with
- * d % 256 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED). */
+ * with fused = 0 each phase is an ordinary grid.  Needs bf16 activations
+ * with d % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).
+ * With desc->expert_dtype == MOE_MXFP8 the data gradients dHu = G W2 and
+ * dXp = dA W1 + dB W3 run in MXFP8 (MoK flash §03), each operand blocked
+ * along that product's contraction axis, and w holds the transposed weights
+ * from moe_quantize_mxfp8_t: w1, w3 the codes of W1^T, W3^T uint8 [E, d, I]
+ * with w1_scale, w3_scale [E, d, I/32]; w2 the codes of W2^T [E, I, d] with
+ * w2_scale [E, I, d/32] (all required).  dY and [dA | dB] are quantised
+ * along their rows inside the call; the weight gradients, dX's gather-sum
+ * and dgate take the bf16 operands as in the bf16 backward.  This variant
+ * runs every phase as an ordinary grid whatever desc->fused says. */
 MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
                  const moe_weights* w, const moe_saved* saved, void* dx,
                  void* dw1, void* dw3, void* dw2, float* dgate,

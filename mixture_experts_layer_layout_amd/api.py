@@ -69,6 +69,8 @@ _lib.moe_layout.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p,
 _lib.moe_gather.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
 _lib.moe_quantize_mxfp8.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, c_void_p,
                                     c_void_p, c_void_p]
+_lib.moe_quantize_mxfp8_t.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      c_void_p, c_void_p, c_void_p]
 _lib.moe_forward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWeights),
                              c_void_p, _P(MoeSaved), c_void_p, ctypes.c_size_t, c_void_p]
 _lib.moe_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, _P(MoeWeights), _P(MoeSaved),
@@ -80,12 +82,12 @@ _lib.moe_router_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, 
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_status_string.restype = ctypes.c_char_p
 for _f in ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather", "moe_quantize_mxfp8",
-           "moe_forward", "moe_backward", "moe_router_backward"):
+           "moe_quantize_mxfp8_t", "moe_forward", "moe_backward", "moe_router_backward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather",
-           "moe_quantize_mxfp8", "moe_forward", "moe_backward", "moe_router_backward",
-           "moe_status_string")
+           "moe_quantize_mxfp8", "moe_quantize_mxfp8_t", "moe_forward", "moe_backward",
+           "moe_router_backward", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -149,6 +151,15 @@ def moe_quantize_mxfp8(src, codes, scales, stream=None):
     rows = src.numel() // K
     _check(_lib.moe_quantize_mxfp8(_p(src), rows, K, _p(codes), _p(scales), _stream(stream)),
            "moe_quantize_mxfp8")
+
+
+def moe_quantize_mxfp8_t(src, codes, scales, stream=None):
+    """src [batch, rows, cols] (or [rows, cols]) -> codes [batch, cols, rows],
+    scales [batch, cols, rows/32]."""
+    batch = 1 if src.dim() == 2 else src.shape[0]
+    rows, cols = src.shape[-2], src.shape[-1]
+    _check(_lib.moe_quantize_mxfp8_t(_p(src), batch, rows, cols, _p(codes), _p(scales), _stream(stream)),
+           "moe_quantize_mxfp8_t")
 
 
 def make_weights(w1, w3, w2, w1_scale=None, w3_scale=None, w2_scale=None) -> MoeWeights:

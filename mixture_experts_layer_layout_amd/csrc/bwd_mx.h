@@ -1,0 +1,184 @@
+// bwd_mx.h -- the backward's two data-gradient GEMMs in MXFP8 (MoK flash
+// §03 quotes the backward in MXFP8; the weight gradients stay bf16 here).
+//
+// Each product takes its operands quantised along its own contraction axis,
+// one E8M0 scale per 32 values:
+//   dHu = G W2_e       G rows are dY rows (quantised once per token along
+//                      d, pulled through the layout's source index like the
+//                      bf16 dh tile's rows); W2_e enters as W2_e^T [I, d],
+//                      blocks along d
+//   dXp = [dA | dB] [W1_e ; W3_e]   [dA | dB] rows quantised along 2I after
+//                      the dh epilogue wrote them; W1_e, W3_e enter as
+//                      W^T [d, I], blocks along I
+// Both run on the scaled matrix-core tile (gemm_mx.h), whose operands are
+// k-contiguous rows, so the transposed weights come from
+// moe_quantize_mxfp8_t (k_mx_quant_t below), once per weight update.  The
+// epilogues are the bf16 tiles' (same accumulator layout).
+#pragma once
+
+#include "mxfp8.h"
+#include "tasks_bwd.h"
+
+namespace moe {
+
+// Rows of codes with k contiguous whose K range is two stored rows: stages
+// kt < split from lo(r), the rest from hi(r) (the W1^T and W3^T halves of
+// one output column of dXp).
+template <int ROWS>
+struct KRowsSplit {
+  static constexpr int PER = ROWS / 32;
+  const bf16_t* lo[PER];
+  const bf16_t* hi[PER];
+  int split;
+  uint4 v[kPrefetch][PER];
+  template <class F, class G>
+  __device__ __forceinline__ void init(F plo, G phi, int split_stage) {
+    const int r0 = threadIdx.x >> 3;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      lo[i] = plo(r0 + 32 * i);
+      hi[i] = phi(r0 + 32 * i);
+    }
+    split = split_stage;
+  }
+  __device__ __forceinline__ void prep(int) {}
+  template <int BUF>
+  __device__ __forceinline__ void load(int kt) {
+    const int ch = threadIdx.x & 7;
+    const bool second = kt >= split;
+    const int ks = second ? kt - split : kt;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[BUF][i] = *(const uint4*)((second ? hi[i] : lo[i]) + ks * 64 + ch * 8);
+  }
+  template <int BUF, bool HI>
+  __device__ __forceinline__ void store(bf16_t* lds) const {
+    const int r0 = threadIdx.x >> 3, ch = threadIdx.x & 7;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) *(uint4*)(lds + lds_idx<HI>(r0 + 32 * i, ch)) = v[BUF][i];
+  }
+};
+
+// KRowsMX (codes of A, scale words of A and B rows) where the B rows' scale
+// words, like their codes, switch to a second stored row at stage `split`.
+// A rows are single rows over the whole K (their second pointer continues
+// the first).
+template <int ROWS, int BROWS>
+struct KRowsMXSplit {
+  static_assert(ROWS + BROWS == kThreads, "one scale row per thread");
+  KRows<ROWS> codes;
+  const uint32_t* slo;
+  const uint32_t* shi;
+  int split;
+  uint32_t sv[kPrefetch];
+  uint4 s4;
+  bool wide;
+  // wide: every scale row 16-byte aligned and split % 4 == 0
+  template <class F, class GA, class GL, class GH>
+  __device__ __forceinline__ void init(F rowptr, GA ascale, GL bscale_lo, GH bscale_hi, int split_stage,
+                                       bool wide_rows) {
+    codes.init([&](int r) { return (const bf16_t*)rowptr(r); });
+    const int t = threadIdx.x;
+    if (t < ROWS) {
+      slo = (const uint32_t*)ascale(t);
+      shi = slo + split_stage;
+    } else {
+      slo = (const uint32_t*)bscale_lo(t - ROWS);
+      shi = (const uint32_t*)bscale_hi(t - ROWS);
+    }
+    split = split_stage;
+    wide = wide_rows;
+  }
+  __device__ __forceinline__ void prep(int) {}
+  template <int BUF>
+  __device__ __forceinline__ void load(int kt) {
+    codes.template load<BUF>(kt);
+    const bool second = kt >= split;
+    const uint32_t* p = second ? shi + (kt - split) : slo + kt;
+    if (wide) {
+      const int q = kt & 3;
+      if (q == 0) s4 = *(const uint4*)p;
+      sv[BUF] = q == 0 ? s4.x : q == 1 ? s4.y : q == 2 ? s4.z : s4.w;
+    } else {
+      sv[BUF] = *p;
+    }
+  }
+  template <int BUF, bool HI>
+  __device__ __forceinline__ void store(bf16_t* lds) const {
+    static_assert(!HI, "the MX tile reads with lds_key<false>");
+    codes.template store<BUF, HI>(lds);
+    ((uint32_t*)(lds + ROWS * 64))[threadIdx.x] = sv[BUF];
+  }
+};
+
+// dHu = G W2_e in MXFP8 for one (row tile, I tile), then the dh epilogue.
+__device__ void bwd_dh_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
+  typedef TileMX128 TL;
+  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const int d = B.d, I = B.I, ds = d / 32;
+  const uint8_t* W = B.w2t + (size_t)e * I * d;
+  const uint8_t* S = B.w2ts + (size_t)e * I * ds;
+  const int c0 = nt * TL::BN;
+  KRowsMX<TL::BM, TL::BN> la;
+  KRows<TL::BN> lb;
+  // rows past n repeat the last row (their outputs are dropped)
+  la.init([&](int r) { return B.dyq + (size_t)B.src[r0 + min(r, n - 1)] * d; },
+          [&](int r) { return B.dys + (size_t)B.src[r0 + min(r, n - 1)] * ds; },
+          [&](int nr) { return S + (size_t)(c0 + nr) * ds; }, B.mx_wide_d != 0);
+  lb.init([&](int nr) { return (const bf16_t*)(W + (size_t)(c0 + nr) * d); });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(d / 128, smem, acc, la, lb);
+  bwd_dh_epilogue<TL>(B, acc, r0, n, nt, smem);
+}
+
+// dXp = [dA | dB] [W1_e ; W3_e] in MXFP8 for one (row tile, d tile): K = 2I,
+// the first I from W1_e^T, the rest from W3_e^T.
+__device__ void bwd_dxp_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
+  typedef TileMX128 TL;
+  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const int d = B.d, I = B.I, I2 = 2 * I, is = I / 32;
+  const uint8_t* W1 = B.w1t + (size_t)e * d * I;
+  const uint8_t* W3 = B.w3t + (size_t)e * d * I;
+  const uint8_t* S1 = B.w1ts + (size_t)e * d * is;
+  const uint8_t* S3 = B.w3ts + (size_t)e * d * is;
+  const int c0 = nt * TL::BN;
+  const int split = I / 128;
+  KRowsMXSplit<TL::BM, TL::BN> la;
+  KRowsSplit<TL::BN> lb;
+  la.init([&](int r) { return B.dabq + (size_t)(r0 + min(r, n - 1)) * I2; },
+          [&](int r) { return B.dabs + (size_t)(r0 + min(r, n - 1)) * (I2 / 32); },
+          [&](int nr) { return S1 + (size_t)(c0 + nr) * is; }, [&](int nr) { return S3 + (size_t)(c0 + nr) * is; },
+          split, B.mx_wide_i != 0);
+  lb.init([&](int nr) { return (const bf16_t*)(W1 + (size_t)(c0 + nr) * I); },
+          [&](int nr) { return (const bf16_t*)(W3 + (size_t)(c0 + nr) * I); }, split);
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL>(I2 / 128, smem, acc, la, lb);
+  const Staged<TL::BM, TL::BN> st{smem};
+  tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
+  st.flush(n, [&](int row) { return B.dxp + (size_t)(r0 + row) * d + c0; });
+}
+
+// Quantisation of the transpose of each [rows, cols] bf16 matrix of a
+// batch along its rows: codes [cols, rows] and scales [cols, rows / 32]
+// per matrix.  Thread c of a workgroup takes column c of a 32-row block:
+// the 32 loads of a step read 512 consecutive bytes across the workgroup's
+// 256 threads, and each thread writes its 32 codes as two 16-byte stores
+// and one scale byte.
+__global__ void __launch_bounds__(256) k_mx_quant_t(const bf16_t* __restrict__ src, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales, int rows, int cols) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const int rb = blockIdx.y;
+  if (c >= cols) return;
+  const size_t mat = (size_t)blockIdx.z * rows * cols;
+  const bf16_t* s = src + mat + (size_t)(32 * rb) * cols + c;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = bf16_to_f32(s[(size_t)j * cols]);
+  uint32_t w[8];
+  const uint32_t sc = mx_quant32(v, w);
+  uint4* dst = (uint4*)(codes + mat + (size_t)c * rows + 32 * rb);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[(size_t)blockIdx.z * cols * (rows / 32) + (size_t)c * (rows / 32) + rb] = (uint8_t)sc;
+}
+
+}  // namespace moe

@@ -19,6 +19,7 @@
 #include "sched.h"
 #include "mxfp8.h"
 #include "router_bwd.h"
+#include "bwd_mx.h"
 
 namespace moe {
 
@@ -79,7 +80,7 @@ int make_plan(const moe_desc* D, Plan* p) {
   // row tiles of the forward (BM rows) and of the backward (TileDH::BM rows)
   const int min_bm = p->BM < TileDH::BM ? p->BM : TileDH::BM;
   p->max_tiles = p->R / min_bm + (E < p->R ? E : p->R) + 1;
-  p->bwd_ok = !f32 && !p->mxfp8 && d % 128 == 0 && I % 128 == 0;
+  p->bwd_ok = !f32 && d % 128 == 0 && I % 128 == 0;
   p->nNdh = I / TileDH::BN;
   p->nNdx = d / TileDH::BN;
   p->nW2m = d / TileDW::BM;
@@ -119,6 +120,12 @@ int make_plan(const moe_desc* D, Plan* p) {
     p->o_zero = take(((size_t)2 * I + d + 256) * 2);
     p->o_dab = take(R * 2 * I * 2);
     p->o_dgp = take((size_t)p->nNdh * R * 4);
+    if (p->mxfp8) {
+      p->o_dyq = take((size_t)T * d);
+      p->o_dys = take((size_t)T * (d / 32));
+      p->o_dabq = take(R * 2 * I);
+      p->o_dabs = take(R * 2 * (I / 32));
+    }
   }
   p->o_rdz = take(R * 4);
   p->o_rpart = take((size_t)kRbSplits * E * d * 4);
@@ -435,6 +442,24 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dxp(Bwd B) {
   bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
 }
 
+__global__ void __launch_bounds__(256, 2) k_bwd_dh_mx(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= *B.s.n_mtiles * B.nNdh) return;
+  int tile, nt;
+  raster_decode(B.etile, B.E, B.nNdh, id, tile, nt);
+  bwd_dh_tile_mx(B, tile, nt, (bf16_t*)smem);
+}
+
+__global__ void __launch_bounds__(256, 2) k_bwd_dxp_mx(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  if (id >= *B.s.n_mtiles * B.nNdx) return;
+  int tile, nt;
+  raster_decode(B.etile, B.E, B.nNdx, id, tile, nt);
+  bwd_dxp_tile_mx(B, tile, nt, (bf16_t*)smem);
+}
+
 __global__ void __launch_bounds__(256, 2) k_bwd_dw2(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   // dispatch order (heaviest experts first) spread round-robin over the XCDs
@@ -680,6 +705,38 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   hipLaunchKernelGGL(k_zero, dim3(cdiv(nz, 256)), dim3(256), 0, st, at<int>(ws, p.o_zero), nz);
   // weight-gradient tiles: their main loop's LDS plus the store staging
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes + kWgradStageBytes;
+  if (p.mxfp8) {
+    // MXFP8 data gradients: every phase as an ordinary grid, with the two
+    // quantisations (dY before dh, [dA | dB] after it) in between
+    B.w1t = (const uint8_t*)w->w1; B.w3t = (const uint8_t*)w->w3; B.w2t = (const uint8_t*)w->w2;
+    B.w1ts = w->w1_scale; B.w3ts = w->w3_scale; B.w2ts = w->w2_scale;
+    B.dyq = at<uint8_t>(ws, p.o_dyq); B.dys = at<uint8_t>(ws, p.o_dys);
+    B.dabq = at<uint8_t>(ws, p.o_dabq); B.dabs = at<uint8_t>(ws, p.o_dabs);
+    auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    B.mx_wide_d = p.d % 512 == 0 && al16(B.dys) && al16(B.w2ts);
+    B.mx_wide_i = p.I % 512 == 0 && al16(B.dabs) && al16(B.w1ts) && al16(B.w3ts);
+    const size_t sm_mx = TileMX128::smem_bytes;
+    if (!set_smem(k_bwd_dh_mx, sm_mx) || !set_smem(k_bwd_dxp_mx, sm_mx) || !set_smem(k_bwd_dw2, sm_dw) ||
+        !set_smem(k_bwd_dw13, sm_dw))
+      return MOE_ERR_HIP;
+    hipLaunchKernelGGL(k_bwd_setup, dim3(1), dim3(256), 0, st, B);
+    if (p.nRP > 0) hipLaunchKernelGGL(k_bwd_rowprep, dim3(p.nRP), dim3(256), 0, st, B);
+    if (p.R > 0) {
+      int rc = mxfp8_quantize_rows(B.dy, p.T, p.d, B.dyq, B.dys, st);
+      if (rc != MOE_OK) return rc;
+      hipLaunchKernelGGL(k_bwd_dh_mx, dim3(p.max_tiles * p.nNdh), dim3(256), sm_mx, st, B);
+    }
+    hipLaunchKernelGGL(k_bwd_dw2, dim3(p.E * p.nW2m * cdiv(p.nW2n, kWgradPerTicket)), dim3(256), sm_dw, st, B);
+    if (p.R > 0) {
+      int rc = mxfp8_quantize_rows(B.dab, p.R, 2 * (int64_t)p.I, B.dabq, B.dabs, st);
+      if (rc != MOE_OK) return rc;
+      hipLaunchKernelGGL(k_bwd_dxp_mx, dim3(p.max_tiles * p.nNdx), dim3(256), sm_mx, st, B);
+    }
+    hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * cdiv(p.nW13n, kWgradPerTicket)), dim3(256), sm_dw, st,
+                       B);
+    if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
+    return launch_status();
+  }
   if (D->fused) {
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
     static_assert(2 * (TileDW::smem_bytes + kWgradStageBytes + 1024) <= 160 * 1024,
@@ -834,6 +891,18 @@ int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* codes,
   return mxfp8_quantize_rows((const bf16_t*)src, rows, K, codes, scales, (hipStream_t)stream);
 }
 
+int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
+                         uint8_t* scales, void* stream) {
+  if (batch < 0 || rows <= 0 || cols <= 0 || rows % 32) return MOE_ERR_INVALID_ARG;
+  if (batch > 65535 || rows / 32 > 65535 || cols > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if (batch == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(k_mx_quant_t, dim3((unsigned)cdiv((int)cols, kThreads), (unsigned)(rows / 32), (unsigned)batch),
+                     dim3(kThreads), 0, (hipStream_t)stream, (const bf16_t*)src, codes, scales, (int)rows,
+                     (int)cols);
+  return launch_status();
+}
+
 static int forward_call(const Plan& p, const moe_desc* desc, const void* x, const void* wr, const float* bias,
                         const moe_weights* w, void* y, const moe_saved* saved, void* workspace, hipStream_t st) {
   Fwd F = make_fwd(p, desc, workspace, saved);
@@ -897,6 +966,7 @@ int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_
   if (!p.bwd_ok) return MOE_ERR_UNSUPPORTED;
   if (!w || !saved) return MOE_ERR_INVALID_ARG;
   if (!saved->offsets || !dw1 || !dw3 || !dw2 || !w->w1 || !w->w3 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (p.mxfp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
   if (p.T > 0 && (!dy || !x || !dx || !dgate || !saved->gate || !saved->perm || !saved->inv || !saved->a ||
                   !saved->b || !saved->h))
     return MOE_ERR_INVALID_ARG;

@@ -36,6 +36,7 @@ struct Plan {
   size_t o_h, o_big1, o_big2, o_dab, o_dgp, o_hs, o_zero, o_gg;
   size_t o_xs;     // MXFP8: x scales (the codes sit at o_big1)
   size_t o_rdz, o_rpart, o_rpbias;  // router backward: dz, dWr and dbias partial sums
+  size_t o_dyq, o_dys, o_dabq, o_dabs;  // MXFP8 backward: dY and [dA | dB] codes and scales
   size_t total;
 };
 

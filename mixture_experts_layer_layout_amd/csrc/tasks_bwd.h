@@ -84,6 +84,20 @@ struct Bwd {
   bf16_t* xp;            // [R, d] X pulled into expert order
   bf16_t* gg;            // [R, d] g_r * dY pulled into expert order
   const bf16_t* zrow;    // >= 2I + d + 256 zeros: the K tail of weight-gradient tiles
+  // MXFP8 data gradients (null / 0 in the bf16 backward): the weights
+  // transposed and quantised along the contraction axis of each product,
+  // the upstream gradient and [dA | dB] quantised along their rows
+  const uint8_t* w1t;    // [E, d, I] codes of W1^T, blocks along I
+  const uint8_t* w3t;    // [E, d, I]
+  const uint8_t* w2t;    // [E, I, d] codes of W2^T, blocks along d
+  const uint8_t* w1ts;   // [E, d, I/32] scale codes
+  const uint8_t* w3ts;
+  const uint8_t* w2ts;   // [E, I, d/32]
+  uint8_t* dyq;          // [T, d] codes of dY
+  uint8_t* dys;          // [T, d/32]
+  uint8_t* dabq;         // [R, 2I] codes of [dA | dB]
+  uint8_t* dabs;         // [R, 2I/32]
+  int mx_wide_d, mx_wide_i;  // scale rows read 4 stages at a time (KRowsMX)
   Sync s;
 };
 
@@ -154,27 +168,21 @@ __device__ void bwd_rowprep(const Bwd& B, int task) {
 }
 
 // ---------------------------------------------------------------- dh
-// dHu = G W2_e for one (row tile, I tile); fused: the dgate partial sum of
-// the tile's columns, dH = g dHu and the SwiGLU backward into [dA | dB].
-__device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float* sred) {
-  typedef TileDH TL;
-  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
-  const int d = B.d, I = B.I;
-  const bf16_t* W2 = B.w2 + (size_t)e * d * I;
+// The dh epilogue of one (row tile, I tile) from the accumulators of dHu:
+// the dgate partial sum of the tile's columns, dH = g dHu and the SwiGLU
+// backward into [dA | dB] (shared by the bf16 and MXFP8 tiles, whose
+// accumulator layouts are the same).
+template <class TL>
+__device__ __forceinline__ void bwd_dh_epilogue(const Bwd& B, f32x16_t (&acc)[TL::MI][TL::NJ], int r0, int n,
+                                                int nt, bf16_t* smem) {
+  const int I = B.I;
   const int c0 = nt * TL::BN;
-  KRows<TL::BM, kDgradAhead> la;
-  // rows past n repeat the last row (their outputs are dropped)
-  la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)B.src[r0 + min(r, n - 1)] * d; });
-  auto lb = kcols_n<TL::BN, kDgradAhead>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
-  f32x16_t acc[TL::MI][TL::NJ];
-  tile_mainloop<TL, kDgradAhead>(d / 64, smem, acc, la, lb);
-
   // dA staged in LDS (dB kept in the accumulators), then dB; the dgate
   // partial sums go through a small LDS area past the staging block
   typedef Staged<TL::BM, TL::BN> St;
   static_assert(St::bytes + 2 * TL::BM * sizeof(float) <= TL::smem_bytes, "dh staging fits the tile's LDS");
   const St st{smem};
-  sred = (float*)(smem + TL::BM * St::LD);
+  float* sred = (float*)(smem + TL::BM * St::LD);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -212,6 +220,22 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
   __syncthreads();
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
   st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + I + c0; });
+}
+
+// dHu = G W2_e for one (row tile, I tile), then the dh epilogue.
+__device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*) {
+  typedef TileDH TL;
+  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const int d = B.d, I = B.I;
+  const bf16_t* W2 = B.w2 + (size_t)e * d * I;
+  const int c0 = nt * TL::BN;
+  KRows<TL::BM, kDgradAhead> la;
+  // rows past n repeat the last row (their outputs are dropped)
+  la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)B.src[r0 + min(r, n - 1)] * d; });
+  auto lb = kcols_n<TL::BN, kDgradAhead>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
+  f32x16_t acc[TL::MI][TL::NJ];
+  tile_mainloop<TL, kDgradAhead>(d / 64, smem, acc, la, lb);
+  bwd_dh_epilogue<TL>(B, acc, r0, n, nt, smem);
 }
 
 // ---------------------------------------------------------------- dxp

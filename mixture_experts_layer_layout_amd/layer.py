@@ -38,6 +38,31 @@ def quantize_mxfp8(t: torch.Tensor):
     return codes, scales
 
 
+def quantize_mxfp8_t(t: torch.Tensor):
+    """E4M3 codes and E8M0 scales of the transpose of each matrix of t
+    ([batch, rows, cols] -> [batch, cols, rows], blocks along rows), by the
+    library's kernel."""
+    t = t.contiguous()
+    rows, cols = t.shape[-2], t.shape[-1]
+    codes = torch.empty(t.shape[:-2] + (cols, rows), dtype=torch.uint8, device=t.device)
+    scales = torch.empty(t.shape[:-2] + (cols, rows // 32), dtype=torch.uint8, device=t.device)
+    api.moe_quantize_mxfp8_t(t, codes, scales)
+    return codes, scales
+
+
+def backward_weights_of(w, inp):
+    """moe_weights for moe_backward: the bf16 weights, or for MXFP8 experts
+    the transposed weights quantised along the data gradients' contraction
+    axes (kept alive in the returned dict)."""
+    if w.experts == "mxfp8":
+        keep = {}
+        for n in ("w1", "w3", "w2"):
+            keep[n], keep[n + "_scale"] = quantize_mxfp8_t(inp[n])
+        return api.make_weights(keep["w1"], keep["w3"], keep["w2"], keep["w1_scale"],
+                                keep["w3_scale"], keep["w2_scale"]), keep
+    return api.make_weights(inp["w1"], inp["w3"], inp["w2"]), {}
+
+
 def weights_of(w, inp):
     """moe_weights for the workload (MXFP8 weights are quantised first and
     kept alive in the returned dict)."""
@@ -100,7 +125,7 @@ def backward(w, inp, saved, fused=True, ws=None, flags=0, n_workgroups=0, weight
     T = inp["x"].shape[0]
     d = desc_for(w, fused, 0, n_workgroups, flags, T=T)
     if weights is None:
-        weights, keep = weights_of(w, inp)
+        weights, keep = backward_weights_of(w, inp)
     if ws is None:
         ws = workspace(d, dev)
     act = _ACT[w.act]

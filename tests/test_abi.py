@@ -152,3 +152,26 @@ def test_status_strings(lib):
         s = lib.moe_status_string(code).decode()
         assert s.startswith("MOE_")
     assert "unknown" in lib.moe_status_string(-99).decode()
+
+
+def test_mxfp8_backward_and_transposed_quantise_validate_on_the_host(lib):
+    vp = ctypes.c_void_p
+    lib.moe_quantize_mxfp8_t.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+    assert lib.moe_quantize_mxfp8_t(None, 1, 48, 64, None, None, None) == -1       # rows % 32
+    assert lib.moe_quantize_mxfp8_t(None, 1, 64, 0, None, None, None) == -1
+    assert lib.moe_quantize_mxfp8_t(None, 70000, 64, 64, None, None, None) == -2    # grid z
+    assert lib.moe_quantize_mxfp8_t(None, 0, 64, 64, None, None, None) == 0         # empty batch
+    assert lib.moe_quantize_mxfp8_t(None, 1, 64, 64, None, None, None) == -1        # null buffers
+    # the MXFP8 backward needs the transposed weights' scales
+    lib.moe_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    dummy = ctypes.c_void_p(256)
+    w = (ctypes.c_void_p * 6)(dummy, dummy, dummy, None, None, None)
+    saved = (ctypes.c_void_p * 11)(*([dummy] * 11))
+    mx = _desc(T=0, d=256, E=8, k=2, I=128, expert_dtype=2)
+    assert lib.moe_backward(ctypes.byref(mx), None, None, ctypes.byref(w), ctypes.byref(saved), None,
+                            dummy, dummy, dummy, None, None, 0, None) == -1
+    w2 = (ctypes.c_void_p * 6)(*([dummy] * 6))
+    # with the scales present the next check is the workspace
+    assert lib.moe_backward(ctypes.byref(mx), None, None, ctypes.byref(w2), ctypes.byref(saved), None,
+                            dummy, dummy, dummy, None, None, 0, None) == -3
