@@ -100,7 +100,9 @@ def algorithmic_bytes(w, counts, part):
     saved = 3 * w.R * w.I * es if w.backward else 0
     if part == "forward":
         return wbytes + 2 * tok + w.E * w.d * es + saved + w.T * w.E * 4 + small
-    return 2 * wbytes + 3 * tok + saved + w.R * 4 + small
+    # the weight gradients are written in the activation type
+    gbytes = int(active * 3 * w.I * w.d * es)
+    return wbytes + gbytes + 3 * tok + saved + w.R * 4 + small
 
 
 def expert_flops(w, part):
@@ -155,6 +157,7 @@ def cpu_baseline(w, inp_cpu, w_gpu, budget_s=15.0):
     return {"value": w.T * frac / secs, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"fp64 numpy oracle: routing+layout{'+quantisation' if mx else ''} of all "
+                       f"{'(backward data gradients unquantised) ' if mx and w.backward else ''}"
                        f"{w.T} tokens, expert "
                        f"{'forward+backward' if w.backward else 'forward'} of experts 0..{n_exp - 1} "
                        f"({rows_done} of {w.R} routed rows), scaled by rows")}
@@ -229,6 +232,9 @@ def main():
 
     fused = not args.unfused
     weights, keep = layer.weights_of(w, dev)
+    # the backward's weights (MXFP8: transposed, quantised along its
+    # contraction axes, once per weight update and outside the step)
+    bweights, bkeep = layer.backward_weights_of(w, dev) if w.backward else (None, {})
     saved = layer.alloc_saved(w, "cuda", full=w.backward)
     desc = layer.desc_for(w, fused=fused, stage_rows=args.stage_rows, flags=args.flags,
                           n_workgroups=args.workgroups)
@@ -250,7 +256,7 @@ def main():
         api.moe_forward(desc, dev["x"], dev["wr"], dev["bias"], weights, y, sv, ws, stream)
 
     def bwd():
-        api.moe_backward(bdesc, dev["dy"], dev["x"], weights, sv, grads["dx"], grads["dw1"],
+        api.moe_backward(bdesc, dev["dy"], dev["x"], bweights, sv, grads["dx"], grads["dw1"],
                          grads["dw3"], grads["dw2"], grads["dgate"], bws, stream)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -339,6 +345,8 @@ def main():
     part = "backward" if w.backward else "forward"
     kern_ms = bwd_ms if w.backward else fwd_ms
     kname = ("k_fused_bwd" if w.backward else "k_fused_fwd") if fused else ("moe_backward" if w.backward else "moe_forward")
+    if w.backward and w.experts == "mxfp8":
+        kname = "moe_backward"   # the MXFP8 backward runs as ordinary grids
     abytes = algorithmic_bytes(w, counts, part)
     achieved = abytes / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

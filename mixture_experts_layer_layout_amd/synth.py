@@ -12,6 +12,8 @@ Workloads (sizes from the MoE shapes the method is measured on):
   dsv3-mxfp8         T=8192, otherwise as dsv3-bf16, expert GEMMs in MXFP8
   dsv3-fwdbwd-zipf   as dsv3-bf16 plus a router bias giving Zipf(1.2) expert
                      loads, and an upstream gradient dY for the backward
+  dsv3-fwdbwd-zipf-mxfp8  the same with the expert GEMMs in MXFP8 (forward,
+                     and the backward's data gradients)
   dsv3-ep8-share     one GPU's share of the DeepSeek-V3 layer split 8 ways by
                      expert: E=32 local experts, ~1024 rows each (a
                      matrix-core-bound shape; not one of the five parity
@@ -98,6 +100,9 @@ WORKLOADS = {
                            experts="mxfp8"),
     "dsv3-fwdbwd-zipf": Workload("dsv3-fwdbwd-zipf", T=4096, d=7168, E=256,
                                  k=8, I=2048, zipf_s=1.2, backward=True),
+    "dsv3-fwdbwd-zipf-mxfp8": Workload("dsv3-fwdbwd-zipf-mxfp8", T=4096, d=7168, E=256,
+                                       k=8, I=2048, zipf_s=1.2, backward=True,
+                                       experts="mxfp8"),
     "dsv3-ep8-share": Workload("dsv3-ep8-share", T=4096, d=7168, E=32, k=8,
                                I=2048),
 }
