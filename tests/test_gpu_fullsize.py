@@ -180,3 +180,47 @@ def test_fullsize_router_backward():
     print(f"  dlogits {e1:.2e} dbias {e2:.2e} dwr {e3:.2e} dx {e4:.2e}", flush=True)
     assert e1 <= 1e-5 and e2 <= 1e-5
     assert e3 <= 1e-2 and e4 <= 1e-2
+
+
+def test_fullsize_mxfp8_backward():
+    """dsv3-fwdbwd-zipf-mxfp8 at full size (MXFP8 forward, MXFP8 data
+    gradients, bf16 weight gradients), as bench.py runs it: routing exact;
+    dX and dgate of one sampled token against the oracle's MXFP8 forward and
+    backward over that token alone (its rows depend on nothing else); dW2 of
+    the least-loaded expert, which takes no quantised operand, against the
+    oracle's per-expert backward given the oracle's MXFP8 H."""
+    from oracle import mxfp8 as Q
+    w = synth.WORKLOADS["dsv3-fwdbwd-zipf-mxfp8"]
+    print(f"\nfull-size {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}", flush=True)
+    inp, dev = full_inputs(w, 0)
+    y, sv = layer.forward(w, dev, fused=True)
+    g = layer.backward(w, dev, sv, fused=True)
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    x = host(inp["x"])
+    wr = host(inp["wr"])
+    dy = host(inp["dy"])
+    bias = None if inp["bias"] is None else inp["bias"].numpy()
+    logits = sv["logits"].cpu().numpy()
+    idx, gate = M.route(logits, w.k, w.score, w.renorm, bias)
+    assert np.array_equal(host(sv["topk_idx"]), idx)
+    counts, offsets, perm, inv, src = M.layout(idx, w.E)
+    assert np.array_equal(host(sv["perm"]), perm)
+    W1, W3, W2 = (DeviceExperts(dev[n]) for n in ("w1", "w3", "w2"))
+    ts = np.array([w.T // 3])
+    f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts])
+    b = Q.backward_mxfp8(dy[ts], x[ts], f, W1, W3, W2, w.k)
+    for n in ("dx", "dgate"):
+        e2 = (dgate_err if n == "dgate" else row_rel_err)(host(g[n])[ts], b[n])
+        print(f"  {n} sampled max row-rel err {e2:.2e}", flush=True)
+        assert e2 <= 6e-2, n
+    e = int(np.argsort(counts, kind="stable")[np.count_nonzero(counts == 0)])   # least-loaded with rows
+    lo, hi = int(offsets[e]), int(offsets[e + 1])
+    rows = src[lo:hi]
+    # the oracle's MXFP8 H of expert e's rows (x quantised along d, W1/W3 along d)
+    _, _, H_e, _ = Q.expert_ffn_mxfp8(Q.fake_quant(x[rows]), W1[e], W3[e], W2[e])
+    g_row = gate.reshape(-1)[perm][lo:hi]
+    dw2 = (g_row[:, None] * dy[rows]).T @ H_e
+    e3 = row_rel_err(host(g["dw2"][e]).reshape(1, -1), dw2.reshape(1, -1))
+    print(f"  dw2[{e}] ({hi - lo} rows) rel err {e3:.2e}", flush=True)
+    assert e3 <= 6e-2
