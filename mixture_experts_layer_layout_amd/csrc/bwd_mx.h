@@ -22,33 +22,32 @@
 namespace moe {
 
 // Rows of codes with k contiguous whose K range is two stored rows: stages
-// kt < split from lo(r), the rest from hi(r) (the W1^T and W3^T halves of
-// one output column of dXp).
+// kt < split from row r of lo, the rest from row r of hi (the W1^T and W3^T
+// halves of one output column of dXp).  Both are matrices of `ld` bf16
+// units a row, so the switch is one offset per stage.  (Laid out like
+// KRows, row pointers then the register buffers: with one base pointer and
+// a row stride instead, the compiler kept one buffer in scratch memory.)
 template <int ROWS>
 struct KRowsSplit {
   static constexpr int PER = ROWS / 32;
-  const bf16_t* lo[PER];
-  const bf16_t* hi[PER];
-  int split;
+  const bf16_t* row[PER];
   uint4 v[kPrefetch][PER];
-  template <class F, class G>
-  __device__ __forceinline__ void init(F plo, G phi, int split_stage) {
+  ptrdiff_t dhi;
+  int split;
+  __device__ __forceinline__ void init(const bf16_t* lo, const bf16_t* hi, int ld_, int split_stage) {
     const int r0 = threadIdx.x >> 3;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      lo[i] = plo(r0 + 32 * i);
-      hi[i] = phi(r0 + 32 * i);
-    }
+    for (int i = 0; i < PER; ++i) row[i] = lo + (size_t)(r0 + 32 * i) * ld_;
+    dhi = ((const char*)hi - (const char*)lo) / (ptrdiff_t)sizeof(bf16_t) - (ptrdiff_t)split_stage * 64;
     split = split_stage;
   }
   __device__ __forceinline__ void prep(int) {}
   template <int BUF>
   __device__ __forceinline__ void load(int kt) {
     const int ch = threadIdx.x & 7;
-    const bool second = kt >= split;
-    const int ks = second ? kt - split : kt;
+    const ptrdiff_t off = (ptrdiff_t)kt * 64 + (kt >= split ? dhi : 0) + ch * 8;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) v[BUF][i] = *(const uint4*)((second ? hi[i] : lo[i]) + ks * 64 + ch * 8);
+    for (int i = 0; i < PER; ++i) v[BUF][i] = *(const uint4*)(row[i] + off);
   }
   template <int BUF, bool HI>
   __device__ __forceinline__ void store(bf16_t* lds) const {
@@ -67,10 +66,10 @@ struct KRowsMXSplit {
   static_assert(ROWS + BROWS == kThreads, "one scale row per thread");
   KRows<ROWS> codes;
   const uint32_t* slo;
-  const uint32_t* shi;
+  ptrdiff_t dhi;  // second row - first row - split, in words (0 for A rows)
   int split;
   uint32_t sv[kPrefetch];
-  uint4 s4;
+  uint32_t s0, s1, s2, s3;  // words of stages 4g .. 4g+3 (wide rows)
   bool wide;
   // wide: every scale row 16-byte aligned and split % 4 == 0
   template <class F, class GA, class GL, class GH>
@@ -80,10 +79,10 @@ struct KRowsMXSplit {
     const int t = threadIdx.x;
     if (t < ROWS) {
       slo = (const uint32_t*)ascale(t);
-      shi = slo + split_stage;
+      dhi = 0;
     } else {
       slo = (const uint32_t*)bscale_lo(t - ROWS);
-      shi = (const uint32_t*)bscale_hi(t - ROWS);
+      dhi = ((const char*)bscale_hi(t - ROWS) - (const char*)slo) / 4 - split_stage;
     }
     split = split_stage;
     wide = wide_rows;
@@ -92,12 +91,18 @@ struct KRowsMXSplit {
   template <int BUF>
   __device__ __forceinline__ void load(int kt) {
     codes.template load<BUF>(kt);
-    const bool second = kt >= split;
-    const uint32_t* p = second ? shi + (kt - split) : slo + kt;
+    const uint32_t* p = slo + kt + (kt >= split ? dhi : 0);
     if (wide) {
+      // word q of the 4 held: two levels of selects (a chain of four
+      // compares became an indexed stack load here)
       const int q = kt & 3;
-      if (q == 0) s4 = *(const uint4*)p;
-      sv[BUF] = q == 0 ? s4.x : q == 1 ? s4.y : q == 2 ? s4.z : s4.w;
+      if (q == 0) {
+        const uint4 u = *(const uint4*)p;
+        s0 = u.x; s1 = u.y; s2 = u.z; s3 = u.w;
+      }
+      const uint32_t w01 = (q & 1) ? s1 : s0;
+      const uint32_t w23 = (q & 1) ? s3 : s2;
+      sv[BUF] = (q & 2) ? w23 : w01;
     } else {
       sv[BUF] = *p;
     }
@@ -148,8 +153,7 @@ __device__ void bwd_dxp_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
           [&](int r) { return B.dabs + (size_t)(r0 + min(r, n - 1)) * (I2 / 32); },
           [&](int nr) { return S1 + (size_t)(c0 + nr) * is; }, [&](int nr) { return S3 + (size_t)(c0 + nr) * is; },
           split, B.mx_wide_i != 0);
-  lb.init([&](int nr) { return (const bf16_t*)(W1 + (size_t)(c0 + nr) * I); },
-          [&](int nr) { return (const bf16_t*)(W3 + (size_t)(c0 + nr) * I); }, split);
+  lb.init((const bf16_t*)(W1 + (size_t)c0 * I), (const bf16_t*)(W3 + (size_t)c0 * I), I / 2, split);
   f32x16_t acc[TL::MI][TL::NJ];
   tile_mainloop<TL>(I2 / 128, smem, acc, la, lb);
   const Staged<TL::BM, TL::BN> st{smem};
