@@ -290,8 +290,10 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
  * with w1_scale, w3_scale [E, d, I/32]; w2 the codes of W2^T [E, I, d] with
  * w2_scale [E, I, d/32] (all required).  dY and [dA | dB] are quantised
  * along their rows inside the call; the weight gradients, dX's gather-sum
- * and dgate take the bf16 operands as in the bf16 backward.  This variant
- * runs every phase as an ordinary grid whatever desc->fused says. */
+ * and dgate take the bf16 operands as in the bf16 backward.  With
+ * desc->fused = 1 this variant runs one persistent launch per phase (the
+ * MOE_FLAG_PERSISTENT_SINGLE and _WGRAD_APART flags do not apply to it),
+ * with the two quantisations as plain launches between them. */
 MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
                  const moe_weights* w, const moe_saved* saved, void* dx,
                  void* dw1, void* dw3, void* dw2, float* dgate,

@@ -487,7 +487,8 @@ constexpr int bwd_occupancy(unsigned mask) {
   return mask == 0x7Fu || mask == 0x57u || mask == 0x28u ? 1 : 2;
 }
 
-template <unsigned MASK>
+// MX: the dh and dxp tasks take the MXFP8 tiles (bwd_mx.h).
+template <unsigned MASK, bool MX = false>
 __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   __shared__ Claim c;
@@ -553,7 +554,10 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       if (t >= s_nmt * B.nNdh) continue;
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdh, t, tile, nt);
-      bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
+      if constexpr (MX)
+        bwd_dh_tile_mx(B, tile, nt, (bf16_t*)smem);
+      else
+        bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
       // dA|dB and the dgate partials are read by dxp, dw13 and dx; the
       // first signal publishes them, the second has nothing new to publish
       signal_add<(MASK & 0x70u) != 0>(&B.s.h_cnt[tile], 1);
@@ -562,7 +566,12 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       if (t >= s_nmt * B.nNdx) continue;
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdx, t, tile, nt);
-      if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
+      if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) {
+        if constexpr (MX)
+          bwd_dxp_tile_mx(B, tile, nt, (bf16_t*)smem);
+        else
+          bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
+      }
       signal_add<(MASK & 64u) != 0>(B.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(B.s.g2_done, s_nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
@@ -615,12 +624,12 @@ static int launch_fused_fwd(const moe_desc* D, const Fwd& F, size_t smem, hipStr
   return launch_status();
 }
 
-template <unsigned MASK>
+template <unsigned MASK, bool MX = false>
 static int launch_fused_bwd(const moe_desc* D, const Bwd& B, size_t smem, hipStream_t st) {
-  if (!set_smem(k_fused_bwd<MASK>, smem)) return MOE_ERR_HIP;
-  const int n_wg = persistent_grid(k_fused_bwd<MASK>, smem, D->n_workgroups);
+  if (!set_smem(k_fused_bwd<MASK, MX>, smem)) return MOE_ERR_HIP;
+  const int n_wg = persistent_grid(k_fused_bwd<MASK, MX>, smem, D->n_workgroups);
   if (n_wg <= 0) return MOE_ERR_HIP;
-  hipLaunchKernelGGL(k_fused_bwd<MASK>, dim3(n_wg), dim3(256), smem, st, B);
+  hipLaunchKernelGGL((k_fused_bwd<MASK, MX>), dim3(n_wg), dim3(256), smem, st, B);
   return launch_status();
 }
 
@@ -706,8 +715,10 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   // weight-gradient tiles: their main loop's LDS plus the store staging
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes + kWgradStageBytes;
   if (p.mxfp8) {
-    // MXFP8 data gradients: every phase as an ordinary grid, with the two
-    // quantisations (dY before dh, [dA | dB] after it) in between
+    // MXFP8 data gradients: the phases of the bf16 backward (persistent
+    // launches, one per phase, or ordinary grids), with dh and dxp on the
+    // MXFP8 tiles and the two quantisations (dY before dh, [dA | dB] after
+    // it) as plain launches in between
     B.w1t = (const uint8_t*)w->w1; B.w3t = (const uint8_t*)w->w3; B.w2t = (const uint8_t*)w->w2;
     B.w1ts = w->w1_scale; B.w3ts = w->w3_scale; B.w2ts = w->w2_scale;
     B.dyq = at<uint8_t>(ws, p.o_dyq); B.dys = at<uint8_t>(ws, p.o_dys);
@@ -716,6 +727,20 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     B.mx_wide_d = p.d % 512 == 0 && al16(B.dys) && al16(B.w2ts);
     B.mx_wide_i = p.I % 512 == 0 && al16(B.dabs) && al16(B.w1ts) && al16(B.w3ts);
     const size_t sm_mx = TileMX128::smem_bytes;
+    static_assert(2 * (TileMX128::smem_bytes + 1024) <= 160 * 1024, "two MXFP8 workgroups per CU");
+    if (D->fused) {
+      const size_t sm_setup = (2 * kMaxE + 16) * sizeof(int);
+      int rc = p.R > 0 ? mxfp8_quantize_rows(B.dy, p.T, p.d, B.dyq, B.dys, st) : MOE_OK;
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x03u>(D, B, sm_setup, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x04u, true>(D, B, sm_mx, st);
+      if (rc == MOE_OK && p.R > 0) rc = mxfp8_quantize_rows(B.dab, p.R, 2 * (int64_t)p.I, B.dabq, B.dabs, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x10u, true>(D, B, sm_mx, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
+      if (rc != MOE_OK) return rc;
+      if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
+      return launch_status();
+    }
     if (!set_smem(k_bwd_dh_mx, sm_mx) || !set_smem(k_bwd_dxp_mx, sm_mx) || !set_smem(k_bwd_dw2, sm_dw) ||
         !set_smem(k_bwd_dw13, sm_dw))
       return MOE_ERR_HIP;

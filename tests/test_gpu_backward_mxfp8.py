@@ -88,6 +88,20 @@ def test_backward_mxfp8_matches_oracle(name):
         assert e <= MX_TOL, f"{n} max row-relative error {e:.3e} > {MX_TOL}"
 
 
+def test_backward_mxfp8_persistent_equals_plain_bitwise():
+    # the persistent launches and the ordinary grids run the same tiles
+    w = SMALL["wide-mx"]
+    inp = synth.make_inputs(w, 6, with_dy=True)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    y, sv = layer.forward(w, dev, fused=True)
+    g1 = layer.backward(w, dev, sv, fused=True)
+    g2 = layer.backward(w, dev, sv, fused=False)
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
+
+
 def test_backward_mxfp8_repeatable_and_empty():
     w = SMALL["dsv3-mx-small"]
     inp = synth.make_inputs(w, 5, with_dy=True)
