@@ -345,8 +345,6 @@ def main():
     part = "backward" if w.backward else "forward"
     kern_ms = bwd_ms if w.backward else fwd_ms
     kname = ("k_fused_bwd" if w.backward else "k_fused_fwd") if fused else ("moe_backward" if w.backward else "moe_forward")
-    if w.backward and w.experts == "mxfp8":
-        kname = "moe_backward"   # the MXFP8 backward runs as ordinary grids
     abytes = algorithmic_bytes(w, counts, part)
     achieved = abytes / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
