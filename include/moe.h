@@ -270,7 +270,7 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
 
 /* Backward of the expert path with the routing frozen (MoK flash §01/§02:
  * pull reverse-combine, expert dgrad and wgrad, push reverse-dispatch).
- * bf16 only.
+ * bf16 activations; bf16 or MXFP8 experts (below).
  *   dy    act [T, d] upstream gradient;  x act [T, d] the forward input;
  *   saved the forward's gate, offsets, perm, inv, a, b, h;
  *   dx    act [T, d] output, gradient through the experts only;
