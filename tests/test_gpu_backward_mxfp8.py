@@ -102,6 +102,23 @@ def test_backward_mxfp8_persistent_equals_plain_bitwise():
         assert torch.equal(g1[n], g2[n]), n
 
 
+@pytest.mark.parametrize("n_wg", [1, 7, 1000])
+def test_backward_mxfp8_any_grid_bitwise(n_wg):
+    # the persistent launches with any number of workgroups (one workgroup
+    # runs every task in ticket order, so every wait is on work already
+    # claimed) give the default grid's bits
+    w = SMALL["dsv3-mx-small"]
+    inp = synth.make_inputs(w, 8, with_dy=True)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    y, sv = layer.forward(w, dev, fused=True)
+    g1 = layer.backward(w, dev, sv, fused=True)
+    g2 = layer.backward(w, dev, sv, fused=True, n_workgroups=n_wg)
+    torch.cuda.synchronize()
+    assert sv["status"].item() == 0
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
+
+
 def test_backward_mxfp8_repeatable_and_empty():
     w = SMALL["dsv3-mx-small"]
     inp = synth.make_inputs(w, 5, with_dy=True)
