@@ -165,6 +165,12 @@ def fake_quant(v):
     return out.reshape(v.shape)
 
 
+def quantize_tokens(x):
+    """The dispatch's quantisation: every token row of x [T, d] in blocks of
+    32 along d (the up projection's contraction axis), fp64 values."""
+    return fake_quant(np.asarray(x, dtype=np.float64))
+
+
 def expert_ffn_mxfp8(xq_rows, w1, w3, w2):
     """One expert's SwiGLU FFN on rows that are already quantised (xq_rows,
     fp64 values of MXFP8 codes): W1/W3 quantised along d and W2 along I
@@ -197,7 +203,7 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
         logits = M.router_logits(x, wr, None)
     idx, gate = M.route(logits, k, score, renorm, bias)
     counts, offsets, perm, inv, src = M.layout(idx, E)
-    xq = fake_quant(np.asarray(x, dtype=np.float64))   # per token along d
+    xq = quantize_tokens(x)                          # per token along d
     xp = xq[src]
     I = np.shape(w1)[1]
     d = np.shape(w1)[2]
