@@ -14,16 +14,24 @@ run first; then exactly K steps are timed between two device
 synchronisations.  Rank 0 prints one JSON line.
 
 The line carries
-  roofline      the dominant kernel (the one persistent launch of the
-                backward when the step has one, else of the forward):
-                algorithmic bytes per launch over its average duration
-                measured with HIP events on the stream it runs on, against
-                the MI355X HBM peak; ``traffic`` is the HBM byte count read
+  roofline      the dominant unit (the backward call when the step has
+                one, else the forward call), timed with HIP events on the
+                stream it runs on, against the roofline that bounds it: for
+                a unit whose algorithmic intensity (expert FLOPs per
+                algorithmic byte) is below the matrix cores' balance point
+                the HBM peak (algorithmic bytes / duration), above it the
+                dense matrix-core peak of the GEMMs' operand type (expert
+                FLOPs / duration); ``traffic`` is the HBM byte count read
                 from the committed counter summary when that summary was
                 taken on the current kernel sources, else null
   cpu_baseline  the CPU oracle timed on the host cores over a bounded
                 sample of the same workload (the rows of the first experts,
                 routing and layout over all tokens), scaled to tokens/s
+  phases        forward / backward times, the step timed again with a
+                512 MB buffer written between steps (so no input of a step
+                sits in the caches; ``step_ms_flushed``), the standalone
+                layout and gathers, and for MXFP8 experts the weight
+                quantisation a weight update costs (outside the step)
 """
 from __future__ import annotations
 
@@ -285,6 +293,35 @@ def main():
     if saved["status"].item() != 0:
         raise RuntimeError("device status " + api.moe_status_string(saved["status"].item()))
 
+    # the step again with a 512 MB buffer written before each step (outside
+    # the events), so no input of the step is left in the L2s or the MALL
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fl_ms = []
+    for _ in range(min(args.steps, 5)):
+        flush.zero_()
+        a, b = ev(), ev()
+        a.record(stream)
+        fwd()
+        if w.backward:
+            bwd()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl_ms.append(a.elapsed_time(b))
+    del flush
+    # MXFP8 experts: the weight quantisation one weight update costs (the
+    # forward's three weights along their contraction axes, and for a
+    # backward the three transposed ones), timed on the same stream
+    quant_ms = None
+    if w.experts == "mxfp8":
+        a, b = ev(), ev()
+        a.record(stream)
+        layer.weights_of(w, dev)
+        if w.backward:
+            layer.backward_weights_of(w, dev)
+        b.record(stream)
+        torch.cuda.synchronize()
+        quant_ms = a.elapsed_time(b)
+
     # the standalone layout and gather (moe_layout, moe_gather: token-major
     # by inv, and the pull by perm) on this step's routing, timed with events
     # on the same stream
@@ -346,10 +383,20 @@ def main():
     kern_ms = bwd_ms if w.backward else fwd_ms
     kname = ("k_fused_bwd" if w.backward else "k_fused_fwd") if fused else ("moe_backward" if w.backward else "moe_forward")
     abytes = algorithmic_bytes(w, counts, part)
-    achieved = abytes / (kern_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(kname, w.name),
-            "kernel": kname, "algorithmic_bytes": abytes, "avg_ms": round(kern_ms, 4)}
+    aflops = expert_flops(w, part)
+    mfma_peak = MFMA_PEAK_TFS[w.experts]
+    # the roofline that bounds the unit: matrix cores when its intensity
+    # exceeds their balance point (peak FLOP/s over peak bytes/s)
+    if aflops / abytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = aflops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / mfma_peak, 4)}
+    else:
+        achieved = abytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": read_traffic(kname, w.name), "kernel": kname, "algorithmic_bytes": abytes,
+                 "algorithmic_flops": aflops, "avg_ms": round(kern_ms, 4)})
     phases = {"forward_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
               "forward_expert_tflops": round(expert_flops(w, "forward") / (fwd_ms * 1e-3) / 1e12, 1),
               "forward_mfma_util": round(expert_flops(w, "forward") / (fwd_ms * 1e-3) / 1e12
@@ -357,6 +404,10 @@ def main():
               "forward_hbm_frac": round(algorithmic_bytes(w, counts, "forward") / (fwd_ms * 1e-3) / 1e9
                                         / HBM_PEAK_GBS, 4),
               "workspace_mb": round(ws.numel() / 1e6, 1)}
+    phases["step_ms_flushed"] = round(sum(fl_ms) / len(fl_ms), 4)
+    if quant_ms is not None:
+        phases["weight_quant_ms_per_update"] = round(quant_ms, 4)
+        phases["tokens_s_with_quant_every_step"] = round(w.T / ((ms_step + quant_ms) * 1e-3), 1)
     phases["max_rows_per_expert"] = int(counts.max())
     phases["min_rows_per_expert"] = int(counts.min())
     if side:

@@ -137,6 +137,18 @@ typedef struct moe_desc {
 #define MOE_FLAG_SPIN_LIMIT_TINY 0x100u /* test only: bounded waits give up
                                       after a few polls (exercises the
                                       MOE_ERR_TIMEOUT path)                 */
+#define MOE_FLAG_TEST_DROP_READY 0x200u /* test only, fused forward: the
+                                      gather of row tile 0 does not raise
+                                      its ready counter, so the waits on it
+                                      expire: the call records
+                                      MOE_ERR_TIMEOUT, every workgroup
+                                      drains its queues and exits, and y is
+                                      undefined                            */
+#define MOE_FLAG_TEST_SHUFFLE_CLAIMS 0x400u /* test only, fused calls:
+                                      workgroups start claiming on a
+                                      sub-queue hashed from their id instead
+                                      of their XCD's (another claim order;
+                                      results are unchanged)               */
 
 /* Expert weights, in output-major order (row n of a matrix is output
  * feature n, contiguous along the contraction axis):

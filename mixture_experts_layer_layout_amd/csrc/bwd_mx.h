@@ -118,7 +118,9 @@ struct KRowsMXSplit {
 // dHu = G W2_e in MXFP8 for one (row tile, I tile), then the dh epilogue.
 __device__ void bwd_dh_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
   typedef TileMX128 TL;
-  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const TileRows tr = bwd_tile(B, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = B.d, I = B.I, ds = d / 32;
   const uint8_t* W = B.w2t + (size_t)e * I * d;
   const uint8_t* S = B.w2ts + (size_t)e * I * ds;
@@ -126,8 +128,8 @@ __device__ void bwd_dh_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
   KRowsMX<TL::BM, TL::BN> la;
   KRows<TL::BN> lb;
   // rows past n repeat the last row (their outputs are dropped)
-  la.init([&](int r) { return B.dyq + (size_t)B.src[r0 + min(r, n - 1)] * d; },
-          [&](int r) { return B.dys + (size_t)B.src[r0 + min(r, n - 1)] * ds; },
+  la.init([&](int r) { return B.dyq + (size_t)clamp_token(B.src[r0 + min(r, n - 1)], B.T) * d; },
+          [&](int r) { return B.dys + (size_t)clamp_token(B.src[r0 + min(r, n - 1)], B.T) * ds; },
           [&](int nr) { return S + (size_t)(c0 + nr) * ds; }, B.mx_wide_d != 0);
   lb.init([&](int nr) { return (const bf16_t*)(W + (size_t)(c0 + nr) * d); });
   f32x16_t acc[TL::MI][TL::NJ];
@@ -139,7 +141,9 @@ __device__ void bwd_dh_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
 // the first I from W1_e^T, the rest from W3_e^T.
 __device__ void bwd_dxp_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
   typedef TileMX128 TL;
-  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const TileRows tr = bwd_tile(B, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = B.d, I = B.I, I2 = 2 * I, is = I / 32;
   const uint8_t* W1 = B.w1t + (size_t)e * d * I;
   const uint8_t* W3 = B.w3t + (size_t)e * d * I;

@@ -7,6 +7,10 @@
 
 #include "../../include/moe.h"
 
+#define MOE_PROTO_FN __host__ __device__ __forceinline__
+#include "protocol.h"
+#include "slots.h"
+
 namespace moe {
 
 typedef uint16_t bf16_t;  // bfloat16 bits
@@ -93,43 +97,42 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 //   consumer  thread 0 polls the counter with relaxed agent-scope atomic
 //             loads (coherent, no cache maintenance) and the workgroup
 //             proceeds behind a workgroup-scope acquire
-// The consumer invalidates no cache: every exchanged buffer in the
-// workspace is written once per launch and read only after its counter
-// shows it complete, so no L1 or L2 can hold an older copy of it from this
-// launch, and the dispatch's own acquire leaves none from earlier launches.
-// (An agent-scope acquire would invalidate the whole XCD's L2 every time,
-// destroying the reuse of the operand rows other workgroups share there.)
-// Every wait is bounded: when the bound expires, or another workgroup has
-// aborted, it records MOE_ERR_TIMEOUT and returns false; `abort` is a
-// workspace word every wait also watches, so one expired wait drains the
-// whole grid instead of hanging it.
-struct WaitCtx {
-  int* abort;
-  int32_t* status;
-  long long spin_limit;
+// The consumer invalidates no cache, so no L1 or L2 may hold a copy of the
+// data it reads that is older than the producer's stores.  That holds when
+// every 128-byte line of an exchanged buffer has one producer task in a
+// launch and is read in that launch only by tasks that waited for that
+// producer: a line read earlier could only have been brought in by a reader
+// of other data on the same line.  So every buffer exchanged inside a launch
+// is laid out with each producer's bytes in lines of their own (row-tile
+// slots of 128-byte multiples, 128-byte aligned row strides and slice
+// strides), and the dispatch's own acquire leaves no copy from earlier
+// launches.  (An agent-scope acquire would invalidate the XCD's whole L2 at
+// every wait, destroying the reuse of the operand rows other workgroups
+// share there.)
+// The claim and wait logic itself is protocol.h, shared with a host model.
+struct DevOps {
+  static __device__ __forceinline__ int load(const int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  static __device__ __forceinline__ int fetch_add(int* p, int v) { return atomicAdd(p, v); }
+  static __device__ __forceinline__ void store(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  static __device__ __forceinline__ void set_status(int32_t* s, int c) {
+    if (s) atomicCAS((int*)s, 0, c);
+  }
+  static __device__ __forceinline__ void pause() { __builtin_amdgcn_s_sleep(2); }
 };
 
-__device__ __forceinline__ int load_relaxed(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+using proto::WaitCtx;
 
-__device__ __forceinline__ void set_status(int32_t* status, int code) {
-  if (status) atomicCAS((int*)status, 0, code);
-}
+__device__ __forceinline__ int load_relaxed(const int* p) { return DevOps::load(p); }
+
+__device__ __forceinline__ void set_status(int32_t* status, int code) { DevOps::set_status(status, code); }
 
 // Thread 0 only: true when *ctr >= target; false on timeout/abort.
 __device__ __forceinline__ bool thread_wait_geq(const int* ctr, int target, const WaitCtx& w) {
-  long long spins = 0;
-  while (load_relaxed(ctr) < target) {
-    if (load_relaxed(w.abort)) return false;
-    if (++spins > w.spin_limit) {
-      set_status(w.status, MOE_ERR_TIMEOUT);
-      __hip_atomic_store(w.abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return true;
+  return proto::wait_geq<DevOps>(ctr, target, w);
 }
 
 // Block-uniform: true when *ctr >= target; false on timeout/abort.

@@ -94,7 +94,10 @@ int make_plan(const moe_desc* D, Plan* p) {
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   p->n_ctr = C_HEADER + kMaxPhases * kXcds + p->nb + 3 * (size_t)p->max_tiles + 2 * (size_t)E + 16;
   p->o_ctr = take(p->n_ctr * 4);
-  p->o_lpart = take((size_t)p->S * T * E * 4);
+  // router slices: each slice starts on a 128-byte line (a top-k task reads
+  // the first rows of every slice while later slices' tasks may still run)
+  p->lstride = slots::router_slice_stride(T, E);
+  p->o_lpart = take((size_t)p->S * p->lstride * 4);
   p->o_topk = take(R * 4);
   p->o_gate = take(R * 4);
   p->o_bmask = take((size_t)p->nb * E * 8);
@@ -107,11 +110,16 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_perm = take(R * 4);
   p->o_inv = take(R * 4);
   p->o_src = take(R * 4);
+  // the forward's source slots, one 128-byte multiple per row tile
+  p->o_tsrc = take(slots::tile_slot(p->max_tiles, 0, p->BM, 1) * 4);
   p->o_grow = take(R * 4);
   p->o_etile = take((size_t)(E + 1) * 4);
+  p->o_eoff = take((size_t)(E + 1) * 4);
   p->o_eorder = take((size_t)E * 4);
   p->o_h = take(R * I * es);
-  p->o_hs = take(R * (I / 32));
+  // MXFP8 H scales by row-tile slot (BM rows of I/32 bytes: a multiple of
+  // 128 bytes per tile, since I % 128 == 0)
+  p->o_hs = take(slots::tile_slot(p->max_tiles, 0, p->BM, I / 32));
   p->o_xs = p->mxfp8 ? take((size_t)T * (d / 32)) : 0;
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
@@ -158,6 +166,7 @@ static Sync make_sync(const Plan& p, void* ws, int32_t* status, uint32_t flags) 
   s.aux2 = q; q += p.E;
   s.status = status;
   s.spin_limit = (flags & MOE_FLAG_SPIN_LIMIT_TINY) ? 64 : (1ll << 22);
+  s.flags = flags;
   return s;
 }
 
@@ -180,6 +189,7 @@ static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved*
   // MXFP8 always pulls token rows from the quantised x (no gathered copy)
   F.direct = p.mxfp8 || ((D->flags & MOE_FLAG_DIRECT_PULL) && !p.f32) ? 1 : 0;
   F.lpart = at<float>(ws, p.o_lpart);
+  F.lstride = p.lstride;
   F.logits = sv ? sv->logits : nullptr;
   F.topk = (sv && sv->topk_idx) ? sv->topk_idx : at<int>(ws, p.o_topk);
   F.gate = (sv && sv->gate) ? sv->gate : at<float>(ws, p.o_gate);
@@ -193,7 +203,7 @@ static Fwd make_fwd(const Plan& p, const moe_desc* D, void* ws, const moe_saved*
   F.etile = at<int>(ws, p.o_etile);
   F.perm = (sv && sv->perm) ? sv->perm : at<int>(ws, p.o_perm);
   F.inv = (sv && sv->inv) ? sv->inv : at<int>(ws, p.o_inv);
-  F.src = at<int>(ws, p.o_src);
+  F.tsrc = at<int>(ws, p.o_tsrc);
   F.grow = nullptr;
   F.xp = at<char>(ws, p.o_big1);
   F.a = sv ? sv->a : nullptr;
@@ -300,8 +310,13 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_g2(Fwd F) {
   run_g2<Act, TL>(F, tile, nt, smem);
 }
 
+// The combine as a plain launch after the persistent ones: nothing to merge
+// once a bounded wait of the call has given up (the rows were not computed).
 template <class Act>
-__global__ void __launch_bounds__(256) k_combine(Fwd F) { combine_tokens<Act>(F, blockIdx.x); }
+__global__ void __launch_bounds__(256) k_combine(Fwd F) {
+  if (load_relaxed(F.s.abort)) return;
+  combine_tokens<Act>(F, blockIdx.x);
+}
 
 // The persistent forward: phases router slices (+ the MXFP8 quantisation
 // of x by token block) | top-k | layout | gather | up-projection tiles |
@@ -320,7 +335,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
   if (threadIdx.x == 0) {
     c.phase = 0;
     c.qoff = 0;
-    c.own = xcc_id();
+    c.own = claim_home(F.s.flags);
     c.nmt = -1;
   }
   for (;;) {
@@ -352,6 +367,8 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
     const WaitCtx W = wctx(F.s);
     const int s_nmt = c.nmt;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // A task whose wait fails (timeout or abort) does no work and raises
+    // no counter (protocol.h).
     if ((MASK & 1u) && ph == 0) {
       if (TL::kMX && t >= F.nb * F.S) {
         quant_tokens(F, t - F.nb * F.S);
@@ -361,10 +378,12 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         signal_add<(MASK & 2u) != 0>(&F.s.r1_cnt[t / F.S], 1);
       }
     } else if ((MASK & 2u) && ph == 1) {
-      if (wait_geq(&F.s.r1_cnt[t / kTopkChunks], F.S, W, &s_flag)) router_topk<true>(F, t, smem);
+      if (!wait_geq(&F.s.r1_cnt[t / kTopkChunks], F.S, W, &s_flag)) continue;
+      router_topk<true>(F, t, smem);
       signal_add<(MASK & 0x4Cu) != 0>(F.s.r2_done, 1);  // read by scan, gather, combine
     } else if ((MASK & 4u) && ph == 2) {
-      if (wait_geq(F.s.r2_done, F.nb * kTopkChunks, W, &s_flag)) layout_scan(F, (int*)smem);
+      if (!wait_geq(F.s.r2_done, F.nb * kTopkChunks, W, &s_flag)) continue;
+      layout_scan(F, (int*)smem);
       signal_add<(MASK & 0x78u) != 0>(F.s.scan_done, 1);
     } else if ((MASK & 8u) && ph == 3) {
       // MXFP8: a row tile is ready once the codes of x are complete too
@@ -377,13 +396,15 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
       if (t >= s_nmt * F.nN1) continue;
       int tile, nt;
       raster_decode(F.etile, F.E, F.nN1, t, tile, nt);
-      if (wait_geq(&F.s.ready[tile], 1, W, &s_flag)) run_g1<Act, TL>(F, tile, nt, smem);
+      if (!wait_geq(&F.s.ready[tile], 1, W, &s_flag)) continue;
+      run_g1<Act, TL>(F, tile, nt, smem);
       signal_add<(MASK & 32u) != 0>(&F.s.h_cnt[tile], 1);
     } else if ((MASK & 32u) && ph == 5) {
       if (t >= s_nmt * F.nN2) continue;
       int tile, nt;
       raster_decode(F.etile, F.E, F.nN2, t, tile, nt);
-      if (wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) run_g2<Act, TL>(F, tile, nt, smem);
+      if (!wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) continue;
+      run_g2<Act, TL>(F, tile, nt, smem);
       signal_add<(MASK & 64u) != 0>(F.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
@@ -396,8 +417,11 @@ template <class Act>
 __global__ void __launch_bounds__(256) k_gather_perm(const Act* __restrict__ x, const int* __restrict__ perm,
                                                      Act* __restrict__ xp, int R, int d, int k) {
   const int nvec = d * (int)sizeof(Act) / 16;
-  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4)
-    wave_copy_row((const uint4*)x + (size_t)(perm[r] / k) * nvec, (uint4*)xp + (size_t)r * nvec, nvec, CopyAsIs());
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < R; r += gridDim.x * 4) {
+    const int a = perm[r];
+    if ((unsigned)a >= (unsigned)R) continue;  // outside [0, R): the row is left unwritten
+    wave_copy_row((const uint4*)x + (size_t)(a / k) * nvec, (uint4*)xp + (size_t)r * nvec, nvec, CopyAsIs());
+  }
 }
 
 // Token-major gather: each wave reads one token row once and writes it to
@@ -473,7 +497,12 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dw13(Bwd B) {
   bwd_dw13_band(B, blockIdx.x / per, blockIdx.x % per, (bf16_t*)smem);
 }
 
-__global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) { bwd_dx_tokens(B, blockIdx.x); }
+// dX as a plain launch after the persistent ones (skipped when a bounded
+// wait of the call gave up: the rows it sums were not computed).
+__global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) {
+  if (load_relaxed(B.s.abort)) return;
+  bwd_dx_tokens(B, blockIdx.x);
+}
 
 // The persistent backward: phases setup | rowprep | dh | dw2 | dxp | dw13
 // | dx through the per-XCD phase queues (dh and dxp tiles in the grouped
@@ -496,7 +525,7 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
   if (threadIdx.x == 0) {
     c.phase = 0;
     c.qoff = 0;
-    c.own = xcc_id();
+    c.own = claim_home(B.s.flags);
     c.nmt = -1;
   }
   for (;;) {
@@ -545,7 +574,7 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       if ((MASK & 8u) && ph == 3) {
         bwd_dw2_band(B, rank, band, (bf16_t*)smem);
       } else if (MASK & 0x20u) {
-        const int e = B.eorder[rank];
+        const int e = min(max(B.eorder[min(rank, B.E - 1)], 0), B.E - 1);
         const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
         if (wait_geq(&B.s.aux1[e], need, W, &s_flag))
           bwd_dw13_band(B, rank, band, (bf16_t*)smem);
@@ -561,17 +590,16 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       // dA|dB and the dgate partials are read by dxp, dw13 and dx; the
       // first signal publishes them, the second has nothing new to publish
       signal_add<(MASK & 0x70u) != 0>(&B.s.h_cnt[tile], 1);
-      signal_add<false>(&B.s.aux1[B.tile_e[tile]], 1);
+      signal_add<false>(&B.s.aux1[bwd_tile(B, tile).e], 1);
     } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * B.nNdx) continue;
       int tile, nt;
       raster_decode(B.etile, B.E, B.nNdx, t, tile, nt);
-      if (wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) {
-        if constexpr (MX)
-          bwd_dxp_tile_mx(B, tile, nt, (bf16_t*)smem);
-        else
-          bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
-      }
+      if (!wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) continue;
+      if constexpr (MX)
+        bwd_dxp_tile_mx(B, tile, nt, (bf16_t*)smem);
+      else
+        bwd_dxp_tile(B, tile, nt, (bf16_t*)smem);
       signal_add<(MASK & 64u) != 0>(B.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(B.s.g2_done, s_nmt * B.nNdx, W, &s_flag)) bwd_dx_tokens(B, t);
@@ -580,16 +608,13 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
 }
 
 // ------------------------------------------------------------------ host
-static int g_num_cus = 0;
-
+// Compute units of the current device, asked on every call (the library
+// keeps no state between calls, and the caller may switch devices).
 static int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    g_num_cus = n;
-  }
-  return g_num_cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
 }
 
 template <class K>
@@ -694,6 +719,7 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   Bwd B;
   memset(&B, 0, sizeof(B));
   B.T = p.T; B.d = p.d; B.E = p.E; B.k = p.k; B.I = p.I; B.R = p.R; B.BM = TileDH::BM;
+  B.max_tiles = p.max_tiles;
   B.nNdh = p.nNdh; B.nNdx = p.nNdx; B.nW2m = p.nW2m; B.nW2n = p.nW2n; B.nW13m = p.nW13m; B.nW13n = p.nW13n;
   B.nRP = p.nRP; B.nC = p.nC;
   B.dy = (const bf16_t*)dy; B.x = (const bf16_t*)x;
@@ -702,7 +728,7 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   B.a = (const bf16_t*)sv->a; B.b = (const bf16_t*)sv->b; B.h = (const bf16_t*)sv->h;
   B.dx = (bf16_t*)dx; B.dw1 = (bf16_t*)dw1; B.dw3 = (bf16_t*)dw3; B.dw2 = (bf16_t*)dw2; B.dgate = dgate;
   B.tile_e = at<int>(ws, p.o_tile_e); B.tile_r0 = at<int>(ws, p.o_tile_r0); B.tile_n = at<int>(ws, p.o_tile_n);
-  B.etile = at<int>(ws, p.o_etile); B.eorder = at<int>(ws, p.o_eorder);
+  B.etile = at<int>(ws, p.o_etile); B.eorder = at<int>(ws, p.o_eorder); B.eoff = at<int>(ws, p.o_eoff);
   B.src = at<int>(ws, p.o_src); B.grow = at<float>(ws, p.o_grow);
   B.dab = at<bf16_t>(ws, p.o_dab); B.dxp = at<bf16_t>(ws, p.o_big2); B.dgp = at<float>(ws, p.o_dgp);
   B.zrow = at<bf16_t>(ws, p.o_zero);

@@ -38,7 +38,9 @@ __device__ void quant_tokens(const Fwd& F, int tb) {
 template <class TL>
 __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   static_assert(TL::kMX, "MXFP8 tile");
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = F.d, I = F.I, ds = d / 32;
   const uint8_t* W1 = (const uint8_t*)F.w1 + (size_t)e * I * d;
   const uint8_t* W3 = (const uint8_t*)F.w3 + (size_t)e * I * d;
@@ -53,9 +55,12 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
     if (scale) return (which ? S3 : S1) + (size_t)(c0 + col) * ds;
     return (which ? W3 : W1) + (size_t)(c0 + col) * d;
   };
-  // rows past the tile's n repeat its last row (their outputs are dropped)
-  la.init([&](int r) { return F.xq + (size_t)F.src[r0 + min(r, n - 1)] * d; },
-          [&](int r) { return F.xs + (size_t)F.src[r0 + min(r, n - 1)] * ds; },
+  // rows past the tile's n repeat its last row (their outputs are dropped);
+  // the source tokens come from the tile's own slot (written by its gather
+  // task in this launch, on lines no other task writes)
+  const int* ts = F.tsrc + slots::tile_slot(tile, 0, F.BM, 1);
+  la.init([&](int r) { return F.xq + (size_t)clamp_token(ts[min(r, n - 1)], F.T) * d; },
+          [&](int r) { return F.xs + (size_t)clamp_token(ts[min(r, n - 1)], F.T) * ds; },
           [&](int nr) { return wrow(nr, true); }, F.mx_wide1 != 0);
   lb.init([&](int nr) { return (const bf16_t*)wrow(nr, false); });
   f32x16_t acc[TL::MI][TL::NJ];
@@ -84,7 +89,7 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
     uint4* dst = (uint4*)(F.hq + r * I + c0 + 32 * blk);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    F.hs[r * (I / 32) + c0 / 32 + blk] = (uint8_t)sc;
+    F.hs[slots::tile_slot(tile, row, F.BM, I / 32) + c0 / 32 + blk] = (uint8_t)sc;
     if (Hb) {
       uint4* hb = (uint4*)(Hb + r * I + c0 + 32 * blk);
 #pragma unroll
@@ -115,7 +120,9 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
 template <class TL>
 __device__ void g2_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   static_assert(TL::kMX, "MXFP8 tile");
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = F.d, I = F.I, is = I / 32;
   const uint8_t* W2 = (const uint8_t*)F.w2 + (size_t)e * d * I;
   const uint8_t* S2 = F.w2s + (size_t)e * d * is;
@@ -123,7 +130,7 @@ __device__ void g2_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   KRowsMX<TL::BM, TL::BN> la;
   KRows<TL::BN> lb;
   la.init([&](int r) { return F.hq + (size_t)(r0 + min(r, n - 1)) * I; },
-          [&](int r) { return F.hs + (size_t)(r0 + min(r, n - 1)) * is; },
+          [&](int r) { return F.hs + slots::tile_slot(tile, min(r, n - 1), F.BM, is); },
           [&](int nr) { return S2 + (size_t)(c0 + nr) * is; }, F.mx_wide2 != 0);
   lb.init([&](int nr) { return (const bf16_t*)(W2 + (size_t)(c0 + nr) * I); });
   f32x16_t acc[TL::MI][TL::NJ];
@@ -143,6 +150,8 @@ __global__ void __launch_bounds__(256) k_mx_quant_rows(const bf16_t* __restrict_
   const int64_t nbk = K / 32, total = rows * nbk;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
     const int64_t r = i / nbk, b = i - r * nbk;
+    // (a perm entry outside [0, rows) leaves its row unwritten)
+    if (GATHER && (unsigned)perm[r] >= (unsigned)rows) continue;
     const int64_t s = GATHER ? (int64_t)(perm[r] / k) : r;
     mx_quant_bf16_block(src + s * K + 32 * b, codes + r * K + 32 * b, scales + i);
   }

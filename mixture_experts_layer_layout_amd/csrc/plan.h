@@ -30,9 +30,10 @@ struct Plan {
   int nRP;         // row-preparation tasks (kPrepTok tokens each)
   // workspace carving (byte offsets)
   size_t o_ctr, n_ctr;
+  size_t lstride;  // floats per router slice (T E rounded up to 32)
   size_t o_lpart, o_topk, o_gate, o_bmask, o_bbase, o_counts, o_offsets;
   size_t o_tile_e, o_tile_r0, o_tile_n, o_perm, o_inv, o_src, o_grow;
-  size_t o_etile, o_eorder;
+  size_t o_etile, o_eorder, o_eoff, o_tsrc;
   size_t o_h, o_big1, o_big2, o_dab, o_dgp, o_hs, o_zero, o_gg;
   size_t o_xs;     // MXFP8: x scales (the codes sit at o_big1)
   size_t o_rdz, o_rpart, o_rpbias;  // router backward: dz, dWr and dbias partial sums

@@ -60,7 +60,7 @@ __device__ void router_bwd_token(const RouterBwd& P, int t) {
   int e = 0;
   float g = 0.0f, dg = 0.0f, z = 0.0f;
   if (mine) {
-    e = P.topk[(size_t)t * k + lane];
+    e = min(max(P.topk[(size_t)t * k + lane], 0), P.E - 1);  // saved indices clamped to [0, E)
     // the unscaled gate and the gradient it receives
     g = P.gate[(size_t)t * k + lane] / P.scale;
     dg = P.dgate[(size_t)t * k + lane] * P.scale;
@@ -153,7 +153,8 @@ __global__ void __launch_bounds__(256) k_router_bwd_dwr(RouterBwd P) {
   __shared__ float redb[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x, ch = blockIdx.y, s = blockIdx.z;
-  const int lo0 = P.offsets[e], n = P.offsets[e + 1] - lo0;
+  // the saved offsets clamped to [0, R] (rows outside are never read)
+  const int lo0 = min(max(P.offsets[e], 0), P.R), n = max(min(max(P.offsets[e + 1], 0), P.R) - lo0, 0);
   const int lo = lo0 + (int)((int64_t)n * s / kRbSplits), hi = lo0 + (int)((int64_t)n * (s + 1) / kRbSplits);
   const int nvec = P.d / EPV;
   const int v = ch * 64 + lane;
@@ -168,7 +169,10 @@ __global__ void __launch_bounds__(256) k_router_bwd_dwr(RouterBwd P) {
     float wz[4];
     uint4 u[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = r0 + 4 * i < hi ? P.perm[r0 + 4 * i] : -1;
+    for (int i = 0; i < 4; ++i) {
+      a[i] = r0 + 4 * i < hi ? P.perm[r0 + 4 * i] : -1;
+      a[i] = (unsigned)a[i] < (unsigned)P.R ? a[i] : -1;  // a perm entry outside [0, R) adds nothing
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       wz[i] = a[i] >= 0 ? P.dz[a[i]] : 0.0f;

@@ -17,46 +17,28 @@
 
 namespace moe {
 
-constexpr int kMaxPhases = 8;
-constexpr int kXcds = 8;
+using proto::kMaxPhases;
+using proto::kXcds;
+using proto::Claim;
 
 // The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
 __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcds - 1);
 }
 
-// Claim state of one workgroup, kept in LDS (only thread 0 touches it) so
-// it occupies no registers across the tasks of the persistent loop.
-struct Claim {
-  int phase;  // current phase
-  int qoff;   // sub-queue being drained: (own + qoff) % 8
-  int own;    // this workgroup's XCD
-  int nmt;    // row tiles once known, else -1
-  int task;   // the claimed task (-1: done)
-};
+// The home sub-queue of this workgroup: its XCD, or (the test-only
+// MOE_FLAG_TEST_SHUFFLE_CLAIMS) a hash of its workgroup id, which changes the
+// order in which the tasks are claimed and where they run without changing
+// what any task computes.
+__device__ __forceinline__ int claim_home(uint32_t flags) {
+  if (flags & MOE_FLAG_TEST_SHUFFLE_CLAIMS) return (int)((blockIdx.x * 0x9E3779B1u) >> 29);
+  return xcc_id();
+}
 
-// Thread 0 only.  shape(phase, groups, per) gives the phase's group count
-// and tasks per group (it may wait for the layout; false = give up).
-// Returns the claimed task's index within its phase (group * per + member)
-// and sets c.phase, or returns -1 when every phase is drained.
+// Thread 0 only (protocol.h: claim_next).
 template <class F>
 __device__ __forceinline__ int claim_next(int* qctr, int nphases, Claim& c, F shape) {
-  while (c.phase < nphases) {
-    int groups = 0, per = 0;
-    if (!shape(c.phase, groups, per)) return -1;
-    const int sub = (c.own + c.qoff) & (kXcds - 1);
-    const int g_sub = groups > sub ? (groups - sub + kXcds - 1) / kXcds : 0;
-    const int n = g_sub * per;
-    if (n > 0) {
-      const int i = atomicAdd(&qctr[c.phase * kXcds + sub], 1);
-      if (i < n) return (sub + kXcds * (i / per)) * per + i % per;
-    }
-    if (++c.qoff == kXcds) {
-      c.qoff = 0;
-      ++c.phase;
-    }
-  }
-  return -1;
+  return proto::claim_next<DevOps>(qctr, nphases, c, shape);
 }
 
 // ---------------------------------------------------------------- raster

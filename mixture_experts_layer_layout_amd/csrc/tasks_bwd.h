@@ -52,7 +52,7 @@ constexpr int kDgradAhead = MOE_DGRAD_AHEAD;
 
 
 struct Bwd {
-  int T, d, E, k, I, R, BM;
+  int T, d, E, k, I, R, BM, max_tiles;
   int nNdh, nNdx, nW2m, nW2n, nW13m, nW13n, nRP, nC;
   const bf16_t* dy;
   const bf16_t* x;
@@ -60,7 +60,9 @@ struct Bwd {
   const bf16_t* w3;
   const bf16_t* w2;
   const float* gate;     // [T, k]
-  const int* offsets;    // [E+1]
+  const int* offsets;    // [E+1] the forward's (caller's) offsets
+  int* eoff;             // [E+1] the same after bwd_setup checked them (all
+                         // zero when they do not describe R rows)
   const int* perm;       // [R]
   const int* inv;        // [R]
   const bf16_t* a;       // [R, I]
@@ -102,20 +104,32 @@ struct Bwd {
 };
 
 // ---------------------------------------------------------------- setup
+// Row tiles and expert order from the saved offsets.  Offsets that do not
+// describe R rows (offsets[0] = 0, nondecreasing, offsets[E] = R) record
+// MOE_ERR_INVALID_ROUTE and are replaced by zeros: no row tile, every
+// expert empty, so no task addresses a row past R.
 __device__ void bwd_setup(const Bwd& B, int* sh /* >= 2*kMaxE + 16 ints */) {
   int* scnt = sh;
   int* stile = sh + kMaxE;
   int* tmp = sh + 2 * kMaxE;
+  __shared__ int s_bad;
+  if (threadIdx.x == 0) s_bad = (B.offsets[0] != 0 || B.offsets[B.E] != B.R) ? 1 : 0;
   __syncthreads();
+  for (int e = threadIdx.x; e < B.E; e += kThreads)
+    if (B.offsets[e + 1] < B.offsets[e]) s_bad = 1;
+  __syncthreads();
+  const bool bad = s_bad != 0;
+  if (bad && threadIdx.x == 0) set_status(B.s.status, MOE_ERR_INVALID_ROUTE);
+  for (int e = threadIdx.x; e <= B.E; e += kThreads) B.eoff[e] = bad ? 0 : B.offsets[e];
   for (int e = threadIdx.x; e < B.E; e += kThreads) {
-    const int c = B.offsets[e + 1] - B.offsets[e];
+    const int c = bad ? 0 : B.offsets[e + 1] - B.offsets[e];
     scnt[e] = c;
     stile[e] = cdiv(c, B.BM);
   }
   __syncthreads();
   const int ntiles = block_exclusive_scan(stile, B.E, tmp);
   for (int e = threadIdx.x; e < B.E; e += kThreads) {
-    const int c = scnt[e], off = B.offsets[e];
+    const int c = scnt[e], off = bad ? 0 : B.offsets[e];
     B.etile[e] = stile[e];
     for (int mt = 0, id = stile[e]; mt * B.BM < c; ++mt, ++id) {
       B.tile_e[id] = e;
@@ -150,7 +164,7 @@ __device__ void bwd_rowprep(const Bwd& B, int task) {
     // lane j < k holds slot j's row and gate
     const int lane_row = lane < k ? B.inv[(size_t)t * k + lane] : -1;
     const float lane_g = lane < k ? B.gate[(size_t)t * k + lane] : 0.0f;
-    if (lane < k && (unsigned)lane_row < (unsigned)B.R) {
+    if (lane < k && (unsigned)lane_row < (unsigned)B.R) {  // inv entries outside [0, R) are skipped
       B.src[lane_row] = t;
       B.grow[lane_row] = lane_g;
     }
@@ -223,15 +237,21 @@ __device__ __forceinline__ void bwd_dh_epilogue(const Bwd& B, f32x16_t (&acc)[TL
 }
 
 // dHu = G W2_e for one (row tile, I tile), then the dh epilogue.
+__device__ __forceinline__ TileRows bwd_tile(const Bwd& B, int tile) {
+  return tile_rows(B.tile_e, B.tile_r0, B.tile_n, tile, B.max_tiles, B.E, B.R, B.BM);
+}
+
 __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*) {
   typedef TileDH TL;
-  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const TileRows tr = bwd_tile(B, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = B.d, I = B.I;
   const bf16_t* W2 = B.w2 + (size_t)e * d * I;
   const int c0 = nt * TL::BN;
   KRows<TL::BM, kDgradAhead> la;
   // rows past n repeat the last row (their outputs are dropped)
-  la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)B.src[r0 + min(r, n - 1)] * d; });
+  la.init([&](int r) -> const bf16_t* { return B.dy + (size_t)clamp_token(B.src[r0 + min(r, n - 1)], B.T) * d; });
   auto lb = kcols_n<TL::BN, kDgradAhead>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
   f32x16_t acc[TL::MI][TL::NJ];
   tile_mainloop<TL, kDgradAhead>(d / 64, smem, acc, la, lb);
@@ -242,7 +262,9 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
 // dXp = [dA | dB] [W1_e ; W3_e] for one (row tile, d tile).
 __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
   typedef TileDH TL;
-  const int e = B.tile_e[tile], r0 = B.tile_r0[tile], n = B.tile_n[tile];
+  const TileRows tr = bwd_tile(B, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = B.d, I = B.I;
   const bf16_t* W1 = B.w1 + (size_t)e * I * d;
   const bf16_t* W3 = B.w3 + (size_t)e * I * d;
@@ -285,12 +307,12 @@ __device__ __forceinline__ void wgrad_band(int nc, int nk, bf16_t* smem, LA& la,
 // (tile_stream) so consecutive column tiles overlap.
 __device__ void bwd_dw2_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   typedef TileDW TL;
-  const int e = B.eorder[rank];
+  const int e = min(max(B.eorder[min(rank, B.E - 1)], 0), B.E - 1);
   const int chunks = cdiv(B.nW2n, kWgradPerTicket);
   const int n0 = (task / chunks) * TL::BM;
   const int cb = (task % chunks) * kWgradPerTicket, nc = min(kWgradPerTicket, B.nW2n - cb);
   const int d = B.d, I = B.I;
-  const int off = B.offsets[e], M = B.offsets[e + 1] - off;
+  const int off = B.eoff[e], M = B.eoff[e + 1] - off;
   bf16_t* out = B.dw2 + (size_t)e * d * I + (size_t)n0 * I;
   auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
     tile_store_staged<TL>(acc, [&](int wm) { return out + (size_t)(wm * TL::WM) * I + (cb + c) * TL::BN; }, I,
@@ -317,12 +339,12 @@ __device__ void bwd_dw2_band(const Bwd& B, int rank, int task, bf16_t* smem) {
 // kWgradPerTicket column tiles of d, streamed like dw2.
 __device__ void bwd_dw13_band(const Bwd& B, int rank, int task, bf16_t* smem) {
   typedef TileDW TL;
-  const int e = B.eorder[rank];
+  const int e = min(max(B.eorder[min(rank, B.E - 1)], 0), B.E - 1);
   const int chunks = cdiv(B.nW13n, kWgradPerTicket);
   const int i0 = (task / chunks) * (TL::BM / 2);
   const int cb = (task % chunks) * kWgradPerTicket, nc = min(kWgradPerTicket, B.nW13n - cb);
   const int d = B.d, I = B.I;
-  const int off = B.offsets[e], M = B.offsets[e + 1] - off;
+  const int off = B.eoff[e], M = B.eoff[e + 1] - off;
   bf16_t* o1 = B.dw1 + (size_t)e * I * d + (size_t)i0 * d;
   bf16_t* o3 = B.dw3 + (size_t)e * I * d + (size_t)i0 * d;
   // wave row block 0 holds the dW1 rows, block 1 the dW3 rows
@@ -361,7 +383,7 @@ __device__ void bwd_dx_tokens_k(const Bwd& B, int cb) {
     if (t >= B.T) break;
     int rows[NR];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) rows[j] = j < k ? B.inv[(size_t)t * k + j] : 0;
+    for (int j = 0; j < NR; ++j) rows[j] = j < k ? clamp_row(B.inv[(size_t)t * k + j], B.R) : 0;
     {
       // dgate[t, j]: slot j's column-tile partials summed by a group of G
       // lanes (G the largest power of two with G k <= 64), each lane a
@@ -372,7 +394,7 @@ __device__ void bwd_dx_tokens_k(const Bwd& B, int cb) {
       const int j = lane / G, q = lane - (lane / G) * G;
       float s = 0.0f;
       if (j < k) {
-        const int r = B.inv[(size_t)t * k + j];
+        const int r = clamp_row(B.inv[(size_t)t * k + j], B.R);
         for (int p = q; p < B.nNdh; p += G) s += B.dgp[(size_t)p * B.R + r];
       }
       for (int o = G >> 1; o > 0; o >>= 1) s += __shfl_xor(s, o);

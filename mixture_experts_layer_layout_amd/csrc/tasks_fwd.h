@@ -58,6 +58,7 @@ struct Sync {
   int* q_done;   // MXFP8 forward: token blocks quantised
   int32_t* status;
   long long spin_limit;
+  uint32_t flags;  // moe_desc.flags (the test-only MOE_FLAG_TEST_* bits)
 };
 
 struct Fwd {
@@ -74,7 +75,8 @@ struct Fwd {
   const void* w3;
   const void* w2;
   void* y;
-  float* lpart;      // [S, T, E]
+  float* lpart;      // [S, lstride]: slice s holds [T, E] at s * lstride
+  size_t lstride;    // T E rounded up to 32 floats: each slice starts on a line
   float* logits;     // [T, E] or null
   int* topk;         // [T, k]
   float* gate;       // [T, k]
@@ -88,7 +90,9 @@ struct Fwd {
   int* etile;        // [E+1] first row tile of each expert (+ the total)
   int* perm;         // [R]
   int* inv;          // [R]
-  int* src;          // [R]
+  int* tsrc;         // [max_tiles, BM]: source token of row i of row tile
+                     // `tile` at tile * BM + i (each tile's slot on lines
+                     // of its own: it is read inside the launch)
   float* grow;       // [R] gate of each row, or null
   void* xp;          // [R, d]
   void* a;           // [R, I] or null
@@ -103,7 +107,7 @@ struct Fwd {
   uint8_t* xq;         // [T, d]
   uint8_t* xs;         // [T, d/32]
   uint8_t* hq;         // [R, I]
-  uint8_t* hs;         // [R, I/32]
+  uint8_t* hs;         // [max_tiles, BM, I/32]: H scales by row-tile slot
   // scale rows of the up / down projection read 16 bytes every 4 stages
   // (K % 512 == 0 and 16-byte aligned scale arrays)
   int mx_wide1, mx_wide2;
@@ -111,6 +115,32 @@ struct Fwd {
 };
 
 __device__ __forceinline__ WaitCtx wctx(const Sync& s) { return WaitCtx{s.abort, s.status, s.spin_limit}; }
+
+// The rows of row tile `tile`, clamped to the arrays they address: the tile
+// id to [0, max_tiles), the expert to [0, E), the first row to [0, R] and the
+// row count to [0, min(BM, R - r0)].  With a layout written by layout_scan
+// (or bwd_setup) these are the values stored; the clamps keep a damaged
+// workspace from turning into out-of-bounds addresses.
+struct TileRows {
+  int e, r0, n;
+};
+__device__ __forceinline__ TileRows tile_rows(const int* te, const int* tr0, const int* tn, int tile, int max_tiles,
+                                              int E, int R, int BM) {
+  tile = min(max(tile, 0), max_tiles - 1);
+  TileRows t;
+  t.e = min(max(te[tile], 0), E - 1);
+  t.r0 = min(max(tr0[tile], 0), R);
+  t.n = min(max(tn[tile], 0), min(BM, R - t.r0));
+  return t;
+}
+__device__ __forceinline__ TileRows fwd_tile(const Fwd& F, int tile) {
+  return tile_rows(F.tile_e, F.tile_r0, F.tile_n, tile, F.max_tiles, F.E, F.R, F.BM);
+}
+
+// A source token index read from the workspace, clamped to [0, T).
+__device__ __forceinline__ int clamp_token(int t, int T) { return (unsigned)t < (unsigned)T ? t : 0; }
+// A row index read from the workspace, clamped to [0, R).
+__device__ __forceinline__ int clamp_row(int r, int R) { return (unsigned)r < (unsigned)R ? r : 0; }
 
 // ---------------------------------------------------------------- router
 // logits slice s of token block b: lpart[s][t][e] = sum over k in slice s.
@@ -150,7 +180,7 @@ __device__ void router_partial<bf16_t>(const Fwd& F, int task) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int orow = b * kTokBlock + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (orow < F.T && ev) F.lpart[((size_t)s * F.T + orow) * F.E + e] = acc[r];
+      if (orow < F.T && ev) F.lpart[(size_t)s * F.lstride + (size_t)orow * F.E + e] = acc[r];
     }
   }
 }
@@ -166,7 +196,7 @@ __device__ void router_partial<float>(const Fwd& F, int task) {
     if (row >= F.T) continue;
     float acc = 0.0f;
     for (int kk = 0; kk < dk; ++kk) acc = fmaf(X[(size_t)row * F.d + k0 + kk], Wr[(size_t)e * F.d + k0 + kk], acc);
-    F.lpart[((size_t)s * F.T + row) * F.E + e] = acc;
+    F.lpart[(size_t)s * F.lstride + (size_t)row * F.E + e] = acc;
   }
 }
 
@@ -190,7 +220,8 @@ __device__ __forceinline__ void wave_topk_gates(const float* row, const float* k
     if (lane < n_group) {
       float t1 = -INFINITY, t2 = -INFINITY;
       for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-        const float v = key[e];
+        float v = key[e];
+        v = v != v ? -INFINITY : v;
         if (v > t1) { t2 = t1; t1 = v; } else if (v > t2) { t2 = v; }
       }
       gsc = gs > 1 ? t1 + t2 : t1;
@@ -218,7 +249,8 @@ __device__ __forceinline__ void wave_topk_gates(const float* row, const float* k
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int e = lane, q = 0; e < E; e += 64, ++q) {
-      const float v = key[e];
+      float v = key[e];
+      v = v != v ? -INFINITY : v;  // a NaN key ranks last, so k experts are always found
       if (!((taken >> q) & 1u) && (v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -279,7 +311,7 @@ __device__ void router_topk(const Fwd& F, int task, char* smem) {
       const int t = t0 + p / E, e = p % E;
       if (t >= F.T) break;
       float v = 0.0f;
-      for (int s = 0; s < F.S; ++s) v += F.lpart[((size_t)s * F.T + t) * E + e];
+      for (int s = 0; s < F.S; ++s) v += F.lpart[(size_t)s * F.lstride + (size_t)t * E + e];
       if (F.logits) F.logits[(size_t)t * E + e] = v;
       if (F.bias && !F.select_only) v += F.bias[e];
       sv[p] = v;
@@ -378,7 +410,11 @@ __device__ int block_exclusive_scan(int* v, int n, int* tmp /* >= 8 ints */) {
   return total;
 }
 
-// One workgroup: counts, offsets, bases, tile list.
+// One workgroup: counts, offsets, bases, tile list.  The masks of a valid
+// routing hold exactly R = T k bits and give at most max_tiles row tiles;
+// anything else (a repeated or out-of-range expert given to moe_layout)
+// records MOE_ERR_INVALID_ROUTE and publishes no row tile, so no later task
+// addresses a row past R.
 __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   int* scnt = sh;
   int* stile = sh + kMaxE;
@@ -394,6 +430,18 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   __syncthreads();
   const int R = block_exclusive_scan(scnt, F.E, tmp);
   const int ntiles = block_exclusive_scan(stile, F.E, tmp);
+  const bool valid = R == F.R && ntiles <= F.max_tiles;
+  if (!valid) {
+    if (threadIdx.x == 0) {
+      set_status(F.s.status, MOE_ERR_INVALID_ROUTE);
+      *F.s.n_mtiles = 0;
+    }
+    for (int e = threadIdx.x; e <= F.E; e += kThreads) {
+      F.etile[e] = 0;
+      F.offsets[e] = 0;
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < F.E; e += kThreads) {
     const int off = scnt[e];
     F.offsets[e] = off;
@@ -444,21 +492,24 @@ __device__ __forceinline__ int row_source(const Fwd& F, int e, int r) {
     const int mid = (lo + hi) >> 1;
     if (F.bbase[(size_t)mid * F.E + e] <= r) lo = mid + 1; else hi = mid;
   }
-  const int b = lo - 1;
+  const int b = max(lo - 1, 0);
   const int rank = r - F.bbase[(size_t)b * F.E + e];
-  const int t = b * kTokBlock + select_bit(F.bmask[(size_t)b * F.E + e], rank);
+  const int t = min(b * kTokBlock + select_bit(F.bmask[(size_t)b * F.E + e], rank), F.T - 1);
   int j = 0;
   for (int jj = 0; jj < F.k; ++jj)
     if (F.topk[(size_t)t * F.k + jj] == e) j = jj;
   return t * F.k + j;
 }
 
-// Rows of one tile: writes perm, inv, src (and the per-row gate), then (if
-// COPY) pulls the token rows into expert order.  Raises ready[tile] (with
-// the agent-scope release when REL: a reader runs in the same launch).
+// Rows of one tile: writes perm, inv, the tile's source slot (and the
+// per-row gate), then (if COPY) pulls the token rows into expert order.
+// Raises ready[tile] (with the agent-scope release when REL: a reader runs
+// in the same launch) unless the test-only MOE_FLAG_TEST_DROP_READY holds
+// back the counter of row tile 0 (its readers' bounded waits then expire).
 template <class Act, bool COPY, bool REL>
 __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int r = r0 + i;
@@ -466,7 +517,7 @@ __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
     const int t = a / F.k;
     F.perm[r] = a;
     F.inv[a] = r;
-    F.src[r] = t;
+    F.tsrc[slots::tile_slot(tile, i, F.BM, 1)] = t;
     if (F.grow) F.grow[r] = F.gate[a];
     ssrc[i] = t;
   }
@@ -479,13 +530,16 @@ __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
     for (int i = wave; i < n; i += 4)
       wave_copy_row(X + (size_t)ssrc[i] * nvec, XP + (size_t)(r0 + i) * nvec, nvec, CopyAsIs());
   }
+  if (tile == 0 && (F.s.flags & MOE_FLAG_TEST_DROP_READY)) return;
   signal_add<REL>(&F.s.ready[tile], 1);
 }
 
 // ---------------------------------------------------------------- GEMMs
 template <class TL>
 __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = F.d, I = F.I;
   const bf16_t* W1 = (const bf16_t*)F.w1 + (size_t)e * I * d;
   const bf16_t* W3 = (const bf16_t*)F.w3 + (size_t)e * I * d;
@@ -497,7 +551,8 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   // rows past the tile's n repeat its last row (their outputs are dropped)
   if (F.direct) {
     const bf16_t* X = (const bf16_t*)F.x;
-    la.init([&](int r) -> const bf16_t* { return X + (size_t)F.src[r0 + min(r, n - 1)] * d; });
+    const int* ts = F.tsrc + slots::tile_slot(tile, 0, F.BM, 1);
+    la.init([&](int r) -> const bf16_t* { return X + (size_t)clamp_token(ts[min(r, n - 1)], F.T) * d; });
   } else {
     const bf16_t* XP = (const bf16_t*)F.xp;
     la.init([&](int r) -> const bf16_t* { return XP + (size_t)(r0 + min(r, n - 1)) * d; });
@@ -535,7 +590,9 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
 
 template <class TL>
 __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
+  if (n <= 0) return;
   const int d = F.d, I = F.I;
   const bf16_t* W2 = (const bf16_t*)F.w2 + (size_t)e * d * I;
   const bf16_t* H = (const bf16_t*)F.h;
@@ -558,7 +615,8 @@ __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
 }
 
 __device__ void g1_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
   const int d = F.d, I = F.I;
   const float* W1 = (const float*)F.w1 + (size_t)e * I * d;
   const float* W3 = (const float*)F.w3 + (size_t)e * I * d;
@@ -582,7 +640,8 @@ __device__ void g1_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
 }
 
 __device__ void g2_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
-  const int e = F.tile_e[tile], r0 = F.tile_r0[tile], n = F.tile_n[tile];
+  const TileRows tr = fwd_tile(F, tile);
+  const int e = tr.e, r0 = tr.r0, n = tr.n;
   const int d = F.d, I = F.I;
   const float* W2 = (const float*)F.w2 + (size_t)e * d * I;
   const float* H = (const float*)F.h;
@@ -615,7 +674,7 @@ __device__ void combine_tokens_k(const Fwd& F, int cb) {
     float g[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-      rows[j] = j < k ? F.inv[(size_t)t * k + j] : 0;
+      rows[j] = j < k ? clamp_row(F.inv[(size_t)t * k + j], F.R) : 0;
       g[j] = j < k ? F.gate[(size_t)t * k + j] : 0.0f;
     }
     // known k: kCombVec vectors per lane per step, every row load of a step

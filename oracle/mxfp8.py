@@ -186,7 +186,12 @@ def expert_ffn_mxfp8(xq_rows, w1, w3, w2):
     return A, B, h, fake_quant(h) @ w2q.T
 
 
-def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
+def _starmap(fn, jobs):
+    for job in jobs:
+        yield fn(*job)
+
+
+def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None, expert_map=None):
     """The forward with the expert GEMMs in MXFP8.
 
     MoK flash §02 folds quantisation into dispatch, the grouped GEMM and
@@ -194,7 +199,9 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
     W1/W3 along d and W2 along I (blocks along the contraction axis of each
     GEMM), and H along I after SwiGLU (expert_ffn_mxfp8).  Routing and the
     weighted combine stay in high precision.  Every product of dequantised
-    operands is exact in fp64 before summation.
+    operands is exact in fp64 before summation.  ``expert_map(fn, jobs)``
+    runs fn(*job) for each expert's job in order and yields the results (a
+    process pool may stand in for the default loop).
     """
     from . import moe as M
     T = np.shape(x)[0]
@@ -212,18 +219,45 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None):
     B = np.zeros((R, I))
     H = np.zeros((R, I))
     Yp = np.zeros((R, d))
-    for e in range(E):
+    live = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+    jobs = ((xp[offsets[e]:offsets[e + 1]], w1[e], w3[e], w2[e]) for e in live)
+    for e, res in zip(live, (expert_map or _starmap)(expert_ffn_mxfp8, jobs)):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi == lo:
-            continue
-        A[lo:hi], B[lo:hi], H[lo:hi], Yp[lo:hi] = expert_ffn_mxfp8(xp[lo:hi], w1[e], w3[e], w2[e])
+        A[lo:hi], B[lo:hi], H[lo:hi], Yp[lo:hi] = res
     y = M.combine(Yp, gate, inv, T, k)
     return dict(logits=logits, topk_idx=idx, gate=gate, counts=counts,
                 offsets=offsets, perm=perm, inv=inv, src=src, A=A, B=B, H=H, Yp=Yp,
                 y=y)
 
 
-def backward_mxfp8(dy, x, fwd, w1, w3, w2, k):
+def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e):
+    """One expert's part of backward_mxfp8 over its rows (the gathered x and
+    dY rows, the rows' gates and the forward's A, B, H of those rows), in
+    the steps of oracle.moe.backward: dHu = G W2 with G quantised along d
+    per row and W2 as [I, d] (W2^T) along d; dgate = <dHu, H>; dW2 = (g G)^T
+    H; dH = g dHu; the SwiGLU backward; dXp = dA W1 + dB W3 with dA, dB
+    quantised along I per row and W1, W3 as [d, I] along I; dW1 = dA^T x,
+    dW3 = dB^T x with the unquantised operands.  Returns dict dw1, dw3, dw2,
+    dxp, dgate (per row), dHu, dA, dB."""
+    from . import moe as M
+    xr = np.asarray(x_rows, dtype=np.float64)
+    G = np.asarray(dy_rows, dtype=np.float64)
+    g = np.asarray(g_rows, dtype=np.float64)
+    w2t = fake_quant(np.asarray(w2_e, dtype=np.float64).T)          # [I, d] along d
+    dHu = quantize_tokens(G) @ w2t.T
+    dgate = np.sum(dHu * H, axis=1)
+    dW2 = (g[:, None] * G).T @ H
+    dH = g[:, None] * dHu
+    sA = M.sigmoid(A)
+    dA = dH * B * sA * (1.0 + A * (1.0 - sA))
+    dB = dH * M.silu(A)
+    w1t = fake_quant(np.asarray(w1_e, dtype=np.float64).T)          # [d, I] along I
+    w3t = fake_quant(np.asarray(w3_e, dtype=np.float64).T)
+    dXp = fake_quant(dA) @ w1t.T + fake_quant(dB) @ w3t.T
+    return dict(dw1=dA.T @ xr, dw3=dB.T @ xr, dw2=dW2, dxp=dXp, dgate=dgate, dHu=dHu, dA=dA, dB=dB)
+
+
+def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None):
     """The backward of the expert path (routing frozen) with the two data
     gradient GEMMs in MXFP8 and the weight gradients in high precision.
 
@@ -234,9 +268,10 @@ def backward_mxfp8(dy, x, fwd, w1, w3, w2, k):
     [I, d] (W2^T) along d; [dA | dB] along I and W1, W3 as [d, I] (W^T)
     along I -- while the weight gradients take the unquantised operands (G,
     the forward's H, dA, dB and the gathered x rows).  The steps are those
-    of moe.backward; fwd holds the forward's gate, layout and A, B, H.
+    of moe.backward, expert by expert (expert_backward_mxfp8, through
+    ``expert_map`` as in forward_mxfp8); fwd holds the forward's gate,
+    layout and A, B, H.
     """
-    from . import moe as M
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     T, d = dy.shape
@@ -246,40 +281,26 @@ def backward_mxfp8(dy, x, fwd, w1, w3, w2, k):
     A, B, H = fwd["A"], fwd["B"], fwd["H"]
     R = perm.shape[0]
     g_row = gate.reshape(-1)[perm]
-    G = dy[src]                                    # pull reverse-combine
-    Gq = fake_quant(dy)[src]                       # rows quantised along d
-    xp = x[src]
-    dHu = np.zeros((R, I))
+    out = dict(dHu=np.zeros((R, I)), dA=np.zeros((R, I)), dB=np.zeros((R, I)), dXp=np.zeros((R, d)))
+    dgate_row = np.zeros(R)
     dW1 = np.zeros((E, I, d))
     dW3 = np.zeros((E, I, d))
     dW2 = np.zeros((E, d, I))
-    dXp = np.zeros((R, d))
-    for e in range(E):
+    live = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+
+    def job(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi == lo:
-            continue
-        w2t = fake_quant(np.asarray(w2[e], dtype=np.float64).T)      # [I, d] along d
-        dHu[lo:hi] = Gq[lo:hi] @ w2t.T
-        dW2[e] = (g_row[lo:hi, None] * G[lo:hi]).T @ H[lo:hi]
-    dgate_row = np.sum(dHu * H, axis=1)
-    dH = g_row[:, None] * dHu
-    sA = M.sigmoid(A)
-    dA = dH * B * sA * (1.0 + A * (1.0 - sA))
-    dB = dH * M.silu(A)
-    dAq = fake_quant(dA)                           # along I
-    dBq = fake_quant(dB)
-    for e in range(E):
+        rows = src[lo:hi]
+        return (x[rows], dy[rows], g_row[lo:hi], A[lo:hi], B[lo:hi], H[lo:hi], w1[e], w3[e], w2[e])
+
+    for e, b in zip(live, (expert_map or _starmap)(expert_backward_mxfp8, (job(e) for e in live))):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi == lo:
-            continue
-        w1t = fake_quant(np.asarray(w1[e], dtype=np.float64).T)      # [d, I] along I
-        w3t = fake_quant(np.asarray(w3[e], dtype=np.float64).T)
-        dXp[lo:hi] = dAq[lo:hi] @ w1t.T + dBq[lo:hi] @ w3t.T
-        dW1[e] = dA[lo:hi].T @ xp[lo:hi]
-        dW3[e] = dB[lo:hi].T @ xp[lo:hi]
+        dW1[e], dW3[e], dW2[e] = b["dw1"], b["dw3"], b["dw2"]
+        dgate_row[lo:hi] = b["dgate"]
+        out["dHu"][lo:hi], out["dA"][lo:hi], out["dB"][lo:hi], out["dXp"][lo:hi] = b["dHu"], b["dA"], b["dB"], b["dxp"]
     dx = np.zeros((T, d))
     for t in range(T):
         for j in range(k):
-            dx[t] += dXp[inv[t * k + j]]
+            dx[t] += out["dXp"][inv[t * k + j]]
     dgate = dgate_row[inv].reshape(T, k)
-    return dict(dx=dx, dw1=dW1, dw3=dW3, dw2=dW2, dgate=dgate, dHu=dHu, dA=dA, dB=dB, dXp=dXp)
+    return dict(dx=dx, dw1=dW1, dw3=dW3, dw2=dW2, dgate=dgate, **out)

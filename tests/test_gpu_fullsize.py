@@ -15,6 +15,8 @@ oracle where the oracle can follow:
     routing and dgate.
 Expert weights are drawn on the device (as bench.py does); the oracle reads
 the experts it needs back one at a time."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -32,18 +34,22 @@ BF16_TOL = 2e-2
 
 
 class DeviceExperts:
-    """[E, rows, cols] weights on the GPU seen by the oracle as fp64 host
-    arrays, one expert at a time."""
+    """[E, rows, cols] weights on the GPU seen by the oracle as host arrays,
+    one expert at a time (fp32 copies, exactly the bf16 values; the oracle
+    computes in fp64), the last `keep` experts cached."""
 
-    def __init__(self, t):
+    def __init__(self, t, keep=16):
         self.t = t
         self.shape = tuple(t.shape)
+        self.keep = keep
         self.cache = {}
 
     def __getitem__(self, e):
         e = int(e)
         if e not in self.cache:
-            self.cache[e] = self.t[e].float().cpu().numpy().astype(np.float64)
+            if len(self.cache) >= self.keep:
+                self.cache.pop(next(iter(self.cache)))
+            self.cache[e] = self.t[e].float().cpu().numpy()
         return self.cache[e]
 
 
@@ -62,6 +68,91 @@ def full_inputs(w, seed):
 def sample_tokens(T, n, seed):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
+
+
+def edge_tokens(offsets, perm, k, experts, BM=128):
+    """Tokens of the rows at the edges of the given experts' row tiles: the
+    first row, the last row of the first tile and the first of the second
+    (a tile boundary), and the expert's last row (the ragged tail)."""
+    out = []
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for r in (lo, lo + BM - 1, lo + BM, hi - 1):
+            if lo <= r < hi:
+                out.append(int(perm[r]) // k)
+    return out
+
+
+def pick_tokens(idx, E, required, n, seed):
+    """`required` tokens plus others up to n, each next one chosen among
+    random candidates to add the fewest experts not yet covered (so the
+    oracle fetches fewer experts), at least n distinct tokens."""
+    rng = np.random.default_rng(seed)
+    chosen = list(dict.fromkeys(int(t) for t in required))
+    have = np.zeros(E, bool)
+    for t in chosen:
+        have[idx[t]] = True
+    T = idx.shape[0]
+    while len(chosen) < n:
+        cand = rng.choice(T, 64, replace=False)
+        cand = [int(t) for t in cand if int(t) not in chosen]
+        new = [int(np.count_nonzero(~have[idx[t]])) for t in cand]
+        t = cand[int(np.argmin(new))]
+        chosen.append(t)
+        have[idx[t]] = True
+    return np.array(sorted(chosen))
+
+
+def expert_rows_backward(x, dy, idx, gate, ts, W1, W3, W2):
+    """dX and dgate of tokens ts by the oracle's per-expert backward: each
+    (token, slot) row of expert e goes through expert_backward with e's
+    weights (fetched once per expert), and a token's dX sums its slots."""
+    k = idx.shape[1]
+    dx = np.zeros((len(ts), x.shape[1]))
+    dg = np.zeros((len(ts), k))
+    by_e = {}
+    for i, t in enumerate(ts):
+        for j in range(k):
+            by_e.setdefault(int(idx[t, j]), []).append((i, j, int(t)))
+    for e, rows in sorted(by_e.items()):
+        tt = [t for _, _, t in rows]
+        eb = M.expert_backward(x[tt], dy[tt], np.array([gate[t, j] for _, j, t in rows]), W1[e], W3[e], W2[e])
+        for q, (i, j, _) in enumerate(rows):
+            dx[i] += eb["dxp"][q]
+            dg[i, j] = eb["dgate"][q]
+    return dx, dg
+
+
+def oracle_pool(n=8):
+    """A process pool for the MXFP8 oracle's per-expert work (the codec costs
+    about a second per expert matrix), started by spawn (the parent holds
+    the GPU) with two BLAS threads per worker; and a map that feeds it n
+    experts at a time, so at most n experts' weights are in flight."""
+    import multiprocessing as mp
+    import itertools
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+    os.environ["OMP_NUM_THREADS"] = os.environ["OPENBLAS_NUM_THREADS"] = "2"
+    try:
+        pool = mp.get_context("spawn").Pool(n)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+    def expert_map(fn, jobs):
+        jobs = iter(jobs)
+        done = 0
+        while True:
+            batch = list(itertools.islice(jobs, n))
+            if not batch:
+                return
+            yield from pool.starmap(fn, batch)
+            done += len(batch)
+            print(f"  oracle {fn.__name__}: {done} experts", flush=True)
+
+    return pool, expert_map
 
 
 @pytest.mark.parametrize("name", ["mixtral-bf16", "dsv3-bf16", "dsv3-fwdbwd-zipf"])
@@ -87,36 +178,34 @@ def test_fullsize_bf16(name):
         assert np.array_equal(host(sv[n]), want), n
     assert counts.sum() == w.R
 
-    ts = sample_tokens(w.T, 8, 1)
-    own = M.router_logits(x[ts], wr)
-    lt = logit_tolerance(x[ts], wr)
-    assert np.max(np.abs(own - logits[ts]) / lt[:, None]) < 1.0
+    ts8 = sample_tokens(w.T, 8, 1)
+    own = M.router_logits(x[ts8], wr)
+    lt = logit_tolerance(x[ts8], wr)
+    assert np.max(np.abs(own - logits[ts8]) / lt[:, None]) < 1.0
 
+    # 32+ tokens: the edges of the heaviest, a median and the lightest
+    # non-empty expert's row tiles, then tokens adding few new experts
+    order = np.argsort(counts, kind="stable")
+    nz = order[counts[order] > 0]
+    edges = [int(nz[-1]), int(nz[len(nz) // 2]), int(nz[0])]
+    ts = pick_tokens(idx, w.E, [0, w.T - 1] + edge_tokens(offsets, perm, w.k, edges), 32, 2)
     W1, W3, W2 = (DeviceExperts(dev[n]) for n in ("w1", "w3", "w2"))
     f = M.forward(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts])
     err = row_rel_err(host(y)[ts], f["y"])
-    print(f"  y sampled max row-rel err {err:.2e}", flush=True)
+    print(f"  y on {len(ts)} tokens max row-rel err {err:.2e}", flush=True)
     assert err <= BF16_TOL
     if not w.backward:
         return
     dy = host(inp["dy"])
-    # dX and dgate of the sampled tokens: the oracle's per-expert backward
-    # on each (token, slot) row, summed over the token's slots
-    want = {"dx": np.zeros((len(ts), w.d)), "dgate": np.zeros((len(ts), w.k))}
-    for i, t in enumerate(ts):
-        for j in range(w.k):
-            e = int(idx[t, j])
-            eb = M.expert_backward(x[[t]], dy[[t]], gate[t, [j]], W1[e], W3[e], W2[e])
-            want["dx"][i] += eb["dxp"][0]
-            want["dgate"][i, j] = eb["dgate"][0]
-    for n in ("dx", "dgate"):
-        e2 = (dgate_err if n == "dgate" else row_rel_err)(host(g[n])[ts], want[n])
-        print(f"  {n} sampled max row-rel err {e2:.2e}", flush=True)
-        assert e2 <= BF16_TOL, n
-    # weight gradients of the least-loaded expert and of a median one
-    order = np.argsort(counts, kind="stable")
+    want_dx, want_dg = expert_rows_backward(x, dy, idx, gate, ts, W1, W3, W2)
+    e1 = row_rel_err(host(g["dx"])[ts], want_dx)
+    e2 = dgate_err(host(g["dgate"])[ts], want_dg)
+    print(f"  dx on {len(ts)} tokens {e1:.2e}, dgate {e2:.2e}", flush=True)
+    assert e1 <= BF16_TOL and e2 <= BF16_TOL
+    # weight gradients of the lightest non-empty, a median and the heaviest
+    # expert (the heaviest runs the longest streamed weight-gradient band)
     g_row = gate.reshape(-1)[perm]
-    for e in (int(order[0]), int(order[len(order) // 2])):
+    for e in edges[::-1]:
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         rows = src[lo:hi]
         eb = M.expert_backward(x[rows], dy[rows], g_row[lo:hi], W1[e], W3[e], W2[e])
@@ -128,8 +217,10 @@ def test_fullsize_bf16(name):
 
 def test_fullsize_mxfp8():
     """dsv3-mxfp8 at full size: routing and layout over every token exact;
-    y of a sampled token against the oracle's MXFP8 forward, which quantises
-    that token's experts' bf16 weights itself."""
+    y of 64 tokens against the oracle's MXFP8 forward, which quantises those
+    tokens' experts' bf16 weights itself: the tokens of the row-tile edges
+    (first row, a tile boundary, the ragged tail) of eight experts, the
+    rest chosen to add few new experts."""
     from oracle import mxfp8 as Q
     w = synth.WORKLOADS["dsv3-mxfp8"]
     print(f"\nfull-size {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}", flush=True)
@@ -146,11 +237,19 @@ def test_fullsize_mxfp8():
     counts, offsets, perm, inv, src = M.layout(idx, w.E)
     for n, want in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)):
         assert np.array_equal(host(sv[n]), want), n
-    ts = np.array([w.T - 1])
+    order = np.argsort(counts, kind="stable")
+    edges = [int(e) for e in order[np.linspace(0, w.E - 1, 8).astype(int)] if counts[e] > 0]
+    ts = pick_tokens(idx, w.E, [w.T - 1] + edge_tokens(offsets, perm, w.k, edges), 64, 3)
+    assert len(np.unique(idx[ts])) >= 32
     W1, W3, W2 = (DeviceExperts(dev[n]) for n in ("w1", "w3", "w2"))
-    f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts])
+    pool, emap = oracle_pool()
+    try:
+        f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts],
+                            expert_map=emap)
+    finally:
+        pool.terminate()
     err = row_rel_err(host(y)[ts], f["y"])
-    print(f"  y sampled max row-rel err {err:.2e}", flush=True)
+    print(f"  y on {len(ts)} tokens ({len(np.unique(idx[ts]))} experts) max row-rel err {err:.2e}", flush=True)
     assert err <= 6e-2
 
 
@@ -185,10 +284,12 @@ def test_fullsize_router_backward():
 def test_fullsize_mxfp8_backward():
     """dsv3-fwdbwd-zipf-mxfp8 at full size (MXFP8 forward, MXFP8 data
     gradients, bf16 weight gradients), as bench.py runs it: routing exact;
-    dX and dgate of one sampled token against the oracle's MXFP8 forward and
-    backward over that token alone (its rows depend on nothing else); dW2 of
-    the least-loaded expert, which takes no quantised operand, against the
-    oracle's per-expert backward given the oracle's MXFP8 H."""
+    dX and dgate of 16 tokens (tile-edge tokens of the heaviest expert
+    included) against the oracle's MXFP8 forward and backward over those
+    tokens alone (their rows depend on nothing else); dW1, dW3 and dW2 of a
+    heavy expert (the third heaviest: a full streamed band) against the
+    oracle's per-expert MXFP8 backward over exactly that expert's rows, given
+    the oracle's MXFP8 A, B, H of those rows."""
     from oracle import mxfp8 as Q
     w = synth.WORKLOADS["dsv3-fwdbwd-zipf-mxfp8"]
     print(f"\nfull-size {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}", flush=True)
@@ -206,21 +307,28 @@ def test_fullsize_mxfp8_backward():
     assert np.array_equal(host(sv["topk_idx"]), idx)
     counts, offsets, perm, inv, src = M.layout(idx, w.E)
     assert np.array_equal(host(sv["perm"]), perm)
+    order = np.argsort(counts, kind="stable")
+    heavy = int(order[-1])
+    ts = pick_tokens(idx, w.E, [w.T // 3] + edge_tokens(offsets, perm, w.k, [heavy]), 16, 4)
     W1, W3, W2 = (DeviceExperts(dev[n]) for n in ("w1", "w3", "w2"))
-    ts = np.array([w.T // 3])
-    f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts])
-    b = Q.backward_mxfp8(dy[ts], x[ts], f, W1, W3, W2, w.k)
-    for n in ("dx", "dgate"):
-        e2 = (dgate_err if n == "dgate" else row_rel_err)(host(g[n])[ts], b[n])
-        print(f"  {n} sampled max row-rel err {e2:.2e}", flush=True)
-        assert e2 <= 6e-2, n
-    e = int(np.argsort(counts, kind="stable")[np.count_nonzero(counts == 0)])   # least-loaded with rows
-    lo, hi = int(offsets[e]), int(offsets[e + 1])
-    rows = src[lo:hi]
-    # the oracle's MXFP8 H of expert e's rows (x quantised along d, W1/W3 along d)
-    _, _, H_e, _ = Q.expert_ffn_mxfp8(Q.fake_quant(x[rows]), W1[e], W3[e], W2[e])
-    g_row = gate.reshape(-1)[perm][lo:hi]
-    dw2 = (g_row[:, None] * dy[rows]).T @ H_e
-    e3 = row_rel_err(host(g["dw2"][e]).reshape(1, -1), dw2.reshape(1, -1))
-    print(f"  dw2[{e}] ({hi - lo} rows) rel err {e3:.2e}", flush=True)
-    assert e3 <= 6e-2
+    pool, emap = oracle_pool()
+    try:
+        f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts],
+                            expert_map=emap)
+        b = Q.backward_mxfp8(dy[ts], x[ts], f, W1, W3, W2, w.k, expert_map=emap)
+        for n in ("dx", "dgate"):
+            e2 = (dgate_err if n == "dgate" else row_rel_err)(host(g[n])[ts], b[n])
+            print(f"  {n} on {len(ts)} tokens max row-rel err {e2:.2e}", flush=True)
+            assert e2 <= 6e-2, n
+        e = int(order[-3])
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows = src[lo:hi]
+        g_row = gate.reshape(-1)[perm][lo:hi]
+        A, B, H, _ = Q.expert_ffn_mxfp8(Q.quantize_tokens(x[rows]), W1[e], W3[e], W2[e])
+        eb = Q.expert_backward_mxfp8(x[rows], dy[rows], g_row, A, B, H, W1[e], W3[e], W2[e])
+    finally:
+        pool.terminate()
+    for n in ("dw1", "dw3", "dw2"):
+        e3 = row_rel_err(host(g[n][e]).reshape(1, -1), eb[n].reshape(1, -1))
+        print(f"  {n}[{e}] ({hi - lo} rows) rel err {e3:.2e}", flush=True)
+        assert e3 <= 6e-2, n
