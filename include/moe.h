@@ -280,6 +280,35 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
                 const moe_saved* saved, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch array moe_forward_noalloc works in. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same layer and the same results bit for bit, with the
+ * workspace in a static device array of MOE_NOALLOC_SCRATCH_BYTES (256 MiB)
+ * inside the library instead of a caller buffer.  Each GPU the library runs
+ * on holds its own array until the process ends; the call allocates nothing
+ * (no hipMalloc, no allocating library routine).
+ *   Arguments as in moe_forward, without workspace and workspace_bytes.
+ *   When the forward's workspace for all T tokens fits the array, one call
+ *   runs and every saved output may be asked for.  Otherwise the tokens
+ *   run in consecutive macrobatches of the most tokens whose workspace fits
+ *   (at most desc->macro_tokens when that is set), as moe_forward does for
+ *   desc->macro_tokens: y and the per-token saved outputs (logits, topk_idx,
+ *   gate, status) are written, and asking for the layout (counts, offsets,
+ *   perm, inv) or the activations (a, b, h), which describe one batch over
+ *   all T, returns MOE_ERR_WORKSPACE.  MOE_ERR_WORKSPACE is also returned
+ *   when not one token's workspace fits the array (d, E or I too large).
+ * Every call on a GPU uses that GPU's one array, which keeps the previous
+ * call's contents (the call clears what must start at zero): calls that
+ * overlap in time on one GPU, on any streams, race and give undefined
+ * results.  Thread-safe to call from several host threads as long as their
+ * calls do not overlap on the device. */
+MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const void* wr,
+                                const float* bias, const moe_weights* w, void* y,
+                                const moe_saved* saved, void* stream);
+
 /* Backward of the expert path with the routing frozen (MoK flash §01/§02:
  * pull reverse-combine, expert dgrad and wgrad, push reverse-dispatch).
  * bf16 activations; bf16 or MXFP8 experts (below).

@@ -75,6 +75,8 @@ _lib.moe_quantize_mxfp8_t.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, 
                                       c_void_p, c_void_p, c_void_p]
 _lib.moe_forward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWeights),
                              c_void_p, _P(MoeSaved), c_void_p, ctypes.c_size_t, c_void_p]
+_lib.moe_forward_noalloc.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWeights),
+                                     c_void_p, _P(MoeSaved), c_void_p]
 _lib.moe_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, _P(MoeWeights), _P(MoeSaved),
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               ctypes.c_size_t, c_void_p]
@@ -84,12 +86,14 @@ _lib.moe_router_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, 
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_status_string.restype = ctypes.c_char_p
 for _f in ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather", "moe_quantize_mxfp8",
-           "moe_quantize_mxfp8_t", "moe_forward", "moe_backward", "moe_router_backward"):
+           "moe_quantize_mxfp8_t", "moe_forward", "moe_forward_noalloc", "moe_backward",
+           "moe_router_backward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather",
-           "moe_quantize_mxfp8", "moe_quantize_mxfp8_t", "moe_forward", "moe_backward",
-           "moe_router_backward", "moe_status_string")
+           "moe_quantize_mxfp8", "moe_quantize_mxfp8_t", "moe_forward", "moe_forward_noalloc",
+           "moe_backward", "moe_router_backward", "moe_status_string")
+MOE_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class MoeError(RuntimeError):
@@ -181,6 +185,12 @@ def moe_forward(desc, x, wr, bias, weights: MoeWeights, y, saved: MoeSaved | Non
                             _p(y), None if saved is None else ctypes.byref(saved), _p(workspace),
                             0 if workspace is None else workspace.numel(), _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_noalloc(desc, x, wr, bias, weights: MoeWeights, y, saved: MoeSaved | None, stream=None):
+    _check(_lib.moe_forward_noalloc(ctypes.byref(desc), _p(x), _p(wr), _p(bias), ctypes.byref(weights),
+                                    _p(y), None if saved is None else ctypes.byref(saved), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_backward(desc, dy, x, weights: MoeWeights, saved: MoeSaved, dx, dw1, dw3, dw2, dgate,

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 
 #include <string.h>
+
+#include <mutex>
 #include <type_traits>
 
 #include "plan.h"
@@ -25,7 +27,7 @@ namespace moe {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int make_plan(const moe_desc* D, Plan* p) {
+int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
   if (!D || !p) return MOE_ERR_INVALID_ARG;
   memset(p, 0, sizeof(*p));
   if (D->T < 0 || D->macro_tokens < 0) return MOE_ERR_INVALID_ARG;
@@ -123,7 +125,7 @@ int make_plan(const moe_desc* D, Plan* p) {
   p->o_xs = p->mxfp8 ? take((size_t)T * (d / 32)) : 0;
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
-  if (p->bwd_ok) {
+  if (p->bwd_ok && !fwd_only) {
     p->o_gg = take(R * d * 2);
     p->o_zero = take(((size_t)2 * I + d + 256) * 2);
     p->o_dab = take(R * 2 * I * 2);
@@ -135,9 +137,11 @@ int make_plan(const moe_desc* D, Plan* p) {
       p->o_dabs = take(R * 2 * (I / 32));
     }
   }
-  p->o_rdz = take(R * 4);
-  p->o_rpart = take((size_t)kRbSplits * E * d * 4);
-  p->o_rpbias = take((size_t)kRbSplits * E * 4);
+  if (!fwd_only) {
+    p->o_rdz = take(R * 4);
+    p->o_rpart = take((size_t)kRbSplits * E * d * 4);
+    p->o_rpbias = take((size_t)kRbSplits * E * 4);
+  }
   p->total = o;
   return MOE_OK;
 }
@@ -970,6 +974,73 @@ static int forward_call(const Plan& p, const moe_desc* desc, const void* x, cons
   return forward_impl<bf16_t, TileD256>(p, desc, F, st);
 }
 
+// Macrobatches: the forward over consecutive ranges of Tm tokens (the last
+// one ragged), each reusing the workspace (stream order keeps each one
+// after the previous).  Per-token outputs only (no layout over all tokens).
+static int forward_in_batches(const moe_desc* desc, int Tm, const void* x, const void* wr, const float* bias,
+                              const moe_weights* w, void* y, const moe_saved* saved, void* workspace,
+                              hipStream_t st) {
+  const int T = desc->T, E = desc->E, k = desc->k, d = desc->d;
+  const size_t es = desc->act_dtype == MOE_F32 ? 4 : 2;
+  for (int t0 = 0; t0 < T; t0 += Tm) {
+    moe_desc md = *desc;
+    md.T = T - t0 < Tm ? T - t0 : Tm;
+    md.macro_tokens = 0;
+    Plan pm;
+    int rc = make_plan(&md, &pm, true);  // the forward's regions only
+    if (rc != MOE_OK) return rc;
+    moe_saved sm;
+    memset(&sm, 0, sizeof(sm));
+    if (saved) {
+      sm.logits = saved->logits ? saved->logits + (size_t)t0 * E : nullptr;
+      sm.topk_idx = saved->topk_idx ? saved->topk_idx + (size_t)t0 * k : nullptr;
+      sm.gate = saved->gate ? saved->gate + (size_t)t0 * k : nullptr;
+      sm.status = saved->status;
+    }
+    rc = forward_call(pm, &md, (const char*)x + (size_t)t0 * d * es, wr, bias, w, (char*)y + (size_t)t0 * d * es,
+                      saved ? &sm : nullptr, workspace, st);
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ no-alloc
+// The forward's workspace in a static device array, for callers that cannot
+// allocate.  Each device the library runs on holds its own copy until the
+// process ends; host code reaches it only through the address
+// hipGetSymbolAddress gives on that device (the array's name is a host-side
+// stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device, looked up once
+// per device with that device current.
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Forward workspace bytes of T tokens, or 0 for an invalid descriptor.
+static size_t forward_bytes(const moe_desc* desc, int T) {
+  moe_desc md = *desc;
+  md.T = T;
+  md.macro_tokens = 0;
+  Plan q;
+  return make_plan(&md, &q, true) == MOE_OK ? q.total : 0;
+}
+
 int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float* bias, const moe_weights* w,
                 void* y, const moe_saved* saved, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
@@ -980,31 +1051,48 @@ int moe_forward(const moe_desc* desc, const void* x, const void* wr, const float
   if (!workspace || workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (!p.macro) return forward_call(p, desc, x, wr, bias, w, y, saved, workspace, st);
-  // Macrobatches: the same call over consecutive token ranges, reusing the
-  // workspace (stream order keeps each macrobatch after the previous one).
   if (saved && (saved->counts || saved->offsets || saved->perm || saved->inv || saved->a || saved->b || saved->h))
     return MOE_ERR_INVALID_ARG;
-  const size_t es = p.act_es;
-  for (int t0 = 0; t0 < p.T_full; t0 += p.T) {
-    moe_desc md = *desc;
-    md.T = p.T_full - t0 < p.T ? p.T_full - t0 : p.T;
-    md.macro_tokens = 0;
-    Plan pm;
-    rc = make_plan(&md, &pm);
-    if (rc != MOE_OK) return rc;
-    moe_saved sm;
-    memset(&sm, 0, sizeof(sm));
-    if (saved) {
-      sm.logits = saved->logits ? saved->logits + (size_t)t0 * p.E : nullptr;
-      sm.topk_idx = saved->topk_idx ? saved->topk_idx + (size_t)t0 * p.k : nullptr;
-      sm.gate = saved->gate ? saved->gate + (size_t)t0 * p.k : nullptr;
-      sm.status = saved->status;
+  return forward_in_batches(desc, p.T, x, wr, bias, w, y, saved, workspace, st);
+}
+
+int moe_forward_noalloc(const moe_desc* desc, const void* x, const void* wr, const float* bias,
+                        const moe_weights* w, void* y, const moe_saved* saved, void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p, true);
+  if (rc != MOE_OK) return rc;
+  if (!w || (p.T > 0 && (!x || !wr || !y || !w->w1 || !w->w3 || !w->w2))) return MOE_ERR_INVALID_ARG;
+  if (p.mxfp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != MOE_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  // tokens per call: all of them when their workspace fits (and the caller
+  // asked for no macrobatches), else the most that fit, at most macro_tokens
+  const int T = desc->T;
+  int Tm = p.macro ? p.T : T;
+  if (forward_bytes(desc, Tm) > MOE_NOALLOC_SCRATCH_BYTES || forward_bytes(desc, Tm) == 0) {
+    int lo = 0, hi = Tm;  // largest fitting count in (lo, hi)
+    while (hi - lo > 1) {
+      const int mid = lo + (hi - lo) / 2;
+      const size_t b = forward_bytes(desc, mid);
+      if (b != 0 && b <= MOE_NOALLOC_SCRATCH_BYTES) lo = mid; else hi = mid;
     }
-    rc = forward_call(pm, &md, (const char*)x + (size_t)t0 * p.d * es, wr, bias, w,
-                      (char*)y + (size_t)t0 * p.d * es, saved ? &sm : nullptr, workspace, st);
-    if (rc != MOE_OK) return rc;
+    Tm = lo;
   }
-  return MOE_OK;
+  if (T > 0 && Tm < 1) return MOE_ERR_WORKSPACE;  // not one token's workspace fits
+  if (Tm >= T) {
+    moe_desc md = *desc;
+    md.macro_tokens = 0;
+    Plan pf;
+    rc = make_plan(&md, &pf, true);
+    if (rc != MOE_OK) return rc;
+    return forward_call(pf, &md, x, wr, bias, w, y, saved, ws, st);
+  }
+  // the layout and the saved activations describe one batch over all T
+  if (saved && (saved->counts || saved->offsets || saved->perm || saved->inv || saved->a || saved->b || saved->h))
+    return MOE_ERR_WORKSPACE;
+  return forward_in_batches(desc, Tm, x, wr, bias, w, y, saved, ws, st);
 }
 
 int moe_backward(const moe_desc* desc, const void* dy, const void* x, const moe_weights* w, const moe_saved* saved,

@@ -46,6 +46,7 @@ enum CtrSlot {
   C_QUEUE = 0, C_ABORT, C_R2, C_SCAN, C_G2, C_NMT, C_AUX3, C_QDONE, C_HEADER = 16
 };
 
-int make_plan(const moe_desc* d, Plan* p);
+// fwd_only: carve only the regions the forward uses (moe_forward_noalloc)
+int make_plan(const moe_desc* d, Plan* p, bool fwd_only = false);
 
 }  // namespace moe
