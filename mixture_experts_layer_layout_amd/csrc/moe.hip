@@ -273,12 +273,24 @@ __global__ void __launch_bounds__(256) k_gather(Fwd F) {
   gather_tile<Act, COPY, false>(F, tile, ssrc);
 }
 
+// The default bf16 tile takes its 64-row variant for row tiles of at most
+// 64 rows.
+template <class TL>
+constexpr bool has_half_tile() {
+  return std::is_same<TL, TileD256>::value;
+}
+
 template <class Act, class TL>
 __device__ __forceinline__ void run_g1(const Fwd& F, int tile, int nt, char* smem) {
   if constexpr (std::is_same<Act, float>::value)
     g1_tile_f32(F, tile, nt, (float*)smem);
   else if constexpr (TL::kMX)
     g1_tile_mx<TL>(F, tile, nt, (bf16_t*)smem);
+  else if constexpr (has_half_tile<TL>())
+    if (fwd_tile(F, tile).n <= TileD256h::BM)
+      g1_tile_bf16<TileD256h>(F, tile, nt, (bf16_t*)smem);
+    else
+      g1_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
   else
     g1_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
 }
@@ -288,6 +300,11 @@ __device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* sme
     g2_tile_f32(F, tile, nt, (float*)smem);
   else if constexpr (TL::kMX)
     g2_tile_mx<TL>(F, tile, nt, (bf16_t*)smem);
+  else if constexpr (has_half_tile<TL>())
+    if (fwd_tile(F, tile).n <= TileD256h::BM)
+      g2_tile_bf16<TileD256h>(F, tile, nt, (bf16_t*)smem);
+    else
+      g2_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
   else
     g2_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
 }

@@ -39,6 +39,10 @@
 namespace moe {
 
 typedef Tile<128, 128> TileDH;  // row tiles: dh, dxp
+// Row tiles holding at most 64 rows (the tail of an expert, or a whole
+// lightly loaded expert) run on a 64-row tile of the same width: the same
+// weight columns are streamed, with half the matrix-core work on padding.
+typedef Tile<64, 128> TileDH64;
 typedef Tile<128, 128> TileDW;  // weight-gradient tiles: dw2, dw13
 constexpr int kPrepTok = 8;     // tokens per row-preparation task
 constexpr int kWgradPerTicket = 8;  // column tiles per weight-gradient task (one band)
@@ -241,8 +245,8 @@ __device__ __forceinline__ TileRows bwd_tile(const Bwd& B, int tile) {
   return tile_rows(B.tile_e, B.tile_r0, B.tile_n, tile, B.max_tiles, B.E, B.R, B.BM);
 }
 
-__device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*) {
-  typedef TileDH TL;
+template <class TL>
+__device__ void bwd_dh_tile_t(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const TileRows tr = bwd_tile(B, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
   if (n <= 0) return;
@@ -258,10 +262,17 @@ __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*
   bwd_dh_epilogue<TL>(B, acc, r0, n, nt, smem);
 }
 
+__device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*) {
+  if (bwd_tile(B, tile).n <= TileDH64::BM)
+    bwd_dh_tile_t<TileDH64>(B, tile, nt, smem);
+  else
+    bwd_dh_tile_t<TileDH>(B, tile, nt, smem);
+}
+
 // ---------------------------------------------------------------- dxp
 // dXp = [dA | dB] [W1_e ; W3_e] for one (row tile, d tile).
-__device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
-  typedef TileDH TL;
+template <class TL>
+__device__ void bwd_dxp_tile_t(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const TileRows tr = bwd_tile(B, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
   if (n <= 0) return;
@@ -279,6 +290,13 @@ __device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const Staged<TL::BM, TL::BN> st{smem};
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
   st.flush(n, [&](int row) { return B.dxp + (size_t)(r0 + row) * d + c0; });
+}
+
+__device__ void bwd_dxp_tile(const Bwd& B, int tile, int nt, bf16_t* smem) {
+  if (bwd_tile(B, tile).n <= TileDH64::BM)
+    bwd_dxp_tile_t<TileDH64>(B, tile, nt, smem);
+  else
+    bwd_dxp_tile_t<TileDH>(B, tile, nt, smem);
 }
 
 // A weight-gradient band: experts with at most 128 rows keep the band's A

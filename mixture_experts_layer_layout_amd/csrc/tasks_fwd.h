@@ -39,6 +39,10 @@ constexpr int kMaxK = 16;
 typedef Tile<128, 128> TileB128;   // 64 KB of LDS: two workgroups per CU
 typedef Tile<256, 128> TileB256;
 typedef TileD<128, 256> TileD256;  // direct-to-LDS ring, 144 KB: one workgroup per CU
+// Row tiles of at most 64 rows (an expert's tail, or a whole lightly loaded
+// expert) run on a 64-row tile of the same width: the same weight columns
+// stream through the ring, with half the matrix-core work on padding.
+typedef TileD<64, 256> TileD256h;
 
 struct Sync {
   int* queue;    // start of the counter region
