@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--stage-rows", type=int, default=0)
     ap.add_argument("--flags", type=lambda v: int(v, 0), default=0, help="moe_desc.flags (MOE_FLAG_*)")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: occupancy limit)")
+    ap.add_argument("--producer-cus", type=int, default=0,
+                    help="CU partition of the fused forward: CUs whose workgroups run only routing, "
+                         "layout, gather and combine (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -245,7 +248,7 @@ def main():
     bweights, bkeep = layer.backward_weights_of(w, dev) if w.backward else (None, {})
     saved = layer.alloc_saved(w, "cuda", full=w.backward)
     desc = layer.desc_for(w, fused=fused, stage_rows=args.stage_rows, flags=args.flags,
-                          n_workgroups=args.workgroups)
+                          n_workgroups=args.workgroups, n_producer_cus=args.producer_cus)
     ws = layer.workspace(desc)
     y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if w.act == "bf16" else torch.float32, device="cuda")
     if w.backward:
@@ -432,6 +435,7 @@ def main():
             "config": {"workload": w.name + (" fwd+bwd" if w.backward else " fwd"), "T": w.T, "d": w.d,
                        "E": w.E, "k": w.k, "I": w.I, "score": w.score, "fused": fused,
                        "stage_rows": args.stage_rows, "flags": args.flags, "workgroups": args.workgroups,
+                       "producer_cus": args.producer_cus,
                        "macro_tokens": args.macro_tokens},
             "roofline": roof, "cpu_baseline": cpu, "phases": phases,
             "input_gen_s": round(t_gen, 1), "source_sha256": source_digest()}

@@ -87,8 +87,8 @@ typedef struct moe_desc {
   int32_t fused;         /* 1: persistent launches driven by device-side
                             ready counters; 0: one launch per step          */
   int32_t stage_rows;    /* rows per ready counter (the minibatch handed to
-                            the expert GEMM): 0 = auto, else 128 or 256
-                            (MXFP8 experts: 0 or 128)                      */
+                            the expert GEMM): 0 = auto (128), else 64, 128
+                            or 256 (MXFP8 experts: 0 or 128)               */
   int32_t n_workgroups;  /* persistent grid size, 0 = auto (all CUs)       */
   uint32_t flags;        /* MOE_FLAG_* below                                */
   /* DeepSeek-V3-style routing options (0 = off):
@@ -115,6 +115,15 @@ typedef struct moe_desc {
    * and status are written.  The other calls return MOE_ERR_UNSUPPORTED
    * for such a descriptor. */
   int32_t macro_tokens;
+  /* n_producer_cus > 0: CU partition of the fused forward (MoK flash §02:
+   * compute units split between moving tokens and the expert FFN).  The
+   * first n_producer_cus x (workgroups per CU) workgroups of the persistent
+   * grid run only the routing, layout, gather and combine tasks, the others
+   * only the expert GEMM tiles.  0 = no partition: every workgroup claims
+   * every phase.  With a partition both sides must be resident at once, so
+   * n_workgroups may not exceed the resident limit (else
+   * MOE_ERR_INVALID_ARG), and at least one GEMM workgroup must remain. */
+  int32_t n_producer_cus;
 } moe_desc;
 
 /* Flags. */
@@ -130,6 +139,10 @@ typedef struct moe_desc {
                                       gradients after the rest           */
 #define MOE_FLAG_PERSISTENT_SINGLE 0x8u /* fused forward and backward: every
                                       phase in one persistent launch     */
+#define MOE_FLAG_PERSISTENT_GEMM_APART 0x800u /* fused forward: the down
+                                      projection in a persistent launch of
+                                      its own (routing .. up projection |
+                                      down projection | combine)         */
 #define MOE_FLAG_BIAS_SELECT_ONLY 0x10u /* the router bias steers the
                                       selection only: experts ranked by
                                       sigmoid(logit) + bias, gates from the
@@ -269,12 +282,16 @@ MOE_API int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, i
  *         FFN_e(v) = (silu(v W1_e^T) * (v W3_e^T)) W2_e^T;
  *   saved optional outputs (may be NULL).
  * With desc->fused = 1 the layer runs as tasks claimed from device-side
- * queues phase by phase (after a small clearing launch), in three
- * persistent launches: routing, counting, layout, gather and the up
- * projection, where an up-projection tile starts as soon as the ready
- * counter of its rows shows them staged (MoK flash §02); the down
- * projection; the combine.  MOE_FLAG_PERSISTENT_SINGLE puts all phases in
- * one launch, MOE_FLAG_PERSISTENT_SPLIT gives each phase group its own. */
+ * queues phase by phase (after a small clearing launch): one persistent
+ * launch runs routing, counting, layout, gather and both projections, an
+ * up-projection tile starting as soon as the ready counter of its rows
+ * shows them staged and a down-projection tile as soon as every
+ * up-projection tile of its rows has stored H (MoK flash §02: GPU-local
+ * counters); the combine follows as a plain launch.  MXFP8 experts run the
+ * down projection in a persistent launch of its own by default.
+ * MOE_FLAG_PERSISTENT_SINGLE puts the combine in the persistent launch too,
+ * MOE_FLAG_PERSISTENT_GEMM_APART gives the down projection its own launch,
+ * MOE_FLAG_PERSISTENT_SPLIT gives each phase group its own. */
 MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
                 const float* bias, const moe_weights* w, void* y,
                 const moe_saved* saved, void* workspace,

@@ -37,6 +37,7 @@ MOE_FLAG_BIAS_SELECT_ONLY = 0x10
 MOE_FLAG_SPIN_LIMIT_TINY = 0x100
 MOE_FLAG_TEST_DROP_READY = 0x200
 MOE_FLAG_TEST_SHUFFLE_CLAIMS = 0x400
+MOE_FLAG_PERSISTENT_GEMM_APART = 0x800
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
 _SC = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
@@ -48,7 +49,8 @@ class MoeDesc(ctypes.Structure):
                 ("score", c_int32), ("renorm", c_int32), ("fused", c_int32),
                 ("stage_rows", c_int32), ("n_workgroups", c_int32),
                 ("flags", ctypes.c_uint32), ("n_group", c_int32), ("topk_group", c_int32),
-                ("routed_scale", ctypes.c_float), ("macro_tokens", c_int32)]
+                ("routed_scale", ctypes.c_float), ("macro_tokens", c_int32),
+                ("n_producer_cus", c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -123,10 +125,10 @@ def _stream(stream):
 
 def make_desc(T, d, E, k, I, act="bf16", experts="bf16", score="sigmoid", renorm=True,
               fused=True, stage_rows=0, n_workgroups=0, flags=0, n_group=0, topk_group=0,
-              routed_scale=0.0, macro_tokens=0) -> MoeDesc:
+              routed_scale=0.0, macro_tokens=0, n_producer_cus=0) -> MoeDesc:
     return MoeDesc(T, d, E, k, I, _DT[act], _DT[experts], _SC[score], int(bool(renorm)),
                    int(bool(fused)), stage_rows, n_workgroups, flags, n_group, topk_group,
-                   routed_scale, macro_tokens)
+                   routed_scale, macro_tokens, n_producer_cus)
 
 
 def moe_workspace_size(desc: MoeDesc) -> int:

@@ -161,6 +161,35 @@ __device__ __forceinline__ void signal_add(int* ctr, int v) {
   }
 }
 
+// Cache policy of a store written through the XCD's L2 to memory, coherent
+// at agent scope (the sc1 bit, as the compiler sets it on agent-scope atomic
+// stores): a workgroup on another XCD that has not cached the line reads
+// the stored value from memory.
+constexpr int kStoreCoherent = 16;
+
+// Block-uniform: adds `v` to *ctr once every wave's earlier stores have
+// completed.  For data stored coherently (kStoreCoherent) this publishes it
+// to readers in the same launch without writing any L2 back: each wave waits
+// for its stores (s_waitcnt vmcnt(0): a coherent store completes once it is
+// performed in memory), the barrier orders the waves, and the count follows.
+__device__ __forceinline__ void signal_add_stored(int* ctr, int v) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes stored coherently (kStoreCoherent) at byte offset `off` of a
+// buffer whose base is the same in every lane.
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rs, int off, uint4 v) {
+  typedef unsigned int u32x4_t __attribute__((__vector_size__(16)));
+  u32x4_t q;
+  q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+  __builtin_amdgcn_raw_buffer_store_b128(q, rs, off, 0, kStoreCoherent);
+}
+__device__ __forceinline__ void store_coherent_u8(__amdgpu_buffer_rsrc_t rs, int off, uint8_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, rs, off, 0, kStoreCoherent);
+}
+
 // ---------------------------------------------------------------- copies
 // One wave copies one row of nvec 16-byte vectors: every lane issues up to
 // kCopyUnroll loads before its first store (the source and destination may

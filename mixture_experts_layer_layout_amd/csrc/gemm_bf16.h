@@ -676,6 +676,20 @@ struct Staged {
       if (row < nrows) *(uint4*)(dst(row) + ch * 8) = *(const uint4*)(s + row * LD + ch * 8);
     }
   }
+  // The same block written coherently (kStoreCoherent) to rows `ld`
+  // elements apart from `base` (the block's first element of its first
+  // row; the block spans less than 2^31 bytes), for a reader in the same
+  // launch (signal_add_stored).
+  __device__ __forceinline__ void flush_coherent(int nrows, bf16_t* base, size_t ld) const {
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(wave_uniform(base));
+    constexpr int CPR = W / 8;
+    for (int c = threadIdx.x; c < ROWS * CPR; c += kThreads) {
+      const int row = c / CPR, ch = c % CPR;
+      if (row < nrows)
+        store_coherent(rs, (int)(((size_t)row * ld + ch * 8) * sizeof(bf16_t)), *(const uint4*)(s + row * LD + ch * 8));
+    }
+  }
 };
 
 // Map a B-tile row of the SwiGLU tile to (which, out_col): which 0 = W1,

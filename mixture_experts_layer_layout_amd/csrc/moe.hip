@@ -48,7 +48,9 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
   } else {
     return MOE_ERR_INVALID_ARG;
   }
-  if (D->stage_rows != 0 && D->stage_rows != 128 && D->stage_rows != 256) return MOE_ERR_UNSUPPORTED;
+  if (D->stage_rows != 0 && D->stage_rows != 64 && D->stage_rows != 128 && D->stage_rows != 256)
+    return MOE_ERR_UNSUPPORTED;
+  if (D->n_producer_cus < 0) return MOE_ERR_INVALID_ARG;
   // routing options
   if (D->n_group < 0 || D->topk_group < 0 || !(D->routed_scale >= 0.0f) || D->routed_scale > 3.0e38f)
     return MOE_ERR_INVALID_ARG;
@@ -74,7 +76,7 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
     // column tiles: the bf16 forward with 128-row tiles uses the 256-wide
     // direct-to-LDS tile, the others 128-wide tiles
     if (p->mxfp8 && p->BM != 128) return MOE_ERR_UNSUPPORTED;  // MXFP8 tiles have 128 rows
-    const int bn = (!p->mxfp8 && p->BM == 128) ? TileD256::BN : TileB128::BN;
+    const int bn = (!p->mxfp8 && p->BM <= 128) ? TileD256::BN : TileB128::BN;
     p->nN1 = I / (bn / 2);
     p->nN2 = d / bn;
   }
@@ -280,33 +282,34 @@ constexpr bool has_half_tile() {
   return std::is_same<TL, TileD256>::value;
 }
 
-template <class Act, class TL>
+// CO: the tile's output has a reader in the same launch (stored coherently).
+template <class Act, class TL, bool CO>
 __device__ __forceinline__ void run_g1(const Fwd& F, int tile, int nt, char* smem) {
   if constexpr (std::is_same<Act, float>::value)
-    g1_tile_f32(F, tile, nt, (float*)smem);
+    g1_tile_f32<CO>(F, tile, nt, (float*)smem);
   else if constexpr (TL::kMX)
-    g1_tile_mx<TL>(F, tile, nt, (bf16_t*)smem);
+    g1_tile_mx<TL, CO>(F, tile, nt, (bf16_t*)smem);
   else if constexpr (has_half_tile<TL>())
     if (fwd_tile(F, tile).n <= TileD256h::BM)
-      g1_tile_bf16<TileD256h>(F, tile, nt, (bf16_t*)smem);
+      g1_tile_bf16<TileD256h, CO>(F, tile, nt, (bf16_t*)smem);
     else
-      g1_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
+      g1_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
   else
-    g1_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
+    g1_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
 }
-template <class Act, class TL>
+template <class Act, class TL, bool CO>
 __device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* smem) {
   if constexpr (std::is_same<Act, float>::value)
-    g2_tile_f32(F, tile, nt, (float*)smem);
+    g2_tile_f32<CO>(F, tile, nt, (float*)smem);
   else if constexpr (TL::kMX)
-    g2_tile_mx<TL>(F, tile, nt, (bf16_t*)smem);
+    g2_tile_mx<TL, CO>(F, tile, nt, (bf16_t*)smem);
   else if constexpr (has_half_tile<TL>())
     if (fwd_tile(F, tile).n <= TileD256h::BM)
-      g2_tile_bf16<TileD256h>(F, tile, nt, (bf16_t*)smem);
+      g2_tile_bf16<TileD256h, CO>(F, tile, nt, (bf16_t*)smem);
     else
-      g2_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
+      g2_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
   else
-    g2_tile_bf16<TL>(F, tile, nt, (bf16_t*)smem);
+    g2_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
 }
 
 __global__ void __launch_bounds__(256) k_quant_tokens(Fwd F) { quant_tokens(F, blockIdx.x); }
@@ -318,7 +321,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_g1(Fwd F) {
   if (id >= *F.s.n_mtiles * F.nN1) return;
   int tile, nt;
   raster_decode(F.etile, F.E, F.nN1, id, tile, nt);
-  run_g1<Act, TL>(F, tile, nt, smem);
+  run_g1<Act, TL, false>(F, tile, nt, smem);
 }
 
 template <class Act, class TL>
@@ -328,7 +331,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_g2(Fwd F) {
   if (id >= *F.s.n_mtiles * F.nN2) return;
   int tile, nt;
   raster_decode(F.etile, F.E, F.nN2, id, tile, nt);
-  run_g2<Act, TL>(F, tile, nt, smem);
+  run_g2<Act, TL, false>(F, tile, nt, smem);
 }
 
 // The combine as a plain launch after the persistent ones: nothing to merge
@@ -348,11 +351,23 @@ __global__ void __launch_bounds__(256) k_combine(Fwd F) {
 // A task's signal releases its stores at agent scope only when a phase
 // that reads them runs in this launch (MASK); readers in later launches see
 // them through the kernel boundary.
+// Phases a workgroup claims under the CU partition: producers (workgroups
+// below n_prod) routing, layout, gather and combine; consumers the GEMMs.
+constexpr unsigned kProducerPhases = 0x4Fu, kConsumerPhases = 0x30u;
+
+// Each workgroup copies the row-tile boundaries of the experts (etile, E+1
+// ints) into LDS at its first GEMM task, for the raster decode's binary
+// search (eight dependent global loads per task otherwise).
+constexpr int kEtileLds = kMaxE + 1;
+
 template <class Act, class TL, unsigned MASK>
 __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   __shared__ Claim c;
   __shared__ int s_flag;
+  __shared__ int s_etile[kEtileLds];
+  bool etile_lds = false;
+  const unsigned roles = F.n_prod == 0 ? 0x7Fu : ((int)blockIdx.x < F.n_prod ? kProducerPhases : kConsumerPhases);
   if (threadIdx.x == 0) {
     c.phase = 0;
     c.qoff = 0;
@@ -367,6 +382,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         per = 1;
         groups = 0;
         if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
+        if (!((roles >> ph) & 1u)) return true;  // phase of the other side of the partition
         if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0); return true; }
         if (ph == 1) { groups = F.nb * kTopkChunks; return true; }
         if (ph == 2) { groups = 1; return true; }
@@ -388,6 +404,12 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
     const WaitCtx W = wctx(F.s);
     const int s_nmt = c.nmt;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if ((ph == 4 || ph == 5) && !etile_lds) {
+      // the layout is complete (the claim waited for it)
+      for (int e = threadIdx.x; e <= F.E; e += kThreads) s_etile[e] = F.etile[e];
+      __syncthreads();
+      etile_lds = true;
+    }
     // A task whose wait fails (timeout or abort) does no work and raises
     // no counter (protocol.h).
     if ((MASK & 1u) && ph == 0) {
@@ -416,17 +438,25 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
     } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * F.nN1) continue;
       int tile, nt;
-      raster_decode(F.etile, F.E, F.nN1, t, tile, nt);
+      raster_decode(s_etile, F.E, F.nN1, t, tile, nt);
       if (!wait_geq(&F.s.ready[tile], 1, W, &s_flag)) continue;
-      run_g1<Act, TL>(F, tile, nt, smem);
-      signal_add<(MASK & 32u) != 0>(&F.s.h_cnt[tile], 1);
+      run_g1<Act, TL, (MASK & 32u) != 0>(F, tile, nt, smem);
+      // H (or its codes) is stored coherently: with the down projection in
+      // this launch the count waits for those stores, with no L2 write-back
+      if constexpr ((MASK & 32u) != 0)
+        signal_add_stored(&F.s.h_cnt[tile], 1);
+      else
+        signal_add<false>(&F.s.h_cnt[tile], 1);
     } else if ((MASK & 32u) && ph == 5) {
       if (t >= s_nmt * F.nN2) continue;
       int tile, nt;
-      raster_decode(F.etile, F.E, F.nN2, t, tile, nt);
+      raster_decode(s_etile, F.E, F.nN2, t, tile, nt);
       if (!wait_geq(&F.s.h_cnt[tile], F.nN1, W, &s_flag)) continue;
-      run_g2<Act, TL>(F, tile, nt, smem);
-      signal_add<(MASK & 64u) != 0>(F.s.g2_done, 1);
+      run_g2<Act, TL, (MASK & 64u) != 0>(F, tile, nt, smem);
+      if constexpr ((MASK & 64u) != 0)
+        signal_add_stored(F.s.g2_done, 1);  // rows stored coherently
+      else
+        signal_add<false>(F.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
       if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
     }
@@ -543,6 +573,8 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   __shared__ Claim c;
   __shared__ int s_flag;
+  __shared__ int s_etile[(MASK & 0x14u) ? kEtileLds : 1];  // dh and dxp tiles only
+  bool etile_lds = false;
   if (threadIdx.x == 0) {
     c.phase = 0;
     c.qoff = 0;
@@ -578,6 +610,14 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
     if (t < 0) break;
     const WaitCtx W = wctx(B.s);
     const int s_nmt = c.nmt;
+    if constexpr ((MASK & 0x14u) != 0) {
+      if ((ph == 2 || ph == 4) && !etile_lds) {
+        // the row tiles are listed (the claim waited for setup)
+        for (int e = threadIdx.x; e <= B.E; e += kThreads) s_etile[e] = B.etile[e];
+        __syncthreads();
+        etile_lds = true;
+      }
+    }
     const int g2 = B.nW2m * cdiv(B.nW2n, kWgradPerTicket), g13 = B.nW13m * cdiv(B.nW13n, kWgradPerTicket);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if ((MASK & 1u) && ph == 0) {
@@ -603,7 +643,7 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
     } else if ((MASK & 4u) && ph == 2) {
       if (t >= s_nmt * B.nNdh) continue;
       int tile, nt;
-      raster_decode(B.etile, B.E, B.nNdh, t, tile, nt);
+      raster_decode(s_etile, B.E, B.nNdh, t, tile, nt);
       if constexpr (MX)
         bwd_dh_tile_mx(B, tile, nt, (bf16_t*)smem);
       else
@@ -615,7 +655,7 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
     } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * B.nNdx) continue;
       int tile, nt;
-      raster_decode(B.etile, B.E, B.nNdx, t, tile, nt);
+      raster_decode(s_etile, B.E, B.nNdx, t, tile, nt);
       if (!wait_geq(&B.s.h_cnt[tile], B.nNdh, W, &s_flag)) continue;
       if constexpr (MX)
         bwd_dxp_tile_mx(B, tile, nt, (bf16_t*)smem);
@@ -662,10 +702,21 @@ static int launch_status() {
 }
 
 template <class Act, class TL, unsigned MASK>
-static int launch_fused_fwd(const moe_desc* D, const Fwd& F, size_t smem, hipStream_t st) {
+static int launch_fused_fwd(const moe_desc* D, const Fwd& F0, size_t smem, hipStream_t st) {
   if (!set_smem(k_fused_fwd<Act, TL, MASK>, smem)) return MOE_ERR_HIP;
+  const int resident = persistent_grid(k_fused_fwd<Act, TL, MASK>, smem, 0);
   const int n_wg = persistent_grid(k_fused_fwd<Act, TL, MASK>, smem, D->n_workgroups);
-  if (n_wg <= 0) return MOE_ERR_HIP;
+  if (n_wg <= 0 || resident <= 0) return MOE_ERR_HIP;
+  Fwd F = F0;
+  F.n_prod = 0;
+  if (D->n_producer_cus > 0 && (MASK & kProducerPhases) && (MASK & kConsumerPhases)) {
+    // a consumer may wait on a producer task not yet claimed, so both sides
+    // must be resident at once: the grid may not exceed the resident limit
+    if (n_wg > resident) return MOE_ERR_INVALID_ARG;
+    const int per_cu = resident / num_cus() > 0 ? resident / num_cus() : 1;
+    F.n_prod = D->n_producer_cus * per_cu;
+    if (F.n_prod >= n_wg) return MOE_ERR_INVALID_ARG;  // no consumer left
+  }
   hipLaunchKernelGGL((k_fused_fwd<Act, TL, MASK>), dim3(n_wg), dim3(256), smem, st, F);
   return launch_status();
 }
@@ -703,17 +754,28 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
       if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x40u>(D, F, 0, st);
       return rc;
     }
-    // Routing through the up projection in one launch (each up-projection
-    // tile starts once its rows are staged), then the down projection, then
-    // the combine: a down-projection tile would need every up-projection
-    // tile of its rows released at agent scope, an L2 write-back per tile,
-    // which costs more on this chip than the launch boundary.
-    // The combine then runs as a plain launch, one workgroup per task: the
-    // launch boundary already orders it after every down-projection tile,
-    // so a persistent launch would only add the claiming (measured: 149 us
-    // persistent against 105 us plain at the DeepSeek-V3 shape).
-    int rc = launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st);
-    if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
+    // MXFP8: H's scale bytes are 2-byte pieces per row and column tile, and
+    // storing them coherently for a reader in the same launch costs more
+    // than the launch boundary (measured at the DeepSeek-V3 shape, T = 8192:
+    // 6.16 ms in one launch against 5.99 ms), so the down projection gets a
+    // launch of its own
+    if ((D->flags & MOE_FLAG_PERSISTENT_GEMM_APART) || TL::kMX) {
+      // routing through the up projection | the down projection | combine
+      int rc = launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st);
+      if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
+      if (rc != MOE_OK) return rc;
+      hipLaunchKernelGGL(k_combine<Act>, dim3(p.nC), dim3(256), 0, st, F);
+      return launch_status();
+    }
+    // Routing through the down projection in one persistent launch: an
+    // up-projection tile starts once its rows are staged, a down-projection
+    // tile once every up-projection tile of its rows has stored H (stored
+    // coherently, so publishing it writes no L2 back).  The combine then
+    // runs as a plain launch, one workgroup per task: the launch boundary
+    // orders it after every down-projection tile, and as a persistent phase
+    // it only adds the claiming (measured: 149 us persistent against 105 us
+    // plain at the DeepSeek-V3 shape).
+    int rc = launch_fused_fwd<Act, TL, 0x3Fu>(D, F, smem, st);
     if (rc != MOE_OK) return rc;
     hipLaunchKernelGGL(k_combine<Act>, dim3(p.nC), dim3(256), 0, st, F);
     return launch_status();
@@ -774,7 +836,7 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     B.mx_wide_d = p.d % 512 == 0 && al16(B.dys) && al16(B.w2ts);
     B.mx_wide_i = p.I % 512 == 0 && al16(B.dabs) && al16(B.w1ts) && al16(B.w3ts);
     const size_t sm_mx = TileMX128::smem_bytes;
-    static_assert(2 * (TileMX128::smem_bytes + 1024) <= 160 * 1024, "two MXFP8 workgroups per CU");
+    static_assert(2 * (TileMX128::smem_bytes + 1024 + 4 * kEtileLds) <= 160 * 1024, "two MXFP8 workgroups per CU");
     if (D->fused) {
       const size_t sm_setup = (2 * kMaxE + 16) * sizeof(int);
       int rc = p.R > 0 ? mxfp8_quantize_rows(B.dy, p.T, p.d, B.dyq, B.dys, st) : MOE_OK;
@@ -988,6 +1050,7 @@ static int forward_call(const Plan& p, const moe_desc* desc, const void* x, cons
   }
   if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st);
   if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st);
+  if (p.BM == 64) return forward_impl<bf16_t, TileD256h>(p, desc, F, st);
   return forward_impl<bf16_t, TileD256>(p, desc, F, st);
 }
 

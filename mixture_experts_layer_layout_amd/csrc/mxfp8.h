@@ -35,7 +35,8 @@ __device__ void quant_tokens(const Fwd& F, int tb) {
 
 // Up projection + SwiGLU of one (row tile, column tile) in MXFP8; H is
 // quantised in the epilogue, 32 columns of one row per block.
-template <class TL>
+// CO as in g1_tile_bf16.
+template <class TL, bool CO>
 __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   static_assert(TL::kMX, "MXFP8 tile");
   const TileRows tr = fwd_tile(F, tile);
@@ -74,6 +75,10 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float bv) { hs[row * LD + col] = silu_f(av) * bv; });
   __syncthreads();
   bf16_t* Hb = (bf16_t*)F.h;
+  // H's codes and scales are read by the down projection, possibly in this
+  // launch: stored coherently (kStoreCoherent)
+  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(wave_uniform(F.hq + (size_t)r0 * I + c0));
+  const __amdgpu_buffer_rsrc_t rsc = buffer_rsrc(wave_uniform(F.hs + slots::tile_slot(tile, 0, F.BM, I / 32) + c0 / 32));
   for (int t = threadIdx.x; t < TL::BM * NBK; t += kThreads) {
     const int row = t % TL::BM, blk = t / TL::BM;
     if (row >= n) continue;
@@ -86,10 +91,17 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
     uint32_t w[8];
     const uint32_t sc = mx_quant32(v, w);
     const size_t r = (size_t)(r0 + row);
-    uint4* dst = (uint4*)(F.hq + r * I + c0 + 32 * blk);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    F.hs[slots::tile_slot(tile, row, F.BM, I / 32) + c0 / 32 + blk] = (uint8_t)sc;
+    if constexpr (CO) {
+      const int qo = row * I + 32 * blk;
+      store_coherent(rq, qo, make_uint4(w[0], w[1], w[2], w[3]));
+      store_coherent(rq, qo + 16, make_uint4(w[4], w[5], w[6], w[7]));
+      store_coherent_u8(rsc, row * (I / 32) + blk, (uint8_t)sc);
+    } else {
+      uint4* dst = (uint4*)(F.hq + r * I + c0 + 32 * blk);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      F.hs[slots::tile_slot(tile, row, F.BM, I / 32) + c0 / 32 + blk] = (uint8_t)sc;
+    }
     if (Hb) {
       uint4* hb = (uint4*)(Hb + r * I + c0 + 32 * blk);
 #pragma unroll
@@ -117,7 +129,7 @@ __device__ void g1_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
 }
 
 // Down projection of one (row tile, column tile) in MXFP8, bf16 output rows.
-template <class TL>
+template <class TL, bool CO>
 __device__ void g2_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   static_assert(TL::kMX, "MXFP8 tile");
   const TileRows tr = fwd_tile(F, tile);
@@ -138,7 +150,10 @@ __device__ void g2_tile_mx(const Fwd& F, int tile, int nt, bf16_t* smem) {
   bf16_t* YP = (bf16_t*)F.yp;
   const Staged<TL::BM, TL::BN> st{smem};
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
-  st.flush(n, [&](int row) { return YP + (size_t)(r0 + row) * d + c0; });
+  if constexpr (CO)
+    st.flush_coherent(n, YP + (size_t)r0 * d + c0, d);
+  else
+    st.flush(n, [&](int row) { return YP + (size_t)(r0 + row) * d + c0; });
 }
 
 // Standalone quantisation of [rows, K] bf16 along K: codes[r] and scales[r]

@@ -24,12 +24,14 @@
 // phases every wait ends whatever the number of workers and whichever
 // sub-queue each starts on (that only steers locality).
 //
-// Waiting.  Every wait is bounded.  It reads the abort word before the
-// counter on every poll, so once any wait has given up (and raised abort)
-// every later wait returns false at its first poll and the workers drain the
-// queues without doing dependent work.  A task whose wait failed neither
-// runs nor raises its own counter: no count ever covers work that was not
-// done.
+// Waiting.  Every wait is bounded.  A task whose wait failed neither runs
+// nor raises its own counter, so no count ever covers work that was not
+// done, and a wait that finds its count met may proceed.  A poll that finds
+// it short reads the abort word: once any wait has given up (and raised
+// abort) every wait still short fails at its next poll and the workers
+// drain the queues without doing dependent work.  (Reading abort on a poll
+// that found the count met would put a second serial agent-scope load on
+// every task; on the MXFP8 down projection that cost a quarter of its time.)
 #pragma once
 
 #include <stdint.h>
@@ -54,10 +56,19 @@ struct Claim {
   int task;   // the claimed task (-1: done)
 };
 
+MOE_PROTO_FN void claim_advance(Claim& c) {
+  if (++c.qoff == kXcds) {
+    c.qoff = 0;
+    ++c.phase;
+  }
+}
+
 // shape(phase, groups, per) gives the phase's group count and tasks per
 // group (it may wait; false = give up).  Returns the claimed task's index
 // within its phase (group * per + member) and sets c.phase, or -1 when
-// every phase is drained or shape gave up.
+// every phase is drained or shape gave up.  (Issuing a worker's next claim
+// while its current task runs was measured slower: a task claimed early
+// starts late, and the counters others wait on rise late with it.)
 template <class Ops, class F>
 MOE_PROTO_FN int claim_next(int* qctr, int nphases, Claim& c, F shape) {
   while (c.phase < nphases) {
@@ -70,10 +81,7 @@ MOE_PROTO_FN int claim_next(int* qctr, int nphases, Claim& c, F shape) {
       const int i = Ops::fetch_add(&qctr[c.phase * kXcds + sub], 1);
       if (i < n) return (sub + kXcds * (i / per)) * per + i % per;
     }
-    if (++c.qoff == kXcds) {
-      c.qoff = 0;
-      ++c.phase;
-    }
+    claim_advance(c);
   }
   return -1;
 }
@@ -89,8 +97,8 @@ struct WaitCtx {
 template <class Ops>
 MOE_PROTO_FN bool wait_geq(const int* ctr, int target, const WaitCtx& w) {
   for (long long spins = 0;; ++spins) {
-    if (Ops::load(w.abort)) return false;
     if (Ops::load(ctr) >= target) return true;
+    if (Ops::load(w.abort)) return false;
     if (spins >= w.spin_limit) {
       Ops::set_status(w.status, kErrTimeout);
       Ops::store(w.abort, 1);

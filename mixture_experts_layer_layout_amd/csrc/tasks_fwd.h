@@ -68,6 +68,10 @@ struct Sync {
 struct Fwd {
   int T, d, E, k, I, R, nb, S, BM, nN1, nN2, nC, max_tiles;
   int score, renorm, direct;
+  int n_prod;  // workgroups [0, n_prod) of a persistent grid run only the
+               // producer phases (routing, layout, gather, combine), the
+               // others only the expert GEMMs; 0: every workgroup runs every
+               // phase
   // routing options: bias for selection only, group-limited selection
   // (n_group > 1), factor on the gates
   int select_only, n_group, topk_group;
@@ -539,7 +543,10 @@ __device__ void gather_tile(const Fwd& F, int tile, int* ssrc) {
 }
 
 // ---------------------------------------------------------------- GEMMs
-template <class TL>
+// CO: a reader of the tile's output runs in the same launch, so the output
+// is stored coherently (kStoreCoherent) and published by signal_add_stored;
+// otherwise ordinary stores (the kernel boundary publishes them).
+template <class TL, bool CO>
 __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const TileRows tr = fwd_tile(F, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
@@ -579,7 +586,10 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   bf16_t* B = (bf16_t*)F.b;
   const St st{smem};
   tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float bv) { st.put(row, col, silu_f(av) * bv); });
-  st.flush(n, [&](int row) { return H + (size_t)(r0 + row) * I + c0; });
+  if constexpr (CO)
+    st.flush_coherent(n, H + (size_t)r0 * I + c0, I);
+  else
+    st.flush(n, [&](int row) { return H + (size_t)(r0 + row) * I + c0; });
   if (A) {
     __syncthreads();
     tile_visit_pairs<TL>(acc, [&](int row, int col, float av, float) { st.put(row, col, av); });
@@ -592,7 +602,7 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   }
 }
 
-template <class TL>
+template <class TL, bool CO>
 __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const TileRows tr = fwd_tile(F, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
@@ -615,9 +625,13 @@ __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   bf16_t* YP = (bf16_t*)F.yp;
   const Staged<TL::BM, TL::BN> st{smem};
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
-  st.flush(n, [&](int row) { return YP + (size_t)(r0 + row) * d + c0; });
+  if constexpr (CO)
+    st.flush_coherent(n, YP + (size_t)r0 * d + c0, d);
+  else
+    st.flush(n, [&](int row) { return YP + (size_t)(r0 + row) * d + c0; });
 }
 
+template <bool CO>
 __device__ void g1_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
   const TileRows tr = fwd_tile(F, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
@@ -636,13 +650,17 @@ __device__ void g1_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
   tile_f32_visit_pairs(acc, [&](int row, int col, float av, float bv) {
     if (row < n) {
       const size_t o = (size_t)(r0 + row) * I + c0 + col;
-      H[o] = silu_f(av) * bv;
+      if constexpr (CO)  // an agent-coherent store (written through the L2)
+        __hip_atomic_store(H + o, silu_f(av) * bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        H[o] = silu_f(av) * bv;
       if (A) A[o] = av;
       if (B) B[o] = bv;
     }
   });
 }
 
+template <bool CO>
 __device__ void g2_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
   const TileRows tr = fwd_tile(F, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
@@ -656,7 +674,11 @@ __device__ void g2_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
            [&](int nr) -> const float* { return W2 + (size_t)(c0 + nr) * I; });
   float* YP = (float*)F.yp;
   tile_f32_visit(acc, [&](int row, int col, float v) {
-    if (row < n) YP[(size_t)(r0 + row) * d + c0 + col] = v;
+    if (row >= n) return;
+    if constexpr (CO)
+      __hip_atomic_store(YP + (size_t)(r0 + row) * d + c0 + col, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      YP[(size_t)(r0 + row) * d + c0 + col] = v;
   });
 }
 

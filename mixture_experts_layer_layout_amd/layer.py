@@ -12,7 +12,7 @@ from . import api
 _ACT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def desc_for(w, fused=True, stage_rows=0, n_workgroups=0, flags=0, T=None):
+def desc_for(w, fused=True, stage_rows=0, n_workgroups=0, flags=0, T=None, n_producer_cus=0):
     """moe_desc of a synth.Workload."""
     if w.select_only:
         flags |= api.MOE_FLAG_BIAS_SELECT_ONLY
@@ -21,7 +21,7 @@ def desc_for(w, fused=True, stage_rows=0, n_workgroups=0, flags=0, T=None):
                          stage_rows=stage_rows, n_workgroups=n_workgroups, flags=flags,
                          n_group=w.n_group, topk_group=w.topk_group,
                          routed_scale=0.0 if w.routed_scale == 1.0 else w.routed_scale,
-                         macro_tokens=w.macro_tokens)
+                         macro_tokens=w.macro_tokens, n_producer_cus=n_producer_cus)
 
 
 def workspace(desc, device="cuda"):
@@ -103,10 +103,10 @@ def alloc_saved(w, device="cuda", full=True, T=None):
 
 
 def forward(w, inp, fused=True, saved=None, ws=None, stage_rows=0, n_workgroups=0, flags=0,
-            weights=None):
+            weights=None, n_producer_cus=0):
     """Runs moe_forward; returns (y, saved dict)."""
     dev = inp["x"].device
-    d = desc_for(w, fused, stage_rows, n_workgroups, flags, T=inp["x"].shape[0])
+    d = desc_for(w, fused, stage_rows, n_workgroups, flags, T=inp["x"].shape[0], n_producer_cus=n_producer_cus)
     if weights is None:
         weights, keep = weights_of(w, inp)
     if saved is None:

@@ -53,13 +53,14 @@ class Desc(ctypes.Structure):
                                                                   ("n_group", ctypes.c_int32),
                                                                   ("topk_group", ctypes.c_int32),
                                                                   ("routed_scale", ctypes.c_float),
-                                                                  ("macro_tokens", ctypes.c_int32)]
+                                                                  ("macro_tokens", ctypes.c_int32),
+                                                                  ("n_producer_cus", ctypes.c_int32)]
 
 
 def _desc(**kw):
     base = dict(T=4096, d=7168, E=256, k=8, I=2048, act_dtype=1, expert_dtype=1, score=1, renorm=1,
                 fused=1, stage_rows=0, n_workgroups=0, flags=0, n_group=0, topk_group=0,
-                routed_scale=0.0, macro_tokens=0)
+                routed_scale=0.0, macro_tokens=0, n_producer_cus=0)
     base.update(kw)
     return Desc(**base)
 
@@ -77,7 +78,8 @@ def test_workspace_size_and_validation(lib):
     # invalid descriptors: k > E, k = 0, E too large, bad dtype, bf16 d not a multiple of 256,
     # MXFP8 experts with 256-row stages
     for bad, code in ((dict(k=9, E=8), -1), (dict(k=0), -1), (dict(E=5000), -1), (dict(act_dtype=7), -1),
-                      (dict(d=7000), -2), (dict(stage_rows=64), -2), (dict(act_dtype=0, expert_dtype=1), -2),
+                      (dict(d=7000), -2), (dict(stage_rows=96), -2), (dict(n_producer_cus=-1), -1),
+                      (dict(act_dtype=0, expert_dtype=1), -2),
                       (dict(expert_dtype=2, stage_rows=256), -2)):
         assert lib.moe_workspace_size(ctypes.byref(_desc(**bad)), ctypes.byref(n)) == code, bad
     assert lib.moe_workspace_size(None, ctypes.byref(n)) == -1

@@ -20,12 +20,12 @@ BF16_TOL = 2e-2     # max row-relative error for bf16 operands, fp32 accumulatio
 F32_TOL = 1e-4      # fp32 layer: fp32 accumulation over d, I <= 256
 
 
-def run_and_check(w, seed, fused, stage_rows=0, flags=0, n_workgroups=0, tol=None):
+def run_and_check(w, seed, fused, stage_rows=0, flags=0, n_workgroups=0, tol=None, n_producer_cus=0):
     inp = synth.make_inputs(w, seed)
     h = {k: (host(v) if v is not None else None) for k, v in inp.items()}
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y, sv = layer.forward(w, dev, fused=fused, stage_rows=stage_rows, flags=flags,
-                          n_workgroups=n_workgroups)
+                          n_workgroups=n_workgroups, n_producer_cus=n_producer_cus)
     torch.cuda.synchronize()
     assert sv["status"].item() == 0
     f = M.forward(h["x"], h["wr"], h["bias"], h["w1"], h["w3"], h["w2"], w.k, w.score, w.renorm)
@@ -76,7 +76,7 @@ SMALL = {
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 @pytest.mark.parametrize("fused", [True, False])
-@pytest.mark.parametrize("stage_rows", [128, 256])
+@pytest.mark.parametrize("stage_rows", [64, 128, 256])
 def test_bf16_small(name, fused, stage_rows):
     run_and_check(SMALL[name], 5, fused, stage_rows=stage_rows)
 
@@ -111,7 +111,7 @@ def test_empty_batch():
     assert host(sv["counts"]).sum() == 0 and np.all(host(sv["offsets"]) == 0)
 
 
-@pytest.mark.parametrize("flags", ["PERSISTENT_SPLIT", "PERSISTENT_SINGLE", "DIRECT_PULL"])
+@pytest.mark.parametrize("flags", ["PERSISTENT_SPLIT", "PERSISTENT_SINGLE", "PERSISTENT_GEMM_APART", "DIRECT_PULL"])
 def test_forward_persistent_variants_equal_unfused(flags):
     w = SMALL["dsv3-zipf-small"]
     f = getattr(api, "MOE_FLAG_" + flags)
@@ -151,3 +151,29 @@ def test_macrobatched_forward_equals_one_call(name):
         assert torch.equal(s0[n], s1[n]), n
     assert torch.equal(y0, y1)
     assert api.moe_workspace_size(layer.desc_for(wm)) < api.moe_workspace_size(layer.desc_for(w))
+
+
+@pytest.mark.parametrize("n_prod", [1, 4, 32])
+@pytest.mark.parametrize("name", ["dsv3-zipf-small", "mixtral-small"])
+def test_cu_partition_equals_unfused(name, n_prod):
+    """moe_desc.n_producer_cus: producer workgroups run routing, layout,
+    gather and combine, the rest the GEMM tiles; the same bits as the
+    separate kernels, and the oracle's routing and outputs."""
+    w = SMALL[name]
+    run_and_check(w, 12, True, n_producer_cus=n_prod)
+    inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 13).items()}
+    y1, s1 = layer.forward(w, inp, fused=True, n_producer_cus=n_prod)
+    y2, s2 = layer.forward(w, inp, fused=False)
+    torch.cuda.synchronize()
+    assert s1["status"].item() == 0
+    assert torch.equal(y1, y2)
+    for n in ("topk_idx", "perm", "inv", "h"):
+        assert torch.equal(s1[n], s2[n]), n
+
+
+def test_cu_partition_rejects_unresident_grid():
+    w = SMALL["dsv3-small"]
+    inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 14).items()}
+    with pytest.raises(api.MoeError) as err:
+        layer.forward(w, inp, fused=True, n_producer_cus=4, n_workgroups=100000)
+    assert err.value.code == api.MOE_ERR_INVALID_ARG
