@@ -644,13 +644,20 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       if (t >= s_nmt * B.nNdh) continue;
       int tile, nt;
       raster_decode(s_etile, B.E, B.nNdh, t, tile, nt);
+      // [dA | dB] is read by dxp and dw13, the dgate partials by dx: with dx
+      // in this launch both are published by an agent-scope release; with
+      // only dxp or dw13, [dA | dB] is stored coherently and the count waits
+      // for those stores; otherwise the launch boundary publishes them
+      constexpr bool CO = (MASK & 0x30u) != 0 && (MASK & 0x40u) == 0;
       if constexpr (MX)
         bwd_dh_tile_mx(B, tile, nt, (bf16_t*)smem);
       else
-        bwd_dh_tile(B, tile, nt, (bf16_t*)smem, (float*)smem);
-      // dA|dB and the dgate partials are read by dxp, dw13 and dx; the
-      // first signal publishes them, the second has nothing new to publish
-      signal_add<(MASK & 0x70u) != 0>(&B.s.h_cnt[tile], 1);
+        bwd_dh_tile<CO>(B, tile, nt, (bf16_t*)smem, (float*)smem);
+      if constexpr (CO && !MX)
+        signal_add_stored(&B.s.h_cnt[tile], 1);
+      else
+        signal_add<(MASK & 0x70u) != 0>(&B.s.h_cnt[tile], 1);
+      // the second count has nothing new to publish
       signal_add<false>(&B.s.aux1[bwd_tile(B, tile).e], 1);
     } else if ((MASK & 16u) && ph == 4) {
       if (t >= s_nmt * B.nNdx) continue;
@@ -887,9 +894,8 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
       // launch boundary, runs as a plain launch (as the forward's combine)
       const size_t sm_setup = (2 * kMaxE + 16) * sizeof(int);
       int rc = launch_fused_bwd<0x03u>(D, B, sm_setup, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x04u>(D, B, sm_dh, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x14u>(D, B, sm_dh, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x10u>(D, B, sm_dh, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
       if (rc != MOE_OK) return rc;
       if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);

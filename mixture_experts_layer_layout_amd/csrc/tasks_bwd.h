@@ -189,8 +189,9 @@ __device__ void bwd_rowprep(const Bwd& B, int task) {
 // The dh epilogue of one (row tile, I tile) from the accumulators of dHu:
 // the dgate partial sum of the tile's columns, dH = g dHu and the SwiGLU
 // backward into [dA | dB] (shared by the bf16 and MXFP8 tiles, whose
-// accumulator layouts are the same).
-template <class TL>
+// accumulator layouts are the same).  CO: a reader of [dA | dB] (dxp, dw13)
+// runs in the same launch, so it is stored coherently (signal_add_stored).
+template <class TL, bool CO = false>
 __device__ __forceinline__ void bwd_dh_epilogue(const Bwd& B, f32x16_t (&acc)[TL::MI][TL::NJ], int r0, int n,
                                                 int nt, bf16_t* smem) {
   const int I = B.I;
@@ -230,14 +231,20 @@ __device__ __forceinline__ void bwd_dh_epilogue(const Bwd& B, f32x16_t (&acc)[TL
     }
   }
   const size_t I2 = 2 * (size_t)I;
-  st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + c0; });
+  if constexpr (CO)
+    st.flush_coherent(n, B.dab + (size_t)r0 * I2 + c0, I2);
+  else
+    st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + c0; });
   if (threadIdx.x < TL::BM && (int)threadIdx.x < n) {
     const int row = threadIdx.x;
     B.dgp[(size_t)nt * B.R + r0 + row] = sred[row] + sred[TL::BM + row];
   }
   __syncthreads();
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
-  st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + I + c0; });
+  if constexpr (CO)
+    st.flush_coherent(n, B.dab + (size_t)r0 * I2 + I + c0, I2);
+  else
+    st.flush(n, [&](int row) { return B.dab + (size_t)(r0 + row) * I2 + I + c0; });
 }
 
 // dHu = G W2_e for one (row tile, I tile), then the dh epilogue.
@@ -245,7 +252,7 @@ __device__ __forceinline__ TileRows bwd_tile(const Bwd& B, int tile) {
   return tile_rows(B.tile_e, B.tile_r0, B.tile_n, tile, B.max_tiles, B.E, B.R, B.BM);
 }
 
-template <class TL>
+template <class TL, bool CO>
 __device__ void bwd_dh_tile_t(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const TileRows tr = bwd_tile(B, tile);
   const int e = tr.e, r0 = tr.r0, n = tr.n;
@@ -259,14 +266,15 @@ __device__ void bwd_dh_tile_t(const Bwd& B, int tile, int nt, bf16_t* smem) {
   auto lb = kcols_n<TL::BN, kDgradAhead>([&](int kk, int) -> const bf16_t* { return W2 + (size_t)kk * I + c0; });
   f32x16_t acc[TL::MI][TL::NJ];
   tile_mainloop<TL, kDgradAhead>(d / 64, smem, acc, la, lb);
-  bwd_dh_epilogue<TL>(B, acc, r0, n, nt, smem);
+  bwd_dh_epilogue<TL, CO>(B, acc, r0, n, nt, smem);
 }
 
+template <bool CO = false>
 __device__ void bwd_dh_tile(const Bwd& B, int tile, int nt, bf16_t* smem, float*) {
   if (bwd_tile(B, tile).n <= TileDH64::BM)
-    bwd_dh_tile_t<TileDH64>(B, tile, nt, smem);
+    bwd_dh_tile_t<TileDH64, CO>(B, tile, nt, smem);
   else
-    bwd_dh_tile_t<TileDH>(B, tile, nt, smem);
+    bwd_dh_tile_t<TileDH, CO>(B, tile, nt, smem);
 }
 
 // ---------------------------------------------------------------- dxp
