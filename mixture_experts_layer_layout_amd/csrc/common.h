@@ -178,6 +178,21 @@ __device__ __forceinline__ void signal_add_stored(int* ctr, int v) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait states after a store of more than 8 bytes, before anything else
+// issues.  Such a store reads its data registers after it has issued, and
+// the compiler may put an instruction that overwrites them right behind it
+// (the register holding a stored word, reused for the next accumulator
+// tile or an address).  On gfx950 that was seen to change what was stored:
+// now and then, in some lanes, the first word of a 16-byte store held the
+// value written by the next instruction (zeros, address bits).  Every
+// 16-byte store issued through a builtin here is followed by this guard;
+// a host test checks the built kernels for the pattern.
+__device__ __forceinline__ void store_data_guard() {
+  __builtin_amdgcn_sched_barrier(0);  // nothing moves between the store and the wait
+  asm volatile("s_nop 3");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // 16 bytes stored coherently (kStoreCoherent) at byte offset `off` of a
 // buffer whose base is the same in every lane.
 __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rs, int off, uint4 v) {
@@ -185,6 +200,7 @@ __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rs, int of
   u32x4_t q;
   q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
   __builtin_amdgcn_raw_buffer_store_b128(q, rs, off, 0, kStoreCoherent);
+  store_data_guard();
 }
 __device__ __forceinline__ void store_coherent_u8(__amdgpu_buffer_rsrc_t rs, int off, uint8_t v) {
   __builtin_amdgcn_raw_buffer_store_b8(v, rs, off, 0, kStoreCoherent);

@@ -651,6 +651,7 @@ __device__ __forceinline__ void tile_store_staged(const f32x16_t (&acc)[TL::MI][
       for (int g = 0; g < 2; ++g) {
         const u32x4_t q = *(const u32x4_t*)(st + sidx(8 * g + rrow, 4 * rch));
         __builtin_amdgcn_raw_buffer_store_b128(q, rs, vo, (32 * i + 16 * h + 8 * g) * ldb, kWgradStorePolicy);
+        store_data_guard();
       }
     }
 }

@@ -499,6 +499,21 @@ __global__ void __launch_bounds__(256) k_bwd_setup(Bwd B) {
 
 __global__ void __launch_bounds__(256) k_bwd_rowprep(Bwd B) { bwd_rowprep(B, blockIdx.x); }
 
+// Setup (block 0) and row preparation (blocks 1 ..) ahead of the persistent
+// backward launches, as one plain launch: neither reads what the other
+// writes, the launch boundary publishes both, and each block still raises
+// the count that the later launches' claims wait on.  (At the DeepSeek-V3
+// shape 186 us, against 196-210 us as a persistent launch; the row pulls
+// write 0.94 GB.)
+__global__ void __launch_bounds__(256) k_bwd_prep(Bwd B) {
+  __shared__ int sh[2 * kMaxE + 16];
+  if (blockIdx.x == 0)
+    bwd_setup(B, sh);
+  else
+    bwd_rowprep(B, blockIdx.x - 1);
+  signal_add<false>(B.s.scan_done, 1);
+}
+
 __global__ void __launch_bounds__(256, 2) k_bwd_dh(Bwd B) {
   extern __shared__ __align__(16) char smem[];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -845,9 +860,8 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     const size_t sm_mx = TileMX128::smem_bytes;
     static_assert(2 * (TileMX128::smem_bytes + 1024 + 4 * kEtileLds) <= 160 * 1024, "two MXFP8 workgroups per CU");
     if (D->fused) {
-      const size_t sm_setup = (2 * kMaxE + 16) * sizeof(int);
       int rc = p.R > 0 ? mxfp8_quantize_rows(B.dy, p.T, p.d, B.dyq, B.dys, st) : MOE_OK;
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x03u>(D, B, sm_setup, st);
+      hipLaunchKernelGGL(k_bwd_prep, dim3(1 + p.nRP), dim3(256), 0, st, B);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x04u, true>(D, B, sm_mx, st);
       if (rc == MOE_OK && p.R > 0) rc = mxfp8_quantize_rows(B.dab, p.R, 2 * (int64_t)p.I, B.dabq, B.dabs, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
@@ -873,8 +887,7 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
       if (rc != MOE_OK) return rc;
       hipLaunchKernelGGL(k_bwd_dxp_mx, dim3(p.max_tiles * p.nNdx), dim3(256), sm_mx, st, B);
     }
-    hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * cdiv(p.nW13n, kWgradPerTicket)), dim3(256), sm_dw, st,
-                       B);
+    hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * cdiv(p.nW13n, kWgradPerTicket)), dim3(256), sm_dw, st, B);
     if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
     return launch_status();
   }
@@ -882,19 +895,20 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
     static_assert(2 * (TileDW::smem_bytes + kWgradStageBytes + 1024) <= 160 * 1024,
                   "two weight-gradient workgroups per CU, with their static LDS");
-    // By default one persistent launch per phase (setup and row pulls
-    // together): no phase reads what another phase of its launch writes, so
-    // no task needs the agent-scope release, and each launch's registers
-    // are those of one task kind.  Every backward task in one launch does
-    // not fit two workgroups' registers per CU (MOE_FLAG_PERSISTENT_SINGLE
+    // By default dH and dXp share a persistent launch (dXp tiles wait on
+    // the dH tiles of their rows, [dA | dB] stored coherently), and the
+    // weight gradients get one each: no other phase reads what another
+    // phase of its launch writes, and each launch's registers are those of
+    // its own task kinds.  Every backward task in one launch does not fit
+    // two workgroups' registers per CU (MOE_FLAG_PERSISTENT_SINGLE
     // runs it anyway).
     if (!(D->flags & (MOE_FLAG_PERSISTENT_SINGLE | MOE_FLAG_PERSISTENT_WGRAD_APART))) {
-      // each launch reserves the LDS its own tasks use (the setup's scan
-      // area, the tiles' stages); the dX gather-sum, last and ordered by the
-      // launch boundary, runs as a plain launch (as the forward's combine)
-      const size_t sm_setup = (2 * kMaxE + 16) * sizeof(int);
-      int rc = launch_fused_bwd<0x03u>(D, B, sm_setup, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x14u>(D, B, sm_dh, st);
+      // each persistent launch reserves the LDS its own tiles use; setup
+      // with the row preparation before them, and the dX gather-sum after
+      // them (ordered by the launch boundary, as the forward's combine), run
+      // as plain launches
+      hipLaunchKernelGGL(k_bwd_prep, dim3(1 + p.nRP), dim3(256), 0, st, B);
+      int rc = launch_fused_bwd<0x14u>(D, B, sm_dh, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
       if (rc != MOE_OK) return rc;
