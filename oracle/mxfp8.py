@@ -171,6 +171,25 @@ def quantize_tokens(x):
     return fake_quant(np.asarray(x, dtype=np.float64))
 
 
+def quantize_along_rows(v):
+    """v [n, C] quantised in blocks of 32 consecutive rows of each column:
+    the token axis, which is the contraction axis of a weight gradient.
+    Blocks start at row 0; a last partial block is filled with zero rows,
+    which change no block maximum.  Returns the fp64 values [n, C]."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    pad = (-n) % BLOCK
+    if pad:
+        v = np.concatenate([v, np.zeros((pad,) + v.shape[1:])])
+    return fake_quant(v.T).T[:n]
+
+
+def wgrad_mxfp8(lhs_rows, rhs_rows):
+    """lhs^T rhs over the rows of one expert (lhs [n, P], rhs [n, Q] -> [P,
+    Q]) with both operands quantised along the rows (quantize_along_rows)."""
+    return quantize_along_rows(lhs_rows).T @ quantize_along_rows(rhs_rows)
+
+
 def expert_ffn_mxfp8(xq_rows, w1, w3, w2):
     """One expert's SwiGLU FFN on rows that are already quantised (xq_rows,
     fp64 values of MXFP8 codes): W1/W3 quantised along d and W2 along I
@@ -230,15 +249,17 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None, expert
                 y=y)
 
 
-def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e):
+def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e, mx_wgrad=True):
     """One expert's part of backward_mxfp8 over its rows (the gathered x and
     dY rows, the rows' gates and the forward's A, B, H of those rows), in
     the steps of oracle.moe.backward: dHu = G W2 with G quantised along d
     per row and W2 as [I, d] (W2^T) along d; dgate = <dHu, H>; dW2 = (g G)^T
     H; dH = g dHu; the SwiGLU backward; dXp = dA W1 + dB W3 with dA, dB
     quantised along I per row and W1, W3 as [d, I] along I; dW1 = dA^T x,
-    dW3 = dB^T x with the unquantised operands.  Returns dict dw1, dw3, dw2,
-    dxp, dgate (per row), dHu, dA, dB."""
+    dW3 = dB^T x.  The three weight gradients contract over the expert's
+    rows: with mx_wgrad their operands (g G, H, dA, dB, x) are quantised
+    along the rows (wgrad_mxfp8), else taken unquantised.  Returns dict dw1,
+    dw3, dw2, dxp, dgate (per row), dHu, dA, dB."""
     from . import moe as M
     xr = np.asarray(x_rows, dtype=np.float64)
     G = np.asarray(dy_rows, dtype=np.float64)
@@ -246,7 +267,8 @@ def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e):
     w2t = fake_quant(np.asarray(w2_e, dtype=np.float64).T)          # [I, d] along d
     dHu = quantize_tokens(G) @ w2t.T
     dgate = np.sum(dHu * H, axis=1)
-    dW2 = (g[:, None] * G).T @ H
+    wg = wgrad_mxfp8 if mx_wgrad else (lambda l, r: l.T @ r)
+    dW2 = wg(g[:, None] * G, H)
     dH = g[:, None] * dHu
     sA = M.sigmoid(A)
     dA = dH * B * sA * (1.0 + A * (1.0 - sA))
@@ -254,23 +276,26 @@ def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e):
     w1t = fake_quant(np.asarray(w1_e, dtype=np.float64).T)          # [d, I] along I
     w3t = fake_quant(np.asarray(w3_e, dtype=np.float64).T)
     dXp = fake_quant(dA) @ w1t.T + fake_quant(dB) @ w3t.T
-    return dict(dw1=dA.T @ xr, dw3=dB.T @ xr, dw2=dW2, dxp=dXp, dgate=dgate, dHu=dHu, dA=dA, dB=dB)
+    return dict(dw1=wg(dA, xr), dw3=wg(dB, xr), dw2=dW2, dxp=dXp, dgate=dgate, dHu=dHu, dA=dA, dB=dB)
 
 
-def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None):
-    """The backward of the expert path (routing frozen) with the two data
-    gradient GEMMs in MXFP8 and the weight gradients in high precision.
+def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None, mx_wgrad=True):
+    """The backward of the expert path (routing frozen) with its GEMMs in
+    MXFP8.
 
     MoK flash §03 quotes the backward in MXFP8 but does not say which
-    products are quantised.  Reading taken: the data gradients dHu = G W2
-    and dXp = dA W1 + dB W3 run in MXFP8, each operand quantised along that
-    product's contraction axis -- the upstream rows G along d and W2 as
-    [I, d] (W2^T) along d; [dA | dB] along I and W1, W3 as [d, I] (W^T)
-    along I -- while the weight gradients take the unquantised operands (G,
-    the forward's H, dA, dB and the gathered x rows).  The steps are those
-    of moe.backward, expert by expert (expert_backward_mxfp8, through
-    ``expert_map`` as in forward_mxfp8); fwd holds the forward's gate,
-    layout and A, B, H.
+    products are quantised.  Reading taken: every product of the expert
+    backward runs in MXFP8, each operand quantised along that product's
+    contraction axis.  The data gradients: dHu = G W2 with the upstream rows
+    G along d and W2 as [I, d] (W2^T) along d; dXp = dA W1 + dB W3 with
+    [dA | dB] along I and W1, W3 as [d, I] (W^T) along I.  The weight
+    gradients contract over the expert's rows: dW2 = (g G)^T H, dW1 = dA^T
+    x and dW3 = dB^T x with all five operands quantised along the rows, in
+    blocks of 32 rows from the expert's first row (the last block filled
+    with zeros); ``mx_wgrad=False`` keeps those three unquantised.  The
+    steps are those of moe.backward, expert by expert (expert_backward_mxfp8,
+    through ``expert_map`` as in forward_mxfp8); fwd holds the forward's
+    gate, layout and A, B, H.
     """
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
@@ -291,7 +316,7 @@ def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None):
     def job(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         rows = src[lo:hi]
-        return (x[rows], dy[rows], g_row[lo:hi], A[lo:hi], B[lo:hi], H[lo:hi], w1[e], w3[e], w2[e])
+        return (x[rows], dy[rows], g_row[lo:hi], A[lo:hi], B[lo:hi], H[lo:hi], w1[e], w3[e], w2[e], mx_wgrad)
 
     for e, b in zip(live, (expert_map or _starmap)(expert_backward_mxfp8, (job(e) for e in live))):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
