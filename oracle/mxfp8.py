@@ -171,6 +171,17 @@ def quantize_tokens(x):
     return fake_quant(np.asarray(x, dtype=np.float64))
 
 
+def round_bf16(v):
+    """fp64 -> the nearest bfloat16 value (8 significant bits: 1 implicit
+    and 7 stored), ties to the even significand, returned as fp64.  From
+    the format: v = m 2^e with m in [0.5, 1) (frexp), so the significand
+    kept is rint(m 2^8) / 2^8; zero stays zero.  (Magnitudes below the
+    bfloat16 normal range do not occur here.)"""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
 def quantize_along_rows(v):
     """v [n, C] quantised in blocks of 32 consecutive rows of each column:
     the token axis, which is the contraction axis of a weight gradient.
@@ -249,7 +260,8 @@ def forward_mxfp8(x, wr, bias, w1, w3, w2, k, score, renorm, logits=None, expert
                 y=y)
 
 
-def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e, mx_wgrad=True):
+def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e, mx_wgrad=True,
+                          saved_bf16=False):
     """One expert's part of backward_mxfp8 over its rows (the gathered x and
     dY rows, the rows' gates and the forward's A, B, H of those rows), in
     the steps of oracle.moe.backward: dHu = G W2 with G quantised along d
@@ -258,8 +270,11 @@ def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e, mx
     quantised along I per row and W1, W3 as [d, I] along I; dW1 = dA^T x,
     dW3 = dB^T x.  The three weight gradients contract over the expert's
     rows: with mx_wgrad their operands (g G, H, dA, dB, x) are quantised
-    along the rows (wgrad_mxfp8), else taken unquantised.  Returns dict dw1,
-    dw3, dw2, dxp, dgate (per row), dHu, dA, dB."""
+    along the rows (wgrad_mxfp8), else taken unquantised.  With saved_bf16
+    dA and dB are rounded to bfloat16 (round_bf16) before they are
+    quantised, as the layer stores them between its GEMMs (A, B, H arrive
+    rounded from backward_mxfp8).  Returns dict dw1, dw3, dw2, dxp, dgate
+    (per row), dHu, dA, dB."""
     from . import moe as M
     xr = np.asarray(x_rows, dtype=np.float64)
     G = np.asarray(dy_rows, dtype=np.float64)
@@ -273,13 +288,15 @@ def expert_backward_mxfp8(x_rows, dy_rows, g_rows, A, B, H, w1_e, w3_e, w2_e, mx
     sA = M.sigmoid(A)
     dA = dH * B * sA * (1.0 + A * (1.0 - sA))
     dB = dH * M.silu(A)
+    if saved_bf16:
+        dA, dB = round_bf16(dA), round_bf16(dB)
     w1t = fake_quant(np.asarray(w1_e, dtype=np.float64).T)          # [d, I] along I
     w3t = fake_quant(np.asarray(w3_e, dtype=np.float64).T)
     dXp = fake_quant(dA) @ w1t.T + fake_quant(dB) @ w3t.T
     return dict(dw1=wg(dA, xr), dw3=wg(dB, xr), dw2=dW2, dxp=dXp, dgate=dgate, dHu=dHu, dA=dA, dB=dB)
 
 
-def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None, mx_wgrad=True):
+def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None, mx_wgrad=True, saved_bf16=True):
     """The backward of the expert path (routing frozen) with its GEMMs in
     MXFP8.
 
@@ -296,6 +313,14 @@ def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None, mx_wgrad=True):
     steps are those of moe.backward, expert by expert (expert_backward_mxfp8,
     through ``expert_map`` as in forward_mxfp8); fwd holds the forward's
     gate, layout and A, B, H.
+
+    Reading taken for the stored values: the layer keeps the activations its
+    forward saves (A, B, H) and the SwiGLU gradients [dA | dB] it hands from
+    one GEMM to the next in bfloat16, so those are the values the MXFP8
+    quantisations see.  With ``saved_bf16`` (the default) A, B, H are
+    rounded to bfloat16 on entry and dA, dB where they are formed
+    (round_bf16); the upstream gradient and x arrive as bfloat16 already,
+    and g G is a product formed without rounding.
     """
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
@@ -304,6 +329,8 @@ def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None, mx_wgrad=True):
     offsets, perm, inv, src = fwd["offsets"], fwd["perm"], fwd["inv"], fwd["src"]
     gate = np.asarray(fwd["gate"], dtype=np.float64)
     A, B, H = fwd["A"], fwd["B"], fwd["H"]
+    if saved_bf16:
+        A, B, H = round_bf16(A), round_bf16(B), round_bf16(H)
     R = perm.shape[0]
     g_row = gate.reshape(-1)[perm]
     out = dict(dHu=np.zeros((R, I)), dA=np.zeros((R, I)), dB=np.zeros((R, I)), dXp=np.zeros((R, d)))
@@ -316,7 +343,8 @@ def backward_mxfp8(dy, x, fwd, w1, w3, w2, k, expert_map=None, mx_wgrad=True):
     def job(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         rows = src[lo:hi]
-        return (x[rows], dy[rows], g_row[lo:hi], A[lo:hi], B[lo:hi], H[lo:hi], w1[e], w3[e], w2[e], mx_wgrad)
+        return (x[rows], dy[rows], g_row[lo:hi], A[lo:hi], B[lo:hi], H[lo:hi], w1[e], w3[e], w2[e], mx_wgrad,
+                saved_bf16)
 
     for e, b in zip(live, (expert_map or _starmap)(expert_backward_mxfp8, (job(e) for e in live))):
         lo, hi = int(offsets[e]), int(offsets[e + 1])

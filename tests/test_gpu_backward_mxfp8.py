@@ -1,7 +1,9 @@
-"""GPU parity of the MXFP8 backward (moe_backward with MXFP8 experts: the
-data gradients dHu = G W2 and dXp = dA W1 + dB W3 on the scaled matrix
-cores, the weight gradients in bf16) and of moe_quantize_mxfp8_t against the
-fp64 oracle (oracle/mxfp8.py backward_mxfp8 and quantize):
+"""GPU parity of the MXFP8 backward (moe_backward with MXFP8 experts: every
+GEMM on the scaled matrix cores -- the data gradients dHu = G W2 and dXp =
+dA W1 + dB W3 with their operands quantised along d and along I, the weight
+gradients dW2 = (g G)^T H, dW1 = dA^T x, dW3 = dB^T x with theirs quantised
+along the expert's rows) and of moe_quantize_mxfp8_t against the fp64
+oracle (oracle/mxfp8.py backward_mxfp8 and quantize):
 
   * the transposed quantisation: codes and scales bit-exact (bf16 inputs,
     so every scale and rounding decision is exact on both sides), with
@@ -10,10 +12,12 @@ fp64 oracle (oracle/mxfp8.py backward_mxfp8 and quantize):
     experts without rows, k = E and one expert, on both the 4-stage (wide)
     and the per-stage scale reads.  The oracle routes on the logits the GPU
     forward exported; the GPU backward consumes the bf16 A, B, H its MXFP8
-    forward saved, the oracle its own fp64 ones.  Both quantise dY, W2^T,
-    W1^T and W3^T identically; [dA | dB] is quantised from bf16 on the GPU
-    and from fp64 in the oracle, so a few of its codes may sit one step
-    apart.  Tolerance: max row-relative error 6e-2 (as for the MXFP8
+    forward saved, the oracle its own, rounded to bfloat16 as the layer
+    saves them (and [dA | dB] likewise).  Both quantise dY, W2^T, W1^T, W3^T
+    and the x rows identically, g dY from the same product (fp32 against
+    fp64), and H, dA, dB from bfloat16 values that differ only where the
+    fp32 and fp64 arithmetic before them round to different bfloat16
+    neighbours.  Tolerance: max row-relative error 6e-2 (as for the MXFP8
     forward's output)."""
 import numpy as np
 import pytest

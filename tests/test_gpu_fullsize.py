@@ -282,14 +282,15 @@ def test_fullsize_router_backward():
 
 
 def test_fullsize_mxfp8_backward():
-    """dsv3-fwdbwd-zipf-mxfp8 at full size (MXFP8 forward, MXFP8 data
-    gradients, bf16 weight gradients), as bench.py runs it: routing exact;
+    """dsv3-fwdbwd-zipf-mxfp8 at full size (MXFP8 forward, MXFP8 data and
+    weight gradients), as bench.py runs it: routing exact;
     dX and dgate of 16 tokens (tile-edge tokens of the heaviest expert
     included) against the oracle's MXFP8 forward and backward over those
     tokens alone (their rows depend on nothing else); dW1, dW3 and dW2 of a
     heavy expert (the third heaviest: a full streamed band) against the
     oracle's per-expert MXFP8 backward over exactly that expert's rows, given
-    the oracle's MXFP8 A, B, H of those rows."""
+    the oracle's MXFP8 A, B, H of those rows, rounded to bfloat16 as the
+    layer saves them."""
     from oracle import mxfp8 as Q
     w = synth.WORKLOADS["dsv3-fwdbwd-zipf-mxfp8"]
     print(f"\nfull-size {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}", flush=True)
@@ -325,7 +326,8 @@ def test_fullsize_mxfp8_backward():
         rows = src[lo:hi]
         g_row = gate.reshape(-1)[perm][lo:hi]
         A, B, H, _ = Q.expert_ffn_mxfp8(Q.quantize_tokens(x[rows]), W1[e], W3[e], W2[e])
-        eb = Q.expert_backward_mxfp8(x[rows], dy[rows], g_row, A, B, H, W1[e], W3[e], W2[e])
+        A, B, H = Q.round_bf16(A), Q.round_bf16(B), Q.round_bf16(H)
+        eb = Q.expert_backward_mxfp8(x[rows], dy[rows], g_row, A, B, H, W1[e], W3[e], W2[e], saved_bf16=True)
     finally:
         pool.terminate()
     for n in ("dw1", "dw3", "dw2"):

@@ -13,7 +13,11 @@ data-gradient pins switch the weight-gradient quantisation off
 (mx_wgrad=False), whose own pins follow them.  Hand-computed roundings pin
 quantize_along_rows, including the zero fill of a last partial block; a
 random case bounds the MXFP8 error against the unquantised backward, and
-planted mistakes in the weight-gradient quantisation must be caught.
+planted mistakes in the weight-gradient quantisation must be caught.  By
+default backward_mxfp8 takes A, B, H and forms dA, dB in bfloat16, as the
+layer stores them: round_bf16 is pinned by hand-computed ties and against
+torch's float32 -> bfloat16 conversion, and a stored value that bfloat16
+cannot hold must act as its rounded neighbour.
 """
 import numpy as np
 import pytest
@@ -114,7 +118,7 @@ def test_dh_exact_along_d():
     A = rng.standard_normal((R, I))
     B = rng.standard_normal((R, I))
     f = _full(fwd, x, A, B, H)
-    got = Q.backward_mxfp8(dy, x, f, w1, w3, w2, 1, mx_wgrad=False)
+    got = Q.backward_mxfp8(dy, x, f, w1, w3, w2, 1, mx_wgrad=False, saved_bf16=False)
     want = M.backward(dy, f, w1, w3, w2, 1)
     assert not np.array_equal(Q.fake_quant(w2[0]), w2[0])   # along I it would not be exact
     assert np.array_equal(got["dHu"], want["dHu"])
@@ -153,9 +157,9 @@ def test_random_case_within_mxfp8_error():
         assert 1e-3 < err < 0.2, (n, err)
     # with the weight gradients unquantised, dW2 takes no quantised operand
     # and dW1, dW3 only inherit dA, dB's error
-    plain = Q.backward_mxfp8(dy, x, f, w1, w3, w2, k, mx_wgrad=False)
+    plain = Q.backward_mxfp8(dy, x, f, w1, w3, w2, k, mx_wgrad=False, saved_bf16=False)
     assert np.array_equal(plain["dw2"], want["dw2"])
-    assert np.array_equal(plain["dx"], got["dx"])
+    assert np.array_equal(plain["dx"], Q.backward_mxfp8(dy, x, f, w1, w3, w2, k, saved_bf16=False)["dx"])
     for n in ("dw1", "dw3"):
         assert 0 < M.max_row_rel_err(plain[n].reshape(E, -1), want[n].reshape(E, -1)) < 0.1
 
@@ -287,4 +291,42 @@ def test_weight_gradient_mutant_is_caught(name, monkeypatch):
         assert wgrad_pins_hold()
     else:
         assert not wgrad_pins_hold(), f"no pin catches {name}"
+
+
+# ------------------------------------------------------------- bfloat16 storage
+def test_round_bf16_hand_computed_and_against_torch():
+    # bfloat16 keeps 8 significant bits: the spacing at 1 is 2^-7
+    assert Q.round_bf16(1 + 2.0 ** -8) == 1.0                     # a tie: to the even significand
+    assert Q.round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6        # a tie: to the even one above
+    assert Q.round_bf16(1 + 2.0 ** -8 + 2.0 ** -20) == 1 + 2.0 ** -7
+    assert Q.round_bf16(-3.0) == -3.0 and Q.round_bf16(0.0) == 0.0
+    assert Q.round_bf16(255.5) == 256.0 and Q.round_bf16(254.5) == 254.0
+    import torch
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal(4096) * np.exp2(rng.integers(-20, 20, 4096))).astype(np.float32).astype(np.float64)
+    want = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(Q.round_bf16(v), want)
+
+
+def test_saved_activations_enter_as_bf16():
+    # B = 1 + 2^-10 is stored as 1.0 (bfloat16): with the stored values the
+    # backward equals the one given B = 1 exactly, without them it differs
+    T, d, E, I = 64, 64, 2, 64
+    rng = np.random.default_rng(10)
+    fwd = _problem(T, d, E, I, 10)
+    x, dy = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    w1, w3, w2 = (rng.standard_normal((E, I, d)), rng.standard_normal((E, I, d)),
+                  rng.standard_normal((E, d, I)))
+    A, H = rng.standard_normal((T, I)), rng.standard_normal((T, I))
+    A, H = Q.round_bf16(A), Q.round_bf16(H)
+    f1 = _full(fwd, x, A, np.full((T, I), 1 + 2.0 ** -10), H)
+    f0 = _full(fwd, x, A, np.ones((T, I)), H)
+    a = Q.backward_mxfp8(dy, x, f1, w1, w3, w2, 1)
+    b = Q.backward_mxfp8(dy, x, f0, w1, w3, w2, 1)
+    c = Q.backward_mxfp8(dy, x, f1, w1, w3, w2, 1, saved_bf16=False)
+    for n in ("dx", "dw1", "dw3", "dw2", "dgate"):
+        assert np.array_equal(a[n], b[n]), n
+    assert not np.array_equal(a["dw1"], c["dw1"])
+    # and dA, dB are rounded where they are formed
+    assert np.array_equal(a["dA"], Q.round_bf16(a["dA"])) and np.array_equal(a["dB"], Q.round_bf16(a["dB"]))
 
