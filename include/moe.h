@@ -143,6 +143,11 @@ typedef struct moe_desc {
                                       projection in a persistent launch of
                                       its own (routing .. up projection |
                                       down projection | combine)         */
+#define MOE_FLAG_MXFP8_WGRAD 0x1000u /* backward with MXFP8 experts: the
+                                      weight gradients in MXFP8 too (their
+                                      operands quantised along the expert's
+                                      rows); without it they take bf16
+                                      operands                             */
 #define MOE_FLAG_BIAS_SELECT_ONLY 0x10u /* the router bias steers the
                                       selection only: experts ranked by
                                       sigmoid(logit) + bias, gates from the
@@ -336,9 +341,11 @@ MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const void*
  *         for experts without rows);
  *   dgate float [T, k] output, dL/dgate.
  * With desc->fused = 1 the phases (setup, rowprep and pulls, dH, dW2, dXp,
- * dW1/dW3, dX) run through the persistent scheduler, one launch per phase
- * (setup and pulls together) unless MOE_FLAG_PERSISTENT_SINGLE or
- * MOE_FLAG_PERSISTENT_WGRAD_APART is set;
+ * dW1/dW3, dX) run as: setup and pulls in one plain launch, dH and dXp in
+ * one persistent launch, dW2 and dW1/dW3 in one each, dX a plain launch
+ * (MOE_FLAG_PERSISTENT_SINGLE: one persistent launch for every phase;
+ * MOE_FLAG_PERSISTENT_WGRAD_APART: the data gradients in one, the weight
+ * gradients in another);
  * with fused = 0 each phase is an ordinary grid.  Needs bf16 activations
  * with d % 128 == 0 and I % 128 == 0 (else MOE_ERR_UNSUPPORTED).
  * With desc->expert_dtype == MOE_MXFP8 the data gradients dHu = G W2 and
@@ -347,11 +354,16 @@ MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const void*
  * from moe_quantize_mxfp8_t: w1, w3 the codes of W1^T, W3^T uint8 [E, d, I]
  * with w1_scale, w3_scale [E, d, I/32]; w2 the codes of W2^T [E, I, d] with
  * w2_scale [E, I, d/32] (all required).  dY and [dA | dB] are quantised
- * along their rows inside the call; the weight gradients, dX's gather-sum
- * and dgate take the bf16 operands as in the bf16 backward.  With
- * desc->fused = 1 this variant runs one persistent launch per phase (the
- * MOE_FLAG_PERSISTENT_SINGLE and _WGRAD_APART flags do not apply to it),
- * with the two quantisations as plain launches between them. */
+ * along their rows inside the call.  The weight gradients take bf16
+ * operands as in the bf16 backward, or with MOE_FLAG_MXFP8_WGRAD run in
+ * MXFP8 too: dW2 = (g G)^T H, dW1 = dA^T x, dW3 = dB^T x with g G, H, dA,
+ * dB and the x rows quantised along the expert's rows (blocks of 32 from
+ * its first row) inside the call, into a larger workspace
+ * (moe_workspace_size with the same flags).  dX's gather-sum and dgate
+ * take bf16 operands.  With desc->fused = 1 this variant runs one
+ * persistent launch per phase (the MOE_FLAG_PERSISTENT_SINGLE and
+ * _WGRAD_APART flags do not apply to it), with the quantisations as plain
+ * launches between them. */
 MOE_API int moe_backward(const moe_desc* desc, const void* dy, const void* x,
                  const moe_weights* w, const moe_saved* saved, void* dx,
                  void* dw1, void* dw3, void* dw2, float* dgate,

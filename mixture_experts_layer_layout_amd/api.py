@@ -38,6 +38,7 @@ MOE_FLAG_SPIN_LIMIT_TINY = 0x100
 MOE_FLAG_TEST_DROP_READY = 0x200
 MOE_FLAG_TEST_SHUFFLE_CLAIMS = 0x400
 MOE_FLAG_PERSISTENT_GEMM_APART = 0x800
+MOE_FLAG_MXFP8_WGRAD = 0x1000
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
 _SC = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}

@@ -1,5 +1,5 @@
-// bwd_mx.h -- the backward's two data-gradient GEMMs in MXFP8 (MoK flash
-// §03 quotes the backward in MXFP8; the weight gradients stay bf16 here).
+// bwd_mx.h -- the backward's GEMMs in MXFP8 (MoK flash §03 quotes the
+// backward in MXFP8).
 //
 // Each product takes its operands quantised along its own contraction axis,
 // one E8M0 scale per 32 values:
@@ -10,7 +10,12 @@
 //   dXp = [dA | dB] [W1_e ; W3_e]   [dA | dB] rows quantised along 2I after
 //                      the dh epilogue wrote them; W1_e, W3_e enter as
 //                      W^T [d, I], blocks along I
-// Both run on the scaled matrix-core tile (gemm_mx.h), whose operands are
+//   dW2_e = (g G)_e^T H_e, dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e
+//                      contract over the expert's rows: g G, H, dA, dB and
+//                      the x rows quantised along the rows in blocks of 32
+//                      from the expert's first row (k_mx_quant_tiles), and
+//                      stored transposed so that the rows are k-contiguous
+// All run on the scaled matrix-core tile (gemm_mx.h), whose operands are
 // k-contiguous rows, so the transposed weights come from
 // moe_quantize_mxfp8_t (k_mx_quant_t below), once per weight update.  The
 // epilogues are the bf16 tiles' (same accumulator layout).
@@ -163,6 +168,140 @@ __device__ void bwd_dxp_tile_mx(const Bwd& B, int tile, int nt, bf16_t* smem) {
   const Staged<TL::BM, TL::BN> st{smem};
   tile_visit<TL>(acc, [&](int row, int col, float v) { st.put(row, col, v); });
   st.flush(n, [&](int row) { return B.dxp + (size_t)(r0 + row) * d + c0; });
+}
+
+// ---------------------------------------------------------------- wgrad
+// The weight gradients' operands quantised along the rows of each row tile
+// (blocks of 32 rows from the tile's first row, hence from the expert's
+// first row) and stored transposed in row-tile slots (Bwd::kcap); rows past
+// a tile's count enter as zeros.  Thread c of a workgroup takes column c of
+// one 32-row block: blockIdx.y is the block (tile y / 4, rows 32 (y % 4)
+// ..), blockIdx.z + Z0 the operand:
+//   0  x rows through src            -> xT   [d, kcap]
+//   1  g_r dY rows through src       -> gT   [d, kcap]  (the product in fp32)
+//   2  H rows                        -> hT   [I, kcap]
+//   3  [dA | dB] rows                -> dabT [2I, kcap]
+// The 32 loads of a thread read one column of 32 rows; a workgroup's loads
+// of one row are 512 consecutive bytes.
+template <int Z0>
+__global__ void __launch_bounds__(256) k_mx_quant_tiles(Bwd B) {
+  const int z = Z0 + (int)blockIdx.z;
+  const int t = blockIdx.y >> 2, q = blockIdx.y & 3;
+  if (t >= min(*B.s.n_mtiles, B.max_tiles)) return;  // the same for the whole block
+  __shared__ int s_src[32];
+  __shared__ float s_g[32];
+  const TileRows tr = bwd_tile(B, t);
+  const int i0 = 32 * q;
+  if (threadIdx.x < 32) {
+    const int r = clamp_row(tr.r0 + min(i0 + (int)threadIdx.x, max(tr.n - 1, 0)), B.R);
+    s_src[threadIdx.x] = z < 2 ? clamp_token(B.src[r], B.T) : 0;
+    s_g[threadIdx.x] = z == 1 ? B.grow[r] : 1.0f;
+  }
+  __syncthreads();
+  const int C = z < 2 ? B.d : z == 2 ? B.I : 2 * B.I;
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c >= C) return;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int i = i0 + j;
+    float x = 0.0f;
+    if (i < tr.n) {  // the same for every thread of the block
+      const size_t r = (size_t)(tr.r0 + i);
+      if (z == 0)
+        x = bf16_to_f32(B.x[(size_t)s_src[j] * B.d + c]);
+      else if (z == 1)
+        x = bf16_to_f32(B.dy[(size_t)s_src[j] * B.d + c]) * s_g[j];
+      else if (z == 2)
+        x = bf16_to_f32(B.h[r * B.I + c]);
+      else
+        x = bf16_to_f32(B.dab[r * 2 * B.I + c]);
+    }
+    v[j] = x;
+  }
+  uint32_t w[8];
+  const uint32_t sc = mx_quant32(v, w);
+  uint8_t* codes = z == 0 ? B.xT : z == 1 ? B.gT : z == 2 ? B.hT : B.dabT;
+  uint8_t* scales = z == 0 ? B.xTs : z == 1 ? B.gTs : z == 2 ? B.hTs : B.dabTs;
+  uint4* dst = (uint4*)(codes + (size_t)c * B.kcap + (size_t)t * B.BM + i0);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[(size_t)c * (B.kcap / 32) + (size_t)t * (B.BM / 32) + q] = (uint8_t)sc;
+}
+
+// One MXFP8 weight-gradient tile: acc = sum over the expert's row-tile
+// slots [t0, t1) of A row r and B row n (both k-contiguous transposed
+// operands, kcap codes and kcap / 32 scales a row).  arow(r), brow(n): the
+// operand row of tile row r / column n.
+template <class AR, class BR>
+__device__ __forceinline__ void wgrad_tile_mx(const Bwd& B, int t0, int t1, AR arow, BR brow,
+                                              const uint8_t* acodes, const uint8_t* ascales,
+                                              const uint8_t* bcodes, const uint8_t* bscales, bf16_t* smem,
+                                              f32x16_t (&acc)[TileMX128::MI][TileMX128::NJ]) {
+  typedef TileMX128 TL;
+  const size_t kc = (size_t)B.kcap, ks = kc / 32;
+  const size_t k0 = (size_t)t0 * B.BM, s0 = (size_t)t0 * (B.BM / 32);
+  KRowsMX<TL::BM, TL::BN> la;
+  KRows<TL::BN> lb;
+  la.init([&](int r) { return acodes + (size_t)arow(r) * kc + k0; },
+          [&](int r) { return ascales + (size_t)arow(r) * ks + s0; },
+          [&](int n) { return bscales + (size_t)brow(n) * ks + s0; }, false);
+  lb.init([&](int n) { return (const bf16_t*)(bcodes + (size_t)brow(n) * kc + k0); });
+  tile_mainloop<TL>((t1 - t0) * B.BM / 128, smem, acc, la, lb);
+}
+
+// The expert's row-tile slots [t0, t1), clamped.
+__device__ __forceinline__ void expert_slots(const Bwd& B, int e, int& t0, int& t1) {
+  t0 = min(max(B.etile[e], 0), B.max_tiles);
+  t1 = min(max(B.etile[e + 1], t0), B.max_tiles);
+}
+
+// dW2_e in MXFP8 for one band (the bf16 band's task split): output rows n0
+// .. +128 of d over kWgradPerTicket column tiles of I, each a full pass
+// over the expert's slots (an expert without rows has none: zeros).
+__device__ void bwd_dw2_band_mx(const Bwd& B, int rank, int task, bf16_t* smem) {
+  typedef TileMX128 TL;
+  const int e = min(max(B.eorder[min(rank, B.E - 1)], 0), B.E - 1);
+  const int chunks = cdiv(B.nW2n, kWgradPerTicket);
+  const int n0 = (task / chunks) * TL::BM;
+  const int cb = (task % chunks) * kWgradPerTicket, nc = min(kWgradPerTicket, B.nW2n - cb);
+  const int d = B.d, I = B.I;
+  int t0, t1;
+  expert_slots(B, e, t0, t1);
+  bf16_t* out = B.dw2 + (size_t)e * d * I + (size_t)n0 * I;
+  bf16_t* stage = smem + TL::smem_bytes / sizeof(bf16_t);
+  for (int c = 0; c < nc; ++c) {
+    const int c0 = (cb + c) * TL::BN;
+    f32x16_t acc[TL::MI][TL::NJ];
+    wgrad_tile_mx(B, t0, t1, [&](int r) { return n0 + r; }, [&](int n) { return c0 + n; }, B.gT, B.gTs, B.hT,
+                  B.hTs, smem, acc);
+    tile_store_staged<TL>(acc, [&](int wm) { return out + (size_t)(wm * TL::WM) * I + c0; }, I, stage);
+  }
+}
+
+// dW1_e and dW3_e in MXFP8 for one band: tile rows 0..63 are dW1 rows i0
+// .., rows 64..127 dW3 rows i0 .. (dA^T and dB^T rows of dabT), over
+// kWgradPerTicket column tiles of d.
+__device__ void bwd_dw13_band_mx(const Bwd& B, int rank, int task, bf16_t* smem) {
+  typedef TileMX128 TL;
+  const int e = min(max(B.eorder[min(rank, B.E - 1)], 0), B.E - 1);
+  const int chunks = cdiv(B.nW13n, kWgradPerTicket);
+  const int i0 = (task / chunks) * (TL::BM / 2);
+  const int cb = (task % chunks) * kWgradPerTicket, nc = min(kWgradPerTicket, B.nW13n - cb);
+  const int d = B.d, I = B.I;
+  int t0, t1;
+  expert_slots(B, e, t0, t1);
+  bf16_t* o1 = B.dw1 + (size_t)e * I * d + (size_t)i0 * d;
+  bf16_t* o3 = B.dw3 + (size_t)e * I * d + (size_t)i0 * d;
+  bf16_t* stage = smem + TL::smem_bytes / sizeof(bf16_t);
+  static_assert(TL::WM == TL::BM / 2, "one wave row block per gradient");
+  for (int c = 0; c < nc; ++c) {
+    const int c0 = (cb + c) * TL::BN;
+    f32x16_t acc[TL::MI][TL::NJ];
+    wgrad_tile_mx(B, t0, t1, [&](int r) { return r < TL::BM / 2 ? i0 + r : I + i0 + r - TL::BM / 2; },
+                  [&](int n) { return c0 + n; }, B.dabT, B.dabTs, B.xT, B.xTs, smem, acc);
+    tile_store_staged<TL>(acc, [&](int wm) { return (wm ? o3 : o1) + c0; }, d, stage);
+  }
 }
 
 // Quantisation of the transpose of each [rows, cols] bf16 matrix of a

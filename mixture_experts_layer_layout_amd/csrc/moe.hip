@@ -127,8 +127,9 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
   p->o_xs = p->mxfp8 ? take((size_t)T * (d / 32)) : 0;
   p->o_big1 = take(R * d * es);
   p->o_big2 = take(R * d * es);
+  p->mx_wgrad = p->mxfp8 && (D->flags & MOE_FLAG_MXFP8_WGRAD) != 0;
   if (p->bwd_ok && !fwd_only) {
-    p->o_gg = take(R * d * 2);
+    if (!p->mx_wgrad) p->o_gg = take(R * d * 2);
     p->o_zero = take(((size_t)2 * I + d + 256) * 2);
     p->o_dab = take(R * 2 * I * 2);
     p->o_dgp = take((size_t)p->nNdh * R * 4);
@@ -137,6 +138,19 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
       p->o_dys = take((size_t)T * (d / 32));
       p->o_dabq = take(R * 2 * I);
       p->o_dabs = take(R * 2 * (I / 32));
+    }
+    if (p->mx_wgrad) {
+      // the weight gradients' operands along the rows, in row-tile slots
+      p->kcap = p->max_tiles * TileDH::BM;
+      const size_t kc = (size_t)p->kcap;
+      p->o_xT = take((size_t)d * kc);
+      p->o_xTs = take((size_t)d * (kc / 32));
+      p->o_gT = take((size_t)d * kc);
+      p->o_gTs = take((size_t)d * (kc / 32));
+      p->o_hT = take((size_t)I * kc);
+      p->o_hTs = take((size_t)I * (kc / 32));
+      p->o_dabT = take((size_t)2 * I * kc);
+      p->o_dabTs = take((size_t)2 * I * (kc / 32));
     }
   }
   if (!fwd_only) {
@@ -563,6 +577,18 @@ __global__ void __launch_bounds__(256, 2) k_bwd_dw13(Bwd B) {
   bwd_dw13_band(B, blockIdx.x / per, blockIdx.x % per, (bf16_t*)smem);
 }
 
+__global__ void __launch_bounds__(256, 2) k_bwd_dw2_mx(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  const int per = B.nW2m * cdiv(B.nW2n, kWgradPerTicket);
+  bwd_dw2_band_mx(B, blockIdx.x / per, blockIdx.x % per, (bf16_t*)smem);
+}
+
+__global__ void __launch_bounds__(256, 2) k_bwd_dw13_mx(Bwd B) {
+  extern __shared__ __align__(16) char smem[];
+  const int per = B.nW13m * cdiv(B.nW13n, kWgradPerTicket);
+  bwd_dw13_band_mx(B, blockIdx.x / per, blockIdx.x % per, (bf16_t*)smem);
+}
+
 // dX as a plain launch after the persistent ones (skipped when a bounded
 // wait of the call gave up: the rows it sums were not computed).
 __global__ void __launch_bounds__(256) k_bwd_dx(Bwd B) {
@@ -582,7 +608,7 @@ constexpr int bwd_occupancy(unsigned mask) {
   return mask == 0x7Fu || mask == 0x57u || mask == 0x28u ? 1 : 2;
 }
 
-// MX: the dh and dxp tasks take the MXFP8 tiles (bwd_mx.h).
+// MX: every GEMM task takes the MXFP8 tiles (bwd_mx.h).
 template <unsigned MASK, bool MX = false>
 __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
   extern __shared__ __align__(16) char smem[];
@@ -648,12 +674,19 @@ __global__ void __launch_bounds__(256, bwd_occupancy(MASK)) k_fused_bwd(Bwd B) {
       const int rank = t / span, band = t % span;
       if (band >= per) continue;  // the last slice's padding
       if ((MASK & 8u) && ph == 3) {
-        bwd_dw2_band(B, rank, band, (bf16_t*)smem);
+        if constexpr (MX)
+          bwd_dw2_band_mx(B, rank, band, (bf16_t*)smem);
+        else
+          bwd_dw2_band(B, rank, band, (bf16_t*)smem);
       } else if (MASK & 0x20u) {
         const int e = min(max(B.eorder[min(rank, B.E - 1)], 0), B.E - 1);
         const int need = (B.etile[e + 1] - B.etile[e]) * B.nNdh;
-        if (wait_geq(&B.s.aux1[e], need, W, &s_flag))
-          bwd_dw13_band(B, rank, band, (bf16_t*)smem);
+        if (wait_geq(&B.s.aux1[e], need, W, &s_flag)) {
+          if constexpr (MX)
+            bwd_dw13_band_mx(B, rank, band, (bf16_t*)smem);
+          else
+            bwd_dw13_band(B, rank, band, (bf16_t*)smem);
+        }
       }
     } else if ((MASK & 4u) && ph == 2) {
       if (t >= s_nmt * B.nNdh) continue;
@@ -846,10 +879,11 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
   // weight-gradient tiles: their main loop's LDS plus the store staging
   const size_t sm_dh = TileDH::smem_bytes, sm_dw = TileDW::smem_bytes + kWgradStageBytes;
   if (p.mxfp8) {
-    // MXFP8 data gradients: the phases of the bf16 backward (persistent
-    // launches, one per phase, or ordinary grids), with dh and dxp on the
-    // MXFP8 tiles and the two quantisations (dY before dh, [dA | dB] after
-    // it) as plain launches in between
+    // MXFP8: the phases of the bf16 backward (persistent launches, one per
+    // phase, or ordinary grids) on the MXFP8 tiles, with the quantisations
+    // as plain launches in between: dY along d before dh; the weight
+    // gradients' x, g dY and H operands along the rows once the row tiles
+    // and sources are known; [dA | dB] along I and along the rows after dh
     B.w1t = (const uint8_t*)w->w1; B.w3t = (const uint8_t*)w->w3; B.w2t = (const uint8_t*)w->w2;
     B.w1ts = w->w1_scale; B.w3ts = w->w3_scale; B.w2ts = w->w2_scale;
     B.dyq = at<uint8_t>(ws, p.o_dyq); B.dys = at<uint8_t>(ws, p.o_dys);
@@ -857,37 +891,62 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
     B.mx_wide_d = p.d % 512 == 0 && al16(B.dys) && al16(B.w2ts);
     B.mx_wide_i = p.I % 512 == 0 && al16(B.dabs) && al16(B.w1ts) && al16(B.w3ts);
-    const size_t sm_mx = TileMX128::smem_bytes;
+    const bool mxw = p.mx_wgrad;
+    B.mx = mxw ? 1 : 0;
+    B.kcap = p.kcap;
+    B.xT = at<uint8_t>(ws, p.o_xT); B.xTs = at<uint8_t>(ws, p.o_xTs);
+    B.gT = at<uint8_t>(ws, p.o_gT); B.gTs = at<uint8_t>(ws, p.o_gTs);
+    B.hT = at<uint8_t>(ws, p.o_hT); B.hTs = at<uint8_t>(ws, p.o_hTs);
+    B.dabT = at<uint8_t>(ws, p.o_dabT); B.dabTs = at<uint8_t>(ws, p.o_dabTs);
+    const size_t sm_mx = TileMX128::smem_bytes, sm_dwmx = TileMX128::smem_bytes + kWgradStageBytes;
     static_assert(2 * (TileMX128::smem_bytes + 1024 + 4 * kEtileLds) <= 160 * 1024, "two MXFP8 workgroups per CU");
+    static_assert(2 * (TileMX128::smem_bytes + kWgradStageBytes + 1024) <= 160 * 1024,
+                  "two MXFP8 weight-gradient workgroups per CU");
+    // operand quantisation along the rows: x, g dY, H in one launch, [dA |
+    // dB] after dh (every block of a listed row tile; the others exit)
+    const dim3 gq3(cdiv(p.d > p.I ? p.d : p.I, kThreads), 4 * p.max_tiles, 3), gq1(cdiv(2 * p.I, kThreads), 4 * p.max_tiles, 1);
     if (D->fused) {
       int rc = p.R > 0 ? mxfp8_quantize_rows(B.dy, p.T, p.d, B.dyq, B.dys, st) : MOE_OK;
       hipLaunchKernelGGL(k_bwd_prep, dim3(1 + p.nRP), dim3(256), 0, st, B);
+      if (mxw && p.R > 0) hipLaunchKernelGGL(k_mx_quant_tiles<0>, gq3, dim3(kThreads), 0, st, B);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x04u, true>(D, B, sm_mx, st);
-      if (rc == MOE_OK && p.R > 0) rc = mxfp8_quantize_rows(B.dab, p.R, 2 * (int64_t)p.I, B.dabq, B.dabs, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
+      if (rc == MOE_OK && p.R > 0) {
+        rc = mxfp8_quantize_rows(B.dab, p.R, 2 * (int64_t)p.I, B.dabq, B.dabs, st);
+        if (mxw) hipLaunchKernelGGL(k_mx_quant_tiles<3>, gq1, dim3(kThreads), 0, st, B);
+      }
+      if (rc == MOE_OK) rc = mxw ? launch_fused_bwd<0x08u, true>(D, B, sm_dwmx, st) : launch_fused_bwd<0x08u>(D, B, sm_dw, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x10u, true>(D, B, sm_mx, st);
-      if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
+      if (rc == MOE_OK) rc = mxw ? launch_fused_bwd<0x20u, true>(D, B, sm_dwmx, st) : launch_fused_bwd<0x20u>(D, B, sm_dw, st);
       if (rc != MOE_OK) return rc;
       if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
       return launch_status();
     }
-    if (!set_smem(k_bwd_dh_mx, sm_mx) || !set_smem(k_bwd_dxp_mx, sm_mx) || !set_smem(k_bwd_dw2, sm_dw) ||
-        !set_smem(k_bwd_dw13, sm_dw))
+    if (!set_smem(k_bwd_dh_mx, sm_mx) || !set_smem(k_bwd_dxp_mx, sm_mx) || !set_smem(k_bwd_dw2_mx, sm_dwmx) ||
+        !set_smem(k_bwd_dw13_mx, sm_dwmx) || !set_smem(k_bwd_dw2, sm_dw) || !set_smem(k_bwd_dw13, sm_dw))
       return MOE_ERR_HIP;
     hipLaunchKernelGGL(k_bwd_setup, dim3(1), dim3(256), 0, st, B);
     if (p.nRP > 0) hipLaunchKernelGGL(k_bwd_rowprep, dim3(p.nRP), dim3(256), 0, st, B);
     if (p.R > 0) {
       int rc = mxfp8_quantize_rows(B.dy, p.T, p.d, B.dyq, B.dys, st);
       if (rc != MOE_OK) return rc;
+      if (mxw) hipLaunchKernelGGL(k_mx_quant_tiles<0>, gq3, dim3(kThreads), 0, st, B);
       hipLaunchKernelGGL(k_bwd_dh_mx, dim3(p.max_tiles * p.nNdh), dim3(256), sm_mx, st, B);
     }
-    hipLaunchKernelGGL(k_bwd_dw2, dim3(p.E * p.nW2m * cdiv(p.nW2n, kWgradPerTicket)), dim3(256), sm_dw, st, B);
+    const dim3 g2(p.E * p.nW2m * cdiv(p.nW2n, kWgradPerTicket)), g13(p.E * p.nW13m * cdiv(p.nW13n, kWgradPerTicket));
+    if (mxw)
+      hipLaunchKernelGGL(k_bwd_dw2_mx, g2, dim3(256), sm_dwmx, st, B);
+    else
+      hipLaunchKernelGGL(k_bwd_dw2, g2, dim3(256), sm_dw, st, B);
     if (p.R > 0) {
       int rc = mxfp8_quantize_rows(B.dab, p.R, 2 * (int64_t)p.I, B.dabq, B.dabs, st);
       if (rc != MOE_OK) return rc;
+      if (mxw) hipLaunchKernelGGL(k_mx_quant_tiles<3>, gq1, dim3(kThreads), 0, st, B);
       hipLaunchKernelGGL(k_bwd_dxp_mx, dim3(p.max_tiles * p.nNdx), dim3(256), sm_mx, st, B);
     }
-    hipLaunchKernelGGL(k_bwd_dw13, dim3(p.E * p.nW13m * cdiv(p.nW13n, kWgradPerTicket)), dim3(256), sm_dw, st, B);
+    if (mxw)
+      hipLaunchKernelGGL(k_bwd_dw13_mx, g13, dim3(256), sm_dwmx, st, B);
+    else
+      hipLaunchKernelGGL(k_bwd_dw13, g13, dim3(256), sm_dw, st, B);
     if (p.nC > 0) hipLaunchKernelGGL(k_bwd_dx, dim3(p.nC), dim3(256), 0, st, B);
     return launch_status();
   }

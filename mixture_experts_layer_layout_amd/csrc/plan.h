@@ -38,6 +38,9 @@ struct Plan {
   size_t o_xs;     // MXFP8: x scales (the codes sit at o_big1)
   size_t o_rdz, o_rpart, o_rpbias;  // router backward: dz, dWr and dbias partial sums
   size_t o_dyq, o_dys, o_dabq, o_dabs;  // MXFP8 backward: dY and [dA | dB] codes and scales
+  bool mx_wgrad;   // MXFP8 backward with MXFP8 weight gradients (MOE_FLAG_MXFP8_WGRAD)
+  int kcap;        // then: row-tile slots of the weight gradients' operands (max_tiles * 128)
+  size_t o_xT, o_xTs, o_gT, o_gTs, o_hT, o_hTs, o_dabT, o_dabTs;  // their codes and scales
   size_t total;
 };
 

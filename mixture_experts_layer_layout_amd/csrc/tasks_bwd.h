@@ -104,6 +104,21 @@ struct Bwd {
   uint8_t* dabq;         // [R, 2I] codes of [dA | dB]
   uint8_t* dabs;         // [R, 2I/32]
   int mx_wide_d, mx_wide_i;  // scale rows read 4 stages at a time (KRowsMX)
+  // MXFP8 weight gradients: their operands quantised along the rows (the
+  // contraction axis) and stored transposed in row-tile slots: column c of
+  // an operand holds local row i of row tile t at byte c * kcap + t * BM +
+  // i (code 0 past the tile's rows), its scales at c * kcap / 32 + t * BM /
+  // 32 + i / 32.  An expert's K range is its row tiles' slots.
+  int mx;                // MXFP8 backward (rowprep then pulls no Xp, gG rows)
+  int kcap;              // max_tiles * BM
+  uint8_t* xT;           // [d, kcap]  x rows (through src)
+  uint8_t* xTs;
+  uint8_t* gT;           // [d, kcap]  g_r dY rows (through src)
+  uint8_t* gTs;
+  uint8_t* hT;           // [I, kcap]  H rows
+  uint8_t* hTs;
+  uint8_t* dabT;         // [2I, kcap] [dA | dB] rows
+  uint8_t* dabTs;
   Sync s;
 };
 
@@ -157,7 +172,7 @@ __device__ void bwd_setup(const Bwd& B, int* sh /* >= 2*kMaxE + 16 ints */) {
 // Token-major row preparation for kPrepTok tokens: each token's x and dY
 // rows are read once and written to its k expert rows, dY scaled by the
 // slot's gate (Xp[r] = x[t], G[r] = g dY[t] for r = inv[t k + j]); the row's
-// source token and gate are recorded.
+// source token and gate are recorded (all the MXFP8 backward needs).
 __device__ void bwd_rowprep(const Bwd& B, int task) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvec = B.d / 8;
@@ -172,6 +187,7 @@ __device__ void bwd_rowprep(const Bwd& B, int task) {
       B.src[lane_row] = t;
       B.grow[lane_row] = lane_g;
     }
+    if (B.mx) continue;  // the MXFP8 weight gradients quantise from x and dY through src
     wave_push_row((const uint4*)(B.x + (size_t)t * B.d), (uint4*)B.xp, nvec, k, B.R, lane_row,
                   [](int, uint4 u) { return u; });
     wave_push_row((const uint4*)(B.dy + (size_t)t * B.d), (uint4*)B.gg, nvec, k, B.R, lane_row, [&](int j, uint4 u) {

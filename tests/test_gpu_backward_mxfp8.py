@@ -1,9 +1,11 @@
-"""GPU parity of the MXFP8 backward (moe_backward with MXFP8 experts: every
-GEMM on the scaled matrix cores -- the data gradients dHu = G W2 and dXp =
-dA W1 + dB W3 with their operands quantised along d and along I, the weight
-gradients dW2 = (g G)^T H, dW1 = dA^T x, dW3 = dB^T x with theirs quantised
-along the expert's rows) and of moe_quantize_mxfp8_t against the fp64
-oracle (oracle/mxfp8.py backward_mxfp8 and quantize):
+"""GPU parity of the MXFP8 backward (moe_backward with MXFP8 experts: the
+data gradients dHu = G W2 and dXp = dA W1 + dB W3 on the scaled matrix
+cores with their operands quantised along d and along I; the weight
+gradients dW2 = (g G)^T H, dW1 = dA^T x, dW3 = dB^T x in bf16 by default,
+and with MOE_FLAG_MXFP8_WGRAD on the scaled matrix cores too, their
+operands quantised along the expert's rows) and of moe_quantize_mxfp8_t
+against the fp64 oracle (oracle/mxfp8.py backward_mxfp8 with mx_wgrad
+matching the flag, and quantize):
 
   * the transposed quantisation: codes and scales bit-exact (bf16 inputs,
     so every scale and rounding decision is exact on both sides), with
@@ -56,27 +58,31 @@ SMALL = {
 }
 
 
-def run(w, seed):
+WG = api.MOE_FLAG_MXFP8_WGRAD
+
+
+def run(w, seed, flags=0):
     inp = synth.make_inputs(w, seed, with_dy=True)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y, sv = layer.forward(w, dev, fused=True)
-    g = layer.backward(w, dev, sv)
+    g = layer.backward(w, dev, sv, flags=flags)
     torch.cuda.synchronize()
     assert sv["status"].item() == 0
     return inp, sv, g
 
 
+@pytest.mark.parametrize("flags", [0, WG])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_backward_mxfp8_matches_oracle(name):
+def test_backward_mxfp8_matches_oracle(name, flags):
     w = SMALL[name]
-    inp, sv, g = run(w, 21)
+    inp, sv, g = run(w, 21, flags)
     h = {k: (host(v) if v is not None else None) for k, v in inp.items()}
     logits = sv["logits"].cpu().numpy()
     f = Q.forward_mxfp8(h["x"], h["wr"], h["bias"], h["w1"], h["w3"], h["w2"], w.k, w.score, w.renorm,
                         logits=logits)
     assert np.array_equal(host(sv["topk_idx"]), f["topk_idx"])
     assert np.array_equal(host(sv["perm"]), f["perm"])
-    b = Q.backward_mxfp8(h["dy"], h["x"], f, h["w1"], h["w3"], h["w2"], w.k)
+    b = Q.backward_mxfp8(h["dy"], h["x"], f, h["w1"], h["w3"], h["w2"], w.k, mx_wgrad=bool(flags & WG))
     errs = {"dx": row_rel_err(host(g["dx"]), b["dx"]), "dgate": dgate_err(host(g["dgate"]), b["dgate"])}
     for n in ("dw1", "dw3", "dw2"):
         got = host(g[n])
@@ -87,27 +93,29 @@ def test_backward_mxfp8_matches_oracle(name):
                 continue
             worst = max(worst, row_rel_err(got[e].reshape(1, -1), b[n][e].reshape(1, -1)))
         errs[n] = worst
-    print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+    print(name, hex(flags), {k: f"{v:.2e}" for k, v in errs.items()})
     for n, e in errs.items():
         assert e <= MX_TOL, f"{n} max row-relative error {e:.3e} > {MX_TOL}"
 
 
-def test_backward_mxfp8_persistent_equals_plain_bitwise():
+@pytest.mark.parametrize("flags", [0, WG])
+def test_backward_mxfp8_persistent_equals_plain_bitwise(flags):
     # the persistent launches and the ordinary grids run the same tiles
     w = SMALL["wide-mx"]
     inp = synth.make_inputs(w, 6, with_dy=True)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y, sv = layer.forward(w, dev, fused=True)
-    g1 = layer.backward(w, dev, sv, fused=True)
-    g2 = layer.backward(w, dev, sv, fused=False)
+    g1 = layer.backward(w, dev, sv, fused=True, flags=flags)
+    g2 = layer.backward(w, dev, sv, fused=False, flags=flags)
     torch.cuda.synchronize()
     assert sv["status"].item() == 0
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
 
 
+@pytest.mark.parametrize("flags", [0, WG])
 @pytest.mark.parametrize("n_wg", [1, 7, 1000])
-def test_backward_mxfp8_any_grid_bitwise(n_wg):
+def test_backward_mxfp8_any_grid_bitwise(n_wg, flags):
     # the persistent launches with any number of workgroups (one workgroup
     # runs every task in ticket order, so every wait is on work already
     # claimed) give the default grid's bits
@@ -115,28 +123,29 @@ def test_backward_mxfp8_any_grid_bitwise(n_wg):
     inp = synth.make_inputs(w, 8, with_dy=True)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y, sv = layer.forward(w, dev, fused=True)
-    g1 = layer.backward(w, dev, sv, fused=True)
-    g2 = layer.backward(w, dev, sv, fused=True, n_workgroups=n_wg)
+    g1 = layer.backward(w, dev, sv, fused=True, flags=flags)
+    g2 = layer.backward(w, dev, sv, fused=True, n_workgroups=n_wg, flags=flags)
     torch.cuda.synchronize()
     assert sv["status"].item() == 0
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
 
 
-def test_backward_mxfp8_repeatable_and_empty():
+@pytest.mark.parametrize("flags", [0, WG])
+def test_backward_mxfp8_repeatable_and_empty(flags):
     w = SMALL["dsv3-mx-small"]
     inp = synth.make_inputs(w, 5, with_dy=True)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y, sv = layer.forward(w, dev, fused=True)
-    g1 = layer.backward(w, dev, sv)
-    g2 = layer.backward(w, dev, sv)
+    g1 = layer.backward(w, dev, sv, flags=flags)
+    g2 = layer.backward(w, dev, sv, flags=flags)
     torch.cuda.synchronize()
     for n in g1:
         assert torch.equal(g1[n], g2[n]), n
     w0 = w.shrink(T=0)
     inp0 = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w0, 0, with_dy=True).items()}
     y0, sv0 = layer.forward(w0, inp0, fused=True)
-    g0 = layer.backward(w0, inp0, sv0)
+    g0 = layer.backward(w0, inp0, sv0, flags=flags)
     torch.cuda.synchronize()
     assert g0["dx"].numel() == 0
     for n in ("dw1", "dw3", "dw2"):
