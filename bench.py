@@ -336,13 +336,19 @@ def main():
         xs_ = torch.empty((w.R, w.d // 32), dtype=torch.uint8, device="cuda") if w.experts == "mxfp8" else None
         lay = {n: torch.empty_like(saved[n]) for n in ("counts", "offsets", "perm", "inv")}
         lws = layer.workspace(gdesc)
+        # the combine alone (moe_combine, the forward's own merge kernel) on
+        # this step's gates and layout, over an expert-output buffer
+        yp_ = torch.zeros((w.R, w.d), dtype=torch.bfloat16, device="cuda")
+        yc_ = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
         reps = 20
         for name, fn in (("layout", lambda: api.moe_layout(gdesc, saved["topk_idx"], lay["counts"], lay["offsets"],
                                                            lay["perm"], lay["inv"], None, lws, stream)),
                          ("gather", lambda: api.moe_gather(gdesc, dev["x"], None, xq_, xs_, stream,
                                                            inv=saved["inv"])),
                          ("gather_pull", lambda: api.moe_gather(gdesc, dev["x"], saved["perm"], xq_, xs_,
-                                                                stream))):
+                                                                stream)),
+                         ("combine", lambda: api.moe_combine(gdesc, yp_, saved["gate"], saved["inv"], yc_,
+                                                             stream))):
             fn()
             a, b = ev(), ev()
             a.record(stream)
@@ -351,7 +357,7 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             side[name] = a.elapsed_time(b) / reps
-        del xq_, xs_, lay, lws
+        del xq_, xs_, lay, lws, yp_, yc_
     if w.backward and not (w.score == "softmax" and not w.renorm):
         # the router backward (moe_router_backward) after the step's
         # backward, timed apart: it is not part of the measured step
@@ -421,6 +427,12 @@ def main():
         phases["gather_gbs"] = round(gbytes / (side["gather"] * 1e-3) / 1e9, 1)
         phases["gather_hbm_frac"] = round(gbytes / (side["gather"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         phases["gather_pull_gbs"] = round(gbytes / (side["gather_pull"] * 1e-3) / 1e9, 1)
+        phases["gather_pull_hbm_frac"] = round(gbytes / (side["gather_pull"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        # combine: the expert outputs read, y written, gates and inv read
+        cbytes = w.R * w.d * 2 + w.T * w.d * 2 + w.R * 8
+        phases["combine_ms"] = round(side["combine"], 4)
+        phases["combine_gbs"] = round(cbytes / (side["combine"] * 1e-3) / 1e9, 1)
+        phases["combine_hbm_frac"] = round(cbytes / (side["combine"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if "router_backward" in side:
         phases["router_backward_ms"] = round(side["router_backward"], 4)
 

@@ -331,6 +331,21 @@ MOE_API int moe_forward_noalloc(const moe_desc* desc, const void* x, const void*
                                 const float* bias, const moe_weights* w, void* y,
                                 const moe_saved* saved, void* stream);
 
+/* The weighted merge on its own (MoK flash §01: each expert's result
+ * returns to its token's position, weighted by the token's gates) -- the
+ * forward's last step, for callers that run the expert GEMMs themselves.
+ *   yp   act [R, d] input, the expert outputs in expert order (the layout
+ *        of moe_layout)
+ *   gate float [T, k], inv int32 [R]: the routing's gates and moe_layout's
+ *        inverse permutation
+ *   y    act [T, d] output, y[t] = sum_j gate[t, j] yp[inv[t k + j]],
+ *        accumulated in fp32 in slot order j = 0 .. k-1: the forward's own
+ *        combine, bit for bit
+ * Entries of inv outside [0, R) read row 0.  No workspace; T = 0 is a
+ * no-op.  Activation type desc->act_dtype (bf16 or f32). */
+MOE_API int moe_combine(const moe_desc* desc, const void* yp, const float* gate, const int32_t* inv,
+                        void* y, void* stream);
+
 /* Backward of the expert path with the routing frozen (MoK flash §01/§02:
  * pull reverse-combine, expert dgrad and wgrad, push reverse-dispatch).
  * bf16 activations; bf16 or MXFP8 experts (below).

@@ -76,6 +76,7 @@ _lib.moe_quantize_mxfp8.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, c_
                                     c_void_p, c_void_p]
 _lib.moe_quantize_mxfp8_t.argtypes = [c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       c_void_p, c_void_p, c_void_p]
+_lib.moe_combine.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
 _lib.moe_forward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWeights),
                              c_void_p, _P(MoeSaved), c_void_p, ctypes.c_size_t, c_void_p]
 _lib.moe_forward_noalloc.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, _P(MoeWeights),
@@ -89,12 +90,12 @@ _lib.moe_router_backward.argtypes = [_P(MoeDesc), c_void_p, c_void_p, c_void_p, 
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_status_string.restype = ctypes.c_char_p
 for _f in ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather", "moe_quantize_mxfp8",
-           "moe_quantize_mxfp8_t", "moe_forward", "moe_forward_noalloc", "moe_backward",
+           "moe_quantize_mxfp8_t", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_backward",
            "moe_router_backward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("moe_workspace_size", "moe_route", "moe_layout", "moe_gather",
-           "moe_quantize_mxfp8", "moe_quantize_mxfp8_t", "moe_forward", "moe_forward_noalloc",
+           "moe_quantize_mxfp8", "moe_quantize_mxfp8_t", "moe_combine", "moe_forward", "moe_forward_noalloc",
            "moe_backward", "moe_router_backward", "moe_status_string")
 MOE_NOALLOC_SCRATCH_BYTES = 256 << 20
 
@@ -169,6 +170,11 @@ def moe_quantize_mxfp8_t(src, codes, scales, stream=None):
     rows, cols = src.shape[-2], src.shape[-1]
     _check(_lib.moe_quantize_mxfp8_t(_p(src), batch, rows, cols, _p(codes), _p(scales), _stream(stream)),
            "moe_quantize_mxfp8_t")
+
+
+def moe_combine(desc, yp, gate, inv, y, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(desc), _p(yp), _p(gate), _p(inv), _p(y), _stream(stream)),
+           "moe_combine")
 
 
 def make_weights(w1, w3, w2, w1_scale=None, w3_scale=None, w2_scale=None) -> MoeWeights:

@@ -356,6 +356,12 @@ __global__ void __launch_bounds__(256) k_combine(Fwd F) {
   combine_tokens<Act>(F, blockIdx.x);
 }
 
+// The same merge for moe_combine (no call state to consult).
+template <class Act>
+__global__ void __launch_bounds__(256) k_combine_alone(Fwd F) {
+  combine_tokens<Act>(F, blockIdx.x);
+}
+
 // The persistent forward: phases router slices (+ the MXFP8 quantisation
 // of x by token block) | top-k | layout | gather | up-projection tiles |
 // down-projection tiles | combine, claimed through
@@ -1094,6 +1100,29 @@ int moe_gather(const moe_desc* desc, const void* x, const int32_t* perm, const i
   else
     hipLaunchKernelGGL(k_gather_perm<bf16_t>, dim3(grid), dim3(256), 0, st, (const bf16_t*)x, perm, (bf16_t*)xp,
                        p.R, p.d, p.k);
+  return launch_status();
+}
+
+int moe_combine(const moe_desc* desc, const void* yp, const float* gate, const int32_t* inv, void* y,
+                void* stream) {
+  Plan p;
+  int rc = make_plan(desc, &p, true);
+  if (rc != MOE_OK) return rc;
+  if (p.macro) return MOE_ERR_UNSUPPORTED;
+  if (p.T == 0) return MOE_OK;
+  if (!yp || !gate || !inv || !y) return MOE_ERR_INVALID_ARG;
+  Fwd F;
+  memset(&F, 0, sizeof(F));
+  F.T = p.T; F.d = p.d; F.k = p.k; F.R = p.R; F.E = p.E;
+  F.yp = const_cast<void*>(yp);
+  F.gate = const_cast<float*>(gate);
+  F.inv = const_cast<int32_t*>(inv);
+  F.y = y;
+  hipStream_t st = (hipStream_t)stream;
+  if (p.f32)
+    hipLaunchKernelGGL(k_combine_alone<float>, dim3(p.nC), dim3(256), 0, st, F);
+  else
+    hipLaunchKernelGGL(k_combine_alone<bf16_t>, dim3(p.nC), dim3(256), 0, st, F);
   return launch_status();
 }
 
