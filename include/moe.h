@@ -106,10 +106,13 @@ typedef struct moe_desc {
   int32_t topk_group;
   float routed_scale;
   /* macro_tokens > 0 (and < T): moe_forward walks the tokens in macrobatches
-   * of this many tokens (the last one ragged), every macrobatch reusing one
-   * workspace sized for a macrobatch (moe_workspace_size returns that size):
-   * the staging rows are a fixed pool reused batch after batch, so memory
-   * stays bounded for any T.  Outputs are identical to one call over all T.
+   * of this many tokens (the last one ragged) through a ring of two
+   * workspace slots, each sized for one macrobatch (moe_workspace_size
+   * returns both): the staging rows are a fixed pool reused batch after
+   * batch, so memory stays bounded for any T (MoK flash §02, the ring token
+   * buffer).  With fused = 1 the merge of macrobatch i runs inside the
+   * launch of macrobatch i+1, beside its routing and dispatch.  Outputs are
+   * identical to one call over all T.
    * The saved layout (counts, offsets, perm, inv) and activations (a, b, h)
    * describe one layout over all T and must be NULL; logits, topk_idx, gate
    * and status are written.  The other calls return MOE_ERR_UNSUPPORTED
@@ -315,8 +318,8 @@ MOE_API int moe_forward(const moe_desc* desc, const void* x, const void* wr,
  *   Arguments as in moe_forward, without workspace and workspace_bytes.
  *   When the forward's workspace for all T tokens fits the array, one call
  *   runs and every saved output may be asked for.  Otherwise the tokens
- *   run in consecutive macrobatches of the most tokens whose workspace fits
- *   (at most desc->macro_tokens when that is set), as moe_forward does for
+ *   run in consecutive macrobatches of the most tokens whose two ring slots
+ *   fit (at most desc->macro_tokens when that is set), as moe_forward does for
  *   desc->macro_tokens: y and the per-token saved outputs (logits, topk_idx,
  *   gate, status) are written, and asking for the layout (counts, offsets,
  *   perm, inv) or the activations (a, b, h), which describe one batch over

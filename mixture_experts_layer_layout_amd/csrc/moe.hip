@@ -32,6 +32,8 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
   memset(p, 0, sizeof(*p));
   if (D->T < 0 || D->macro_tokens < 0) return MOE_ERR_INVALID_ARG;
   const bool macro = D->macro_tokens > 0 && D->macro_tokens < D->T;
+  // macrobatches run the forward only, through a ring of two slots
+  if (macro) fwd_only = true;
   // with macrobatches every size below is that of one macrobatch
   const int T = macro ? D->macro_tokens : D->T, d = D->d, E = D->E, k = D->k, I = D->I;
   if (d <= 0 || E <= 0 || k <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
@@ -158,7 +160,7 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
     p->o_rpart = take((size_t)kRbSplits * E * d * 4);
     p->o_rpbias = take((size_t)kRbSplits * E * 4);
   }
-  p->total = o;
+  p->total = macro ? 2 * align256(o) : o;
   return MOE_OK;
 }
 
@@ -353,13 +355,13 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_g2(Fwd F) {
 template <class Act>
 __global__ void __launch_bounds__(256) k_combine(Fwd F) {
   if (load_relaxed(F.s.abort)) return;
-  combine_tokens<Act>(F, blockIdx.x);
+  combine_tokens<Act>(merge_of(F), blockIdx.x);
 }
 
 // The same merge for moe_combine (no call state to consult).
 template <class Act>
 __global__ void __launch_bounds__(256) k_combine_alone(Fwd F) {
-  combine_tokens<Act>(F, blockIdx.x);
+  combine_tokens<Act>(merge_of(F), blockIdx.x);
 }
 
 // The persistent forward: phases router slices (+ the MXFP8 quantisation
@@ -403,7 +405,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         groups = 0;
         if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
         if (!((roles >> ph) & 1u)) return true;  // phase of the other side of the partition
-        if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0); return true; }
+        if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0) + F.prev_nC; return true; }
         if (ph == 1) { groups = F.nb * kTopkChunks; return true; }
         if (ph == 2) { groups = 1; return true; }
         if (c.nmt < 0) {
@@ -433,7 +435,11 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
     // A task whose wait fails (timeout or abort) does no work and raises
     // no counter (protocol.h).
     if ((MASK & 1u) && ph == 0) {
-      if (TL::kMX && t >= F.nb * F.S) {
+      const int nr = F.nb * F.S + (TL::kMX ? F.nb : 0);
+      if (t >= nr) {
+        // the previous macrobatch's merge (its operands are complete)
+        if (!load_relaxed(F.prev_abort)) combine_tokens<Act>(F.prev, t - nr);
+      } else if (TL::kMX && t >= F.nb * F.S) {
         quant_tokens(F, t - F.nb * F.S);
         signal_add<(MASK & 0x18u) != 0>(F.s.q_done, 1);  // read by gather, g1
       } else {
@@ -478,7 +484,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
       else
         signal_add<false>(F.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
-      if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(F, t);
+      if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(merge_of(F), t);
     }
   }
 }
@@ -791,8 +797,10 @@ static int launch_fused_bwd(const moe_desc* D, const Bwd& B, size_t smem, hipStr
   return launch_status();
 }
 
+// ring: a macrobatch of the ring (forward_in_batches): the default launch
+// structure, and this macrobatch's merge is left to the next launch.
 template <class Act, class TL>
-static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStream_t st) {
+static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStream_t st, bool ring = false) {
   constexpr bool isf = std::is_same<Act, float>::value;
   // the persistent kernel's LDS serves every task: GEMM stages, routing
   // masks (kMaxE u64), the layout scan (2 kMaxE + 16 ints), gather rows
@@ -806,6 +814,11 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
     return launch_status();
   }
   if (D->fused) {
+    if (ring) {
+      int rc = TL::kMX ? launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st) : launch_fused_fwd<Act, TL, 0x3Fu>(D, F, smem, st);
+      if (rc == MOE_OK && TL::kMX) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
+      return rc;
+    }
     if (D->flags & MOE_FLAG_PERSISTENT_SINGLE) return launch_fused_fwd<Act, TL, 0x7Fu>(D, F, smem, st);
     if (D->flags & MOE_FLAG_PERSISTENT_SPLIT) {
       // the same persistent scheduler, one launch per phase group
@@ -1145,8 +1158,8 @@ int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, int64_t c
   return launch_status();
 }
 
-static int forward_call(const Plan& p, const moe_desc* desc, const void* x, const void* wr, const float* bias,
-                        const moe_weights* w, void* y, const moe_saved* saved, void* workspace, hipStream_t st) {
+static Fwd forward_args(const Plan& p, const moe_desc* desc, const void* x, const void* wr, const float* bias,
+                        const moe_weights* w, void* y, const moe_saved* saved, void* workspace) {
   Fwd F = make_fwd(p, desc, workspace, saved);
   F.x = x; F.wr = wr; F.bias = bias; F.w1 = w->w1; F.w3 = w->w3; F.w2 = w->w2; F.y = y;
   if (p.mxfp8) {
@@ -1154,23 +1167,50 @@ static int forward_call(const Plan& p, const moe_desc* desc, const void* x, cons
     auto al16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
     F.mx_wide1 = p.d % 512 == 0 && al16(F.xs) && al16(F.w1s) && al16(F.w3s);
     F.mx_wide2 = p.I % 512 == 0 && al16(F.hs) && al16(F.w2s);
-    return forward_impl<bf16_t, TileMX128>(p, desc, F, st);
   }
-  if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st);
-  if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st);
-  if (p.BM == 64) return forward_impl<bf16_t, TileD256h>(p, desc, F, st);
-  return forward_impl<bf16_t, TileD256>(p, desc, F, st);
+  return F;
 }
 
-// Macrobatches: the forward over consecutive ranges of Tm tokens (the last
-// one ragged), each reusing the workspace (stream order keeps each one
-// after the previous).  Per-token outputs only (no layout over all tokens).
+static int forward_run(const Plan& p, const moe_desc* desc, const Fwd& F, hipStream_t st, bool ring = false) {
+  if (p.mxfp8) return forward_impl<bf16_t, TileMX128>(p, desc, F, st, ring);
+  if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st, ring);
+  if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st, ring);
+  if (p.BM == 64) return forward_impl<bf16_t, TileD256h>(p, desc, F, st, ring);
+  return forward_impl<bf16_t, TileD256>(p, desc, F, st, ring);
+}
+
+static int forward_call(const Plan& p, const moe_desc* desc, const void* x, const void* wr, const float* bias,
+                        const moe_weights* w, void* y, const moe_saved* saved, void* workspace, hipStream_t st) {
+  return forward_run(p, desc, forward_args(p, desc, x, wr, bias, w, y, saved, workspace), st);
+}
+
+// Bytes of one slot of the macrobatch ring: the forward's regions for Tm
+// tokens (0 for an invalid descriptor).
+static size_t forward_bytes(const moe_desc* desc, int T);
+static size_t ring_slot_bytes(const moe_desc* desc, int Tm) { return align256(forward_bytes(desc, Tm)); }
+
+// Macrobatches (MoK flash §02: token volume streamed through a fixed ring
+// of token buffers): the forward over consecutive ranges of Tm tokens (the
+// last one ragged) through a ring of two workspace slots, macrobatch i in
+// slot i % 2.  With the persistent path, the launch of macrobatch i also
+// runs the merge of macrobatch i-1 -- whose expert outputs sit in the other
+// slot, complete at the launch boundary -- as extra tasks of its first
+// phase, so that merge overlaps this macrobatch's routing and dispatch; the
+// last macrobatch's merge follows as a plain launch.  A slot is written
+// again two launches later, after the launch that merged from it has ended
+// (stream order), so every buffer is written once per launch as in a single
+// call.  Per-token outputs only (no layout over all tokens).
 static int forward_in_batches(const moe_desc* desc, int Tm, const void* x, const void* wr, const float* bias,
                               const moe_weights* w, void* y, const moe_saved* saved, void* workspace,
                               hipStream_t st) {
   const int T = desc->T, E = desc->E, k = desc->k, d = desc->d;
   const size_t es = desc->act_dtype == MOE_F32 ? 4 : 2;
-  for (int t0 = 0; t0 < T; t0 += Tm) {
+  const size_t slot = ring_slot_bytes(desc, Tm);
+  const bool ring = desc->fused != 0;
+  Fwd prev;
+  bool have_prev = false;
+  bool prev_f32 = false;
+  for (int t0 = 0, i = 0; t0 < T; t0 += Tm, ++i) {
     moe_desc md = *desc;
     md.T = T - t0 < Tm ? T - t0 : Tm;
     md.macro_tokens = 0;
@@ -1185,9 +1225,26 @@ static int forward_in_batches(const moe_desc* desc, int Tm, const void* x, const
       sm.gate = saved->gate ? saved->gate + (size_t)t0 * k : nullptr;
       sm.status = saved->status;
     }
-    rc = forward_call(pm, &md, (const char*)x + (size_t)t0 * d * es, wr, bias, w, (char*)y + (size_t)t0 * d * es,
-                      saved ? &sm : nullptr, workspace, st);
+    void* ws = (char*)workspace + (size_t)(i & 1) * slot;
+    Fwd F = forward_args(pm, &md, (const char*)x + (size_t)t0 * d * es, wr, bias, w,
+                         (char*)y + (size_t)t0 * d * es, saved ? &sm : nullptr, ws);
+    if (ring && have_prev) {
+      F.prev = Merge{prev.T, prev.d, prev.k, prev.R, prev.yp, prev.gate, prev.inv, prev.y};
+      F.prev_nC = prev.nC;
+      F.prev_abort = prev.s.abort;
+    }
+    rc = forward_run(pm, &md, F, st, ring);
     if (rc != MOE_OK) return rc;
+    prev = F;
+    prev_f32 = pm.f32;
+    have_prev = pm.T > 0;
+  }
+  if (ring && have_prev) {
+    if (prev_f32)
+      hipLaunchKernelGGL(k_combine<float>, dim3(prev.nC), dim3(256), 0, st, prev);
+    else
+      hipLaunchKernelGGL(k_combine<bf16_t>, dim3(prev.nC), dim3(256), 0, st, prev);
+    return launch_status();
   }
   return MOE_OK;
 }
@@ -1256,19 +1313,25 @@ int moe_forward_noalloc(const moe_desc* desc, const void* x, const void* wr, con
   if (rc != MOE_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   // tokens per call: all of them when their workspace fits (and the caller
-  // asked for no macrobatches), else the most that fit, at most macro_tokens
+  // asked for no macrobatches), else macrobatches of the most tokens whose
+  // two ring slots fit, at most macro_tokens
   const int T = desc->T;
-  int Tm = p.macro ? p.T : T;
-  if (forward_bytes(desc, Tm) > MOE_NOALLOC_SCRATCH_BYTES || forward_bytes(desc, Tm) == 0) {
-    int lo = 0, hi = Tm;  // largest fitting count in (lo, hi)
+  const size_t all = forward_bytes(desc, T);
+  int Tm = T;
+  if (p.macro || all == 0 || all > MOE_NOALLOC_SCRATCH_BYTES) {
+    const int cap = p.macro ? p.T : T;
+    auto fits = [&](int n) {
+      const size_t b = forward_bytes(desc, n);
+      return b != 0 && 2 * ring_slot_bytes(desc, n) <= MOE_NOALLOC_SCRATCH_BYTES;
+    };
+    int lo = 0, hi = cap + 1;  // largest fitting count in [lo, hi)
     while (hi - lo > 1) {
       const int mid = lo + (hi - lo) / 2;
-      const size_t b = forward_bytes(desc, mid);
-      if (b != 0 && b <= MOE_NOALLOC_SCRATCH_BYTES) lo = mid; else hi = mid;
+      if (fits(mid)) lo = mid; else hi = mid;
     }
     Tm = lo;
+    if (T > 0 && Tm < 1) return MOE_ERR_WORKSPACE;  // not one token's ring fits
   }
-  if (T > 0 && Tm < 1) return MOE_ERR_WORKSPACE;  // not one token's workspace fits
   if (Tm >= T) {
     moe_desc md = *desc;
     md.macro_tokens = 0;

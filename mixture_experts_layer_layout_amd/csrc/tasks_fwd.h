@@ -65,6 +65,16 @@ struct Sync {
   uint32_t flags;  // moe_desc.flags (the test-only MOE_FLAG_TEST_* bits)
 };
 
+// The operands of one weighted merge: T tokens of k slots, rows of d
+// elements.
+struct Merge {
+  int T, d, k, R;
+  const void* yp;     // [R, d] expert outputs in expert order
+  const float* gate;  // [T, k]
+  const int* inv;     // [R]
+  void* y;            // [T, d]
+};
+
 struct Fwd {
   int T, d, E, k, I, R, nb, S, BM, nN1, nN2, nC, max_tiles;
   int score, renorm, direct;
@@ -119,6 +129,13 @@ struct Fwd {
   // scale rows of the up / down projection read 16 bytes every 4 stages
   // (K % 512 == 0 and 16-byte aligned scale arrays)
   int mx_wide1, mx_wide2;
+  // Macrobatches through a ring of two workspace slots: the merge of the
+  // previous macrobatch (its expert outputs in the other slot, complete
+  // when this launch starts) runs as extra tasks of this launch's first
+  // phase, beside this macrobatch's routing.  prev.T = 0: none.
+  Merge prev;
+  int prev_nC;             // its combine tasks
+  const int* prev_abort;   // its call's abort word (set: nothing to merge)
   Sync s;
 };
 
@@ -683,11 +700,13 @@ __device__ void g2_tile_f32(const Fwd& F, int tile, int nt, float* smem) {
 }
 
 // ---------------------------------------------------------------- combine
+__device__ __forceinline__ Merge merge_of(const Fwd& F) { return Merge{F.T, F.d, F.k, F.R, F.yp, F.gate, F.inv, F.y}; }
+
 // y[t] = sum_j gate[t,j] * yp[inv[t*k+j]], fp32 accumulation in slot order.
 // K = k when known at compile time (every row load of a vector is issued
 // before the first one is used), 0 for any k up to kMaxK.
 template <class Act, int K>
-__device__ void combine_tokens_k(const Fwd& F, int cb) {
+__device__ void combine_tokens_k(const Merge& F, int cb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int EPV = 16 / sizeof(Act);  // elements per 16-byte vector
   constexpr int NR = K ? K : kMaxK;
@@ -765,7 +784,7 @@ __device__ void combine_tokens_k(const Fwd& F, int cb) {
 }
 
 template <class Act>
-__device__ void combine_tokens(const Fwd& F, int cb) {
+__device__ void combine_tokens(const Merge& F, int cb) {
   switch (F.k) {
     case 1: combine_tokens_k<Act, 1>(F, cb); break;
     case 2: combine_tokens_k<Act, 2>(F, cb); break;

@@ -138,7 +138,7 @@ def test_macrobatches_bound_the_workspace_and_other_calls_refuse_them(lib):
     full, part = ctypes.c_size_t(0), ctypes.c_size_t(0)
     assert lib.moe_workspace_size(ctypes.byref(_desc(T=65536)), ctypes.byref(full)) == 0
     assert lib.moe_workspace_size(ctypes.byref(_desc(T=65536, macro_tokens=4096)), ctypes.byref(part)) == 0
-    assert part.value * 8 < full.value * 1.01  # about a sixteenth, plus the per-expert parts
+    assert part.value * 4 < full.value * 1.01  # two ring slots of about a sixteenth, plus per-expert parts
     assert lib.moe_workspace_size(ctypes.byref(_desc(macro_tokens=-1)), ctypes.byref(part)) == -1
     vp = ctypes.c_void_p
     lib.moe_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
