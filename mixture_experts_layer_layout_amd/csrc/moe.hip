@@ -382,7 +382,10 @@ constexpr unsigned kProducerPhases = 0x4Fu, kConsumerPhases = 0x30u;
 // search (eight dependent global loads per task otherwise).
 constexpr int kEtileLds = kMaxE + 1;
 
-template <class Act, class TL, unsigned MASK>
+// RING: a launch of the macrobatch ring, whose first phase also runs the
+// previous macrobatch's merge (instantiated apart: the merge's registers
+// would otherwise weigh on every other launch's routing phase).
+template <class Act, class TL, unsigned MASK, bool RING = false>
 __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) {
   extern __shared__ __align__(16) char smem[];
   __shared__ Claim c;
@@ -405,7 +408,7 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         groups = 0;
         if (!((MASK >> ph) & 1u)) return true;  // phase run by another launch
         if (!((roles >> ph) & 1u)) return true;  // phase of the other side of the partition
-        if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0) + F.prev_nC; return true; }
+        if (ph == 0) { groups = F.nb * F.S + (TL::kMX ? F.nb : 0) + (RING ? F.prev_nC : 0); return true; }
         if (ph == 1) { groups = F.nb * kTopkChunks; return true; }
         if (ph == 2) { groups = 1; return true; }
         if (c.nmt < 0) {
@@ -436,9 +439,10 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
     // no counter (protocol.h).
     if ((MASK & 1u) && ph == 0) {
       const int nr = F.nb * F.S + (TL::kMX ? F.nb : 0);
-      if (t >= nr) {
+      if (RING && t >= nr) {
         // the previous macrobatch's merge (its operands are complete)
-        if (!load_relaxed(F.prev_abort)) combine_tokens<Act>(F.prev, t - nr);
+        if constexpr (RING)
+          if (!load_relaxed(F.prev_abort)) combine_tokens<Act>(F.prev, t - nr);
       } else if (TL::kMX && t >= F.nb * F.S) {
         quant_tokens(F, t - F.nb * F.S);
         signal_add<(MASK & 0x18u) != 0>(F.s.q_done, 1);  // read by gather, g1
@@ -768,11 +772,11 @@ static int launch_status() {
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-template <class Act, class TL, unsigned MASK>
+template <class Act, class TL, unsigned MASK, bool RING = false>
 static int launch_fused_fwd(const moe_desc* D, const Fwd& F0, size_t smem, hipStream_t st) {
-  if (!set_smem(k_fused_fwd<Act, TL, MASK>, smem)) return MOE_ERR_HIP;
-  const int resident = persistent_grid(k_fused_fwd<Act, TL, MASK>, smem, 0);
-  const int n_wg = persistent_grid(k_fused_fwd<Act, TL, MASK>, smem, D->n_workgroups);
+  if (!set_smem(k_fused_fwd<Act, TL, MASK, RING>, smem)) return MOE_ERR_HIP;
+  const int resident = persistent_grid(k_fused_fwd<Act, TL, MASK, RING>, smem, 0);
+  const int n_wg = persistent_grid(k_fused_fwd<Act, TL, MASK, RING>, smem, D->n_workgroups);
   if (n_wg <= 0 || resident <= 0) return MOE_ERR_HIP;
   Fwd F = F0;
   F.n_prod = 0;
@@ -784,7 +788,7 @@ static int launch_fused_fwd(const moe_desc* D, const Fwd& F0, size_t smem, hipSt
     F.n_prod = D->n_producer_cus * per_cu;
     if (F.n_prod >= n_wg) return MOE_ERR_INVALID_ARG;  // no consumer left
   }
-  hipLaunchKernelGGL((k_fused_fwd<Act, TL, MASK>), dim3(n_wg), dim3(256), smem, st, F);
+  hipLaunchKernelGGL((k_fused_fwd<Act, TL, MASK, RING>), dim3(n_wg), dim3(256), smem, st, F);
   return launch_status();
 }
 
@@ -815,7 +819,8 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   }
   if (D->fused) {
     if (ring) {
-      int rc = TL::kMX ? launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st) : launch_fused_fwd<Act, TL, 0x3Fu>(D, F, smem, st);
+      int rc = TL::kMX ? launch_fused_fwd<Act, TL, 0x1Fu, true>(D, F, smem, st)
+                       : launch_fused_fwd<Act, TL, 0x3Fu, true>(D, F, smem, st);
       if (rc == MOE_OK && TL::kMX) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
       return rc;
     }
