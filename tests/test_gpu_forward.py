@@ -133,17 +133,21 @@ MACRO = {
 }
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", sorted(MACRO))
-def test_macrobatched_forward_equals_one_call(name):
-    """moe_forward in macrobatches (the last one ragged) writes the same bits
-    as one call over all tokens, from a workspace sized for a macrobatch."""
+def test_macrobatched_forward_equals_one_call(name, fused):
+    """moe_forward in macrobatches (the last one ragged) through the ring of
+    two workspace slots writes the same bits as one call over all tokens,
+    from a workspace sized for two macrobatches; fused: each macrobatch's
+    merge runs in the next one's launch, else the plain kernels in stream
+    order."""
     import dataclasses
     w, tm = MACRO[name]
     wm = dataclasses.replace(w, macro_tokens=tm)
     inp = synth.make_inputs(w, 5)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     y0, s0 = layer.forward(w, dev)
-    y1, s1 = layer.forward(wm, dev)
+    y1, s1 = layer.forward(wm, dev, fused=fused)
     torch.cuda.synchronize()
     assert s0["status"].item() == 0 and s1["status"].item() == 0
     assert "perm" not in s1

@@ -281,9 +281,11 @@ def test_fullsize_router_backward():
     assert e3 <= 1e-2 and e4 <= 1e-2
 
 
-def test_fullsize_mxfp8_backward():
+@pytest.mark.parametrize("mx_wgrad", [False, True])
+def test_fullsize_mxfp8_backward(mx_wgrad):
     """dsv3-fwdbwd-zipf-mxfp8 at full size (MXFP8 forward, MXFP8 data
-    gradients, bf16 weight gradients), as bench.py runs it: routing exact;
+    gradients, bf16 weight gradients -- or MXFP8 ones with
+    MOE_FLAG_MXFP8_WGRAD), as bench.py runs it: routing exact;
     dX and dgate of 16 tokens (tile-edge tokens of the heaviest expert
     included) against the oracle's MXFP8 forward and backward over those
     tokens alone (their rows depend on nothing else); dW1, dW3 and dW2 of a
@@ -296,7 +298,7 @@ def test_fullsize_mxfp8_backward():
     print(f"\nfull-size {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} I={w.I}", flush=True)
     inp, dev = full_inputs(w, 0)
     y, sv = layer.forward(w, dev, fused=True)
-    g = layer.backward(w, dev, sv, fused=True)
+    g = layer.backward(w, dev, sv, fused=True, flags=api.MOE_FLAG_MXFP8_WGRAD if mx_wgrad else 0)
     torch.cuda.synchronize()
     assert sv["status"].item() == 0
     x = host(inp["x"])
@@ -316,7 +318,7 @@ def test_fullsize_mxfp8_backward():
     try:
         f = Q.forward_mxfp8(x[ts], wr, bias, W1, W3, W2, w.k, w.score, w.renorm, logits=logits[ts],
                             expert_map=emap)
-        b = Q.backward_mxfp8(dy[ts], x[ts], f, W1, W3, W2, w.k, expert_map=emap, mx_wgrad=False)
+        b = Q.backward_mxfp8(dy[ts], x[ts], f, W1, W3, W2, w.k, expert_map=emap, mx_wgrad=mx_wgrad)
         for n in ("dx", "dgate"):
             e2 = (dgate_err if n == "dgate" else row_rel_err)(host(g[n])[ts], b[n])
             print(f"  {n} on {len(ts)} tokens max row-rel err {e2:.2e}", flush=True)
@@ -327,7 +329,7 @@ def test_fullsize_mxfp8_backward():
         g_row = gate.reshape(-1)[perm][lo:hi]
         A, B, H, _ = Q.expert_ffn_mxfp8(Q.quantize_tokens(x[rows]), W1[e], W3[e], W2[e])
         A, B, H = Q.round_bf16(A), Q.round_bf16(B), Q.round_bf16(H)
-        eb = Q.expert_backward_mxfp8(x[rows], dy[rows], g_row, A, B, H, W1[e], W3[e], W2[e], mx_wgrad=False,
+        eb = Q.expert_backward_mxfp8(x[rows], dy[rows], g_row, A, B, H, W1[e], W3[e], W2[e], mx_wgrad=mx_wgrad,
                                      saved_bf16=True)
     finally:
         pool.terminate()
