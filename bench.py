@@ -2,7 +2,7 @@
 """Throughput of one GPU's share of the fused MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--unfused] [--no-cpu-baseline]
+                    [--unfused] [--no-cpu-baseline] [--no-ablation]
     python bench.py --copy-calibration      # a plain copy of known size, for
                                             # scaling HBM byte counters
 
@@ -29,9 +29,12 @@ The line carries
                 routing and layout over all tokens), scaled to tokens/s
   phases        forward / backward times, the step timed again with a
                 512 MB buffer written between steps (so no input of a step
-                sits in the caches; ``step_ms_flushed``), the standalone
-                layout and gathers, and for MXFP8 experts the weight
-                quantisation a weight update costs (outside the step)
+                sits in the caches; ``step_ms_flushed``), the same step
+                through the separate kernels (``unfused_step_ms``,
+                ``fused_speedup``: the ablation of the persistent path), the
+                standalone layout, gathers and merge, and for MXFP8 experts
+                the weight quantisation a weight update costs (outside the
+                step)
 """
 from __future__ import annotations
 
@@ -192,6 +195,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--unfused", action="store_true", help="one launch per step instead of the persistent kernel")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip timing the same step through the separate kernels")
     ap.add_argument("--stage-rows", type=int, default=0)
     ap.add_argument("--flags", type=lambda v: int(v, 0), default=0, help="moe_desc.flags (MOE_FLAG_*)")
     ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: occupancy limit)")
@@ -311,6 +316,30 @@ def main():
         torch.cuda.synchronize()
         fl_ms.append(a.elapsed_time(b))
     del flush
+    # ablation: the same step through the separate kernels (fused = 0: one
+    # ordinary grid per phase, the stream ordering them), on the same
+    # buffers, timed with events around a few steps
+    unfused_ms = None
+    if fused and not args.no_ablation:
+        udesc = layer.desc_for(w, fused=False, stage_rows=args.stage_rows, flags=args.flags)
+        ubdesc = layer.desc_for(w, fused=False, flags=args.flags) if w.backward else None
+
+        def ustep():
+            api.moe_forward(udesc, dev["x"], dev["wr"], dev["bias"], weights, y, sv, ws, stream)
+            if w.backward:
+                api.moe_backward(ubdesc, dev["dy"], dev["x"], bweights, sv, grads["dx"], grads["dw1"],
+                                 grads["dw3"], grads["dw2"], grads["dgate"], bws, stream)
+        ustep()
+        a, b = ev(), ev()
+        n_u = min(args.steps, 5)
+        a.record(stream)
+        for _ in range(n_u):
+            ustep()
+        b.record(stream)
+        torch.cuda.synchronize()
+        unfused_ms = a.elapsed_time(b) / n_u
+        if saved["status"].item() != 0:
+            raise RuntimeError("device status " + api.moe_status_string(saved["status"].item()))
     # MXFP8 experts: the weight quantisation one weight update costs (the
     # forward's three weights along their contraction axes, and for a
     # backward the three transposed ones), timed on the same stream
@@ -414,6 +443,9 @@ def main():
                                         / HBM_PEAK_GBS, 4),
               "workspace_mb": round(ws.numel() / 1e6, 1)}
     phases["step_ms_flushed"] = round(sum(fl_ms) / len(fl_ms), 4)
+    if unfused_ms is not None:
+        phases["unfused_step_ms"] = round(unfused_ms, 4)
+        phases["fused_speedup"] = round(unfused_ms / ms_step, 3)
     if quant_ms is not None:
         phases["weight_quant_ms_per_update"] = round(quant_ms, 4)
         phases["tokens_s_with_quant_every_step"] = round(w.T / ((ms_step + quant_ms) * 1e-3), 1)
