@@ -34,23 +34,25 @@
 
 namespace moe {
 
-// The XOR key of tile row `row`.  The LDS serves 256 bytes (64 banks) per
-// cycle, i.e. one 16-byte access for each of 16 lanes, or one 8-byte access
-// for each of 32.  (row >> 1) & 7 places the same chunk of 16 consecutive
-// rows (two rows per 256 bytes) in 16 different slots, and the 8 chunks of
-// one row in 8 different slots: the fragment reads (16 aligned consecutive
-// rows, one chunk) and the row-wise stores need no more.  HI adds the term
-// (row >> 4) << 1, constant over 16 aligned rows, for the K-major loader's
-// 8-byte stores: a 32-lane group writes one row of each of 8 column blocks
-// (rows 8 apart) for 4 k-groups, and without the term column blocks of
-// equal parity share slots.  Measured on the backward's register-staged
-// tiles it takes 15-26% of the LDS instruction cycles off (the K-major
-// tiles run 4-6% faster); on the direct-to-LDS forward tile it raised the
-// bank-conflict count by two orders of magnitude and cost 1.5%, so that tile keeps the
-// plain key (Tile::kKeyHi / TileD::kKeyHi).
+// The XOR key of tile row `row`: chunk c of the row is stored at slot
+// c ^ key.  (row >> 1) & 7 places the same chunk of 16 aligned consecutive
+// rows in distinct slot pairs and the 8 chunks of one row in 8 slots, which
+// the fragment reads (32 consecutive rows, one chunk) and the row-wise
+// 16-byte stores need; the K-major loader's 8-byte stores (a lane group
+// writes rows 8 apart, one per column block) also need column blocks of
+// equal parity apart.  HI XORs in row >> 4 for that.  Measured per access
+// pattern with single-pattern probe kernels (SQ_LDS_BANK_CONFLICT over
+// SQ_LDS_IDX_ACTIVE): with HI the fragment reads, the row stores and the
+// K-major stores (4 or 8 k-rows a thread) all run without conflicts, 4 LDS
+// cycles per fragment read and per 8-byte store instruction.  The plain key
+// has the K-major stores at 16 cycles (75% conflict cycles); the earlier
+// term (row >> 4) << 1 had both the fragment reads and those stores at 8.
+// The direct-to-LDS forward tile keeps the plain key (TileD::kKeyHi): its
+// fragment reads and DMA writes are conflict-free with it and it has no
+// K-major stores.
 template <bool HI>
 __device__ __forceinline__ int lds_key(int row) {
-  return HI ? ((row >> 1) ^ ((row >> 4) << 1)) & 7 : (row >> 1) & 7;
+  return HI ? ((row >> 1) ^ (row >> 4)) & 7 : (row >> 1) & 7;
 }
 
 // Element index of 16-byte chunk `chunk` of tile row `row` in an LDS stage.
