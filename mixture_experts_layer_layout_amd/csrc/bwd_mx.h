@@ -256,6 +256,117 @@ __device__ __forceinline__ void expert_slots(const Bwd& B, int e, int& t0, int& 
   t1 = min(max(B.etile[e + 1], t0), B.max_tiles);
 }
 
+// The band of an expert with one row-tile slot (at most 128 rows: one
+// 128-deep stage per output tile), the MXFP8 form of tile_band with one
+// stage: A's codes and scale words are loaded into LDS once, and B's stage
+// of each of the nc column tiles (codes and scale words; column tile c is
+// B rows c * BN further) streams two ahead in registers, so the next
+// tiles' loads overlap this tile's MFMAs and stores instead of every tile
+// restarting the pipeline.  The B scale words sit with their B stage.
+// LDS (bf16 units): A codes | A scale words | B0 codes | B0 words | B1 codes
+// | B1 words.  epi(c, acc) writes column tile c.
+struct MxBandLds {
+  static constexpr int BM = TileMX128::BM, BN = TileMX128::BN;
+  static constexpr int A_SC = BM * 64, B0 = BM * 66, BSTAGE = BN * 66;
+  static constexpr size_t bytes = (size_t)(B0 + 2 * BSTAGE) * sizeof(bf16_t);
+  static_assert((B0 * sizeof(bf16_t)) % 16 == 0 && (BSTAGE * sizeof(bf16_t)) % 16 == 0, "16-byte aligned stages");
+};
+
+// B's stage of a column tile: codes of rows r0 + 32 i (16 bytes a lane) and
+// the scale word of row t (t < BN), for two register buffers.
+struct MxBandB {
+  const uint8_t* c[4];
+  const uint8_t* s;
+  size_t cstep_c, cstep_s;  // bytes from one column tile's rows to the next
+  uint4 v[2][4];
+  uint32_t w[2];
+  template <int BUF>
+  __device__ __forceinline__ void load(int ct) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[BUF][i] = *(const uint4*)(c[i] + (size_t)ct * cstep_c);
+    w[BUF] = threadIdx.x < MxBandLds::BN ? *(const uint32_t*)(s + (size_t)ct * cstep_s) : 0u;
+  }
+  template <int BUF>
+  __device__ __forceinline__ void store(bf16_t* lds) const {
+    const int r0 = threadIdx.x >> 3, ch = threadIdx.x & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(uint4*)(lds + lds_idx<false>(r0 + 32 * i, ch)) = v[BUF][i];
+    if (threadIdx.x < MxBandLds::BN) ((uint32_t*)(lds + MxBandLds::BN * 64))[threadIdx.x] = w[BUF];
+  }
+};
+
+// Step j of the band: the loads of column tile j + 2 into register buffer
+// CUR (= j % 2), the MFMAs of tile j from LDS buffer CUR, tile j + 1
+// (register buffer CUR ^ 1) into the other LDS buffer, then tile j's stores.
+template <int CUR, class EPI>
+__device__ __forceinline__ void band_step_mx(int j, int last, const bf16_t* As, bf16_t* smem, MxBandB& Bl,
+                                             f32x16_t (&acc)[TileMX128::MI][TileMX128::NJ], EPI& epi) {
+  typedef TileMX128 TL;
+  typedef MxBandLds L;
+  bf16_t* cur = smem + L::B0 + CUR * L::BSTAGE;
+  bf16_t* nxt = smem + L::B0 + (CUR ^ 1) * L::BSTAGE;
+  Bl.template load<CUR>(min(j + 2, last));
+  __builtin_amdgcn_sched_barrier(0);
+  tile_compute_mx<TL>(As, cur, (const uint32_t*)(smem + L::A_SC), (const uint32_t*)(cur + L::BN * 64), acc);
+  __builtin_amdgcn_sched_barrier(0);
+  Bl.template store<CUR ^ 1>(nxt);
+  epi(j, acc);
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TL::NJ; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+  __syncthreads();
+}
+
+template <class AR, class BR, class EPI>
+__device__ __forceinline__ void wgrad_band_mx1(const Bwd& B, int t0, int nc, AR arow, BR brow0,
+                                               const uint8_t* acodes, const uint8_t* ascales,
+                                               const uint8_t* bcodes, const uint8_t* bscales, bf16_t* smem,
+                                               EPI& epi) {
+  typedef TileMX128 TL;
+  typedef MxBandLds L;
+  static_assert(L::bytes <= TL::smem_bytes, "the band fits the tile's LDS (the store staging follows it)");
+  const size_t kc = (size_t)B.kcap, ks = kc / 32;
+  const size_t k0 = (size_t)t0 * B.BM, s0 = (size_t)t0 * (B.BM / 32);
+  const int t = threadIdx.x, r0 = t >> 3, ch = t & 7;
+  f32x16_t acc[TL::MI][TL::NJ];
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (nc <= 0) return;
+  const int last = nc - 1;
+  // B rows of column tile 0; column tile c is c * BN rows further
+  MxBandB Bl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Bl.c[i] = bcodes + (size_t)brow0(r0 + 32 * i) * kc + k0 + ch * 16;
+  Bl.s = bscales + (size_t)brow0(t < L::BN ? t : 0) * ks + s0;
+  Bl.cstep_c = (size_t)L::BN * kc;
+  Bl.cstep_s = (size_t)L::BN * ks;
+  Bl.load<0>(0);
+  Bl.load<1>(min(1, last));
+  // the LDS may still be read by the previous user
+  __syncthreads();
+  // A: codes of rows r0 + 32 i and the scale word of row t (t < BM), once
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *(uint4*)(smem + lds_idx<false>(r0 + 32 * i, ch)) =
+        *(const uint4*)(acodes + (size_t)arow(r0 + 32 * i) * kc + k0 + ch * 16);
+  if (t < L::BM) ((uint32_t*)(smem + L::A_SC))[t] = *(const uint32_t*)(ascales + (size_t)arow(t) * ks + s0);
+  Bl.store<0>(smem + L::B0);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < nc; j += 2) {
+    band_step_mx<0>(j, last, smem, smem, Bl, acc, epi);
+    band_step_mx<1>(j + 1, last, smem, smem, Bl, acc, epi);
+  }
+  if (j < nc) band_step_mx<0>(j, last, smem, smem, Bl, acc, epi);
+}
+
 // dW2_e in MXFP8 for one band (the bf16 band's task split): output rows n0
 // .. +128 of d over kWgradPerTicket column tiles of I, each a full pass
 // over the expert's slots (an expert without rows has none: zeros).
@@ -270,6 +381,15 @@ __device__ void bwd_dw2_band_mx(const Bwd& B, int rank, int task, bf16_t* smem) 
   expert_slots(B, e, t0, t1);
   bf16_t* out = B.dw2 + (size_t)e * d * I + (size_t)n0 * I;
   bf16_t* stage = smem + TL::smem_bytes / sizeof(bf16_t);
+  if (t1 - t0 == 1) {
+    auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
+      tile_store_staged<TL>(acc, [&](int wm) { return out + (size_t)(wm * TL::WM) * I + (cb + c) * TL::BN; }, I,
+                            stage);
+    };
+    wgrad_band_mx1(B, t0, nc, [&](int r) { return n0 + r; }, [&](int n) { return cb * TL::BN + n; }, B.gT, B.gTs,
+                   B.hT, B.hTs, smem, epi);
+    return;
+  }
   for (int c = 0; c < nc; ++c) {
     const int c0 = (cb + c) * TL::BN;
     f32x16_t acc[TL::MI][TL::NJ];
@@ -295,11 +415,19 @@ __device__ void bwd_dw13_band_mx(const Bwd& B, int rank, int task, bf16_t* smem)
   bf16_t* o3 = B.dw3 + (size_t)e * I * d + (size_t)i0 * d;
   bf16_t* stage = smem + TL::smem_bytes / sizeof(bf16_t);
   static_assert(TL::WM == TL::BM / 2, "one wave row block per gradient");
+  auto arow = [&](int r) { return r < TL::BM / 2 ? i0 + r : I + i0 + r - TL::BM / 2; };
+  if (t1 - t0 == 1) {
+    auto epi = [&](int c, const f32x16_t (&acc)[TL::MI][TL::NJ]) {
+      tile_store_staged<TL>(acc, [&](int wm) { return (wm ? o3 : o1) + (cb + c) * TL::BN; }, d, stage);
+    };
+    wgrad_band_mx1(B, t0, nc, arow, [&](int n) { return cb * TL::BN + n; }, B.dabT, B.dabTs, B.xT, B.xTs, smem,
+                   epi);
+    return;
+  }
   for (int c = 0; c < nc; ++c) {
     const int c0 = (cb + c) * TL::BN;
     f32x16_t acc[TL::MI][TL::NJ];
-    wgrad_tile_mx(B, t0, t1, [&](int r) { return r < TL::BM / 2 ? i0 + r : I + i0 + r - TL::BM / 2; },
-                  [&](int n) { return c0 + n; }, B.dabT, B.dabTs, B.xT, B.xTs, smem, acc);
+    wgrad_tile_mx(B, t0, t1, arow, [&](int n) { return c0 + n; }, B.dabT, B.dabTs, B.xT, B.xTs, smem, acc);
     tile_store_staged<TL>(acc, [&](int wm) { return (wm ? o3 : o1) + c0; }, d, stage);
   }
 }

@@ -105,14 +105,13 @@ __device__ __forceinline__ f32x16_t mfma_mx(i32x8_t a, uint32_t sa, i32x8_t b, u
 // The 128-deep stage as 2 slices of 64: the fragments of both slices are
 // read first (two 16-byte LDS reads per fragment and slice), then the MFMAs
 // of slice 0 and of slice 1.
+// sa, sb: the stage's scale words of the A rows and of the B rows.
 template <class TL>
-__device__ __forceinline__ void tile_compute_mx(const bf16_t* As, const bf16_t* Bs,
-                                                f32x16_t (&acc)[TL::MI][TL::NJ]) {
+__device__ __forceinline__ void tile_compute_mx(const bf16_t* As, const bf16_t* Bs, const uint32_t* sa,
+                                                const uint32_t* sb, f32x16_t (&acc)[TL::MI][TL::NJ]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, rr = lane & 31;
-  const uint32_t* sa = (const uint32_t*)(As + TL::BM * 64);
-  const uint32_t* sb = sa + TL::BM;
   auto frag = [&](const bf16_t* base, int row, int s) -> i32x8_t {
     const uint4 lo = *(const uint4*)(base + lds_idx<TL::kKeyHi>(row, 4 * s + h));
     const uint4 hi = *(const uint4*)(base + lds_idx<TL::kKeyHi>(row, 4 * s + 2 + h));
@@ -145,7 +144,8 @@ __device__ __forceinline__ void tile_compute_mx(const bf16_t* As, const bf16_t* 
 template <int BM_, int BN_>
 __device__ __forceinline__ void TileMX<BM_, BN_>::stage(const bf16_t* As, const bf16_t* Bs,
                                                        f32x16_t (&acc)[MI][NJ]) {
-  tile_compute_mx<TileMX<BM_, BN_>>(As, Bs, acc);
+  const uint32_t* sa = (const uint32_t*)(As + BM * 64);
+  tile_compute_mx<TileMX<BM_, BN_>>(As, Bs, sa, sa + BM, acc);
 }
 
 // ---------------------------------------------------------------- codec
