@@ -89,7 +89,11 @@ typedef struct moe_desc {
   int32_t stage_rows;    /* rows per ready counter (the minibatch handed to
                             the expert GEMM): 0 = auto (128), else 64, 128
                             or 256 (MXFP8 experts: 0 or 128)               */
-  int32_t n_workgroups;  /* persistent grid size, 0 = auto (all CUs)       */
+  int32_t n_workgroups;  /* persistent grid size; 0 = auto: as many as
+                          * fit on the CUs at once, but no more than the
+                          * most tasks any phase of the launch can have
+                          * (and at least 8); any size gives the same
+                          * results                                        */
   uint32_t flags;        /* MOE_FLAG_* below                                */
   /* DeepSeek-V3-style routing options (0 = off):
    * n_group, topk_group: group-limited selection.  The E experts form
