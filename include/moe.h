@@ -279,8 +279,8 @@ MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K,
  *   src    bf16  [batch, rows, cols]
  *   codes  uint8 [batch, cols, rows]      E4M3 codes of src^T
  *   scales uint8 [batch, cols, rows/32]   E8M0 codes, blocks of 32 along rows
- * rows % 32 == 0 (else MOE_ERR_INVALID_ARG); batch <= 65535, rows/32 <=
- * 65535 and cols <= 2^30 (else MOE_ERR_UNSUPPORTED).  The same encoding as
+ * rows % 32 == 0 (else MOE_ERR_INVALID_ARG); batch <= 65535, rows <=
+ * 128 * 65535 and cols <= 2^30 (else MOE_ERR_UNSUPPORTED).  The same encoding as
  * moe_quantize_mxfp8. */
 MOE_API int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                  uint8_t* codes, uint8_t* scales, void* stream);

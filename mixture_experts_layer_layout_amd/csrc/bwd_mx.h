@@ -434,26 +434,55 @@ __device__ void bwd_dw13_band_mx(const Bwd& B, int rank, int task, bf16_t* smem)
 
 // Quantisation of the transpose of each [rows, cols] bf16 matrix of a
 // batch along its rows: codes [cols, rows] and scales [cols, rows / 32]
-// per matrix.  Thread c of a workgroup takes column c of a 32-row block:
-// the 32 loads of a step read 512 consecutive bytes across the workgroup's
-// 256 threads, and each thread writes its 32 codes as two 16-byte stores
-// and one scale byte.
+// per matrix (moe_quantize_mxfp8_t).  A workgroup takes a block of 128 rows
+// x 128 columns of one matrix, loads it row by row into LDS (16 bytes a
+// lane when VEC: the columns a multiple of 8, the source 16-byte aligned;
+// else 2 bytes a lane), and thread t quantises column t % 128 over rows
+// 64 (t / 128) .. +63 of the block (two 32-row blocks) from the LDS copy,
+// writing 64 consecutive code bytes of that column and two scale bytes.
+// Measured on a [256, 2048, 7168] matrix: 3.06 ms, against 3.77 ms when
+// each thread read its column's 32 rows straight from memory (2 bytes a
+// lane, 128 bytes a wave load) and wrote 32-byte pieces.
+template <bool VEC>
 __global__ void __launch_bounds__(256) k_mx_quant_t(const bf16_t* __restrict__ src, uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, int rows, int cols) {
-  const int c = blockIdx.x * kThreads + threadIdx.x;
-  const int rb = blockIdx.y;
-  if (c >= cols) return;
+                                                     uint8_t* __restrict__ scales, int rows, int cols) {
+  __shared__ __align__(16) bf16_t blk[128 * 128];
+  const int c0 = blockIdx.x * 128, r0 = blockIdx.y * 128;
   const size_t mat = (size_t)blockIdx.z * rows * cols;
-  const bf16_t* s = src + mat + (size_t)(32 * rb) * cols + c;
-  float v[32];
+  const int t = threadIdx.x;
+  {
+    const int ch = t & 15, rr = t >> 4;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) v[j] = bf16_to_f32(s[(size_t)j * cols]);
-  uint32_t w[8];
-  const uint32_t sc = mx_quant32(v, w);
-  uint4* dst = (uint4*)(codes + mat + (size_t)c * rows + 32 * rb);
-  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  scales[(size_t)blockIdx.z * cols * (rows / 32) + (size_t)c * (rows / 32) + rb] = (uint8_t)sc;
+    for (int i = 0; i < 8; ++i) {
+      const int r = rr + 16 * i, c = c0 + 8 * ch;
+      if (r0 + r >= rows || c >= cols) continue;
+      const bf16_t* row = src + mat + (size_t)(r0 + r) * cols;
+      if (VEC) {
+        *(uint4*)(blk + r * 128 + 8 * ch) = *(const uint4*)(row + c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c + e < cols) blk[r * 128 + 8 * ch + e] = row[c + e];
+      }
+    }
+  }
+  __syncthreads();
+  const int cc = t & 127, h = t >> 7, c = c0 + cc;
+  if (c >= cols) return;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int rb = 2 * h + b;  // 32-row block of the workgroup's block
+    if (r0 + 32 * rb >= rows) break;
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = bf16_to_f32(blk[(32 * rb + j) * 128 + cc]);
+    uint32_t w[8];
+    const uint32_t sc = mx_quant32(v, w);
+    uint4* dst = (uint4*)(codes + mat + (size_t)c * rows + r0 + 32 * rb);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[(size_t)blockIdx.z * cols * (rows / 32) + (size_t)c * (rows / 32) + r0 / 32 + rb] = (uint8_t)sc;
+  }
 }
 
 }  // namespace moe

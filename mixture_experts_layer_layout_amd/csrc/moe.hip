@@ -1196,12 +1196,16 @@ int moe_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* codes,
 int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
                          uint8_t* scales, void* stream) {
   if (batch < 0 || rows <= 0 || cols <= 0 || rows % 32) return MOE_ERR_INVALID_ARG;
-  if (batch > 65535 || rows / 32 > 65535 || cols > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if (batch > 65535 || cdiv64(rows, 128) > 65535 || cols > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
   if (batch == 0) return MOE_OK;
   if (!src || !codes || !scales) return MOE_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(k_mx_quant_t, dim3((unsigned)cdiv((int)cols, kThreads), (unsigned)(rows / 32), (unsigned)batch),
-                     dim3(kThreads), 0, (hipStream_t)stream, (const bf16_t*)src, codes, scales, (int)rows,
-                     (int)cols);
+  const dim3 grid((unsigned)cdiv((int)cols, 128), (unsigned)cdiv((int)rows, 128), (unsigned)batch);
+  if (cols % 8 == 0 && ((uintptr_t)src & 15) == 0)
+    hipLaunchKernelGGL(k_mx_quant_t<true>, grid, dim3(kThreads), 0, (hipStream_t)stream, (const bf16_t*)src, codes,
+                       scales, (int)rows, (int)cols);
+  else
+    hipLaunchKernelGGL(k_mx_quant_t<false>, grid, dim3(kThreads), 0, (hipStream_t)stream, (const bf16_t*)src, codes,
+                       scales, (int)rows, (int)cols);
   return launch_status();
 }
 
