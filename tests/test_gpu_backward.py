@@ -89,6 +89,17 @@ def test_backward_any_grid_size(n_wg):
     check_against_oracle(w, inp, sv, g)
 
 
+def test_auto_grid_matches_large_grid_bitwise():
+    # the automatic grid is capped at the most tasks a phase can have; any
+    # grid size computes the same bits
+    w = SMALL["dsv3-zipf-small"]
+    a = run_fwd_bwd(w, 9, True, n_workgroups=0)
+    b = run_fwd_bwd(w, 9, True, n_workgroups=1000)
+    assert torch.equal(a[1], b[1])
+    for n in a[3]:
+        assert torch.equal(a[3][n], b[3][n]), n
+
+
 def test_backward_repeatable():
     w = SMALL["dsv3-zipf-small"]
     inp = synth.make_inputs(w, 6, with_dy=True)

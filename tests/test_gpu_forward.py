@@ -91,6 +91,18 @@ def test_fused_any_grid_size(n_wg):
     run_and_check(SMALL["dsv3-small"], 7, True, n_workgroups=n_wg)
 
 
+@pytest.mark.parametrize("name", ["tiny-fp32", "dsv3-small"])
+def test_auto_grid_matches_large_grid_bitwise(name):
+    # the automatic grid is capped at the most tasks a phase can have (a
+    # handful for the 64-token fp32 layer); any grid size gives the same bits
+    w = synth.WORKLOADS[name] if name in synth.WORKLOADS else SMALL[name]
+    inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 10).items()}
+    y1, _ = layer.forward(w, inp, fused=True, n_workgroups=0)
+    y2, _ = layer.forward(w, inp, fused=True, n_workgroups=1000)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 def test_fused_equals_unfused_bitwise():
     w = SMALL["dsv3-zipf-small"]
     inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 8).items()}
