@@ -220,30 +220,57 @@ __device__ __forceinline__ void bwd_dh_epilogue(const Bwd& B, f32x16_t (&acc)[TL
   float* sred = (float*)(smem + TL::BM * St::LD);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  // Accumulator entries r and r + 1 (r even) are rows R and R + 1 of the
+  // lane's column, and lanes 2m, 2m + 1 hold columns c, c + 1 of the same
+  // rows: the even lane loads the 4-byte word of both columns in row R,
+  // the odd lane that of row R + 1, and one lane-pair swap gives each the
+  // value of its column in the other row (half the load instructions of
+  // one 2-byte load per element, each moving twice the bytes).
+  const bool odd = lane & 1;
+  auto pair_of = [&](const bf16_t* base, size_t o, float& vr, float& vr1) {
+    const uint32_t w = *(const uint32_t*)(base + o);
+    const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+    const float own = odd ? hi : lo, got = swap_lane_pair(odd ? lo : hi);
+    vr = odd ? got : own;
+    vr1 = odd ? own : got;
+  };
 #pragma unroll
   for (int i = 0; i < TL::MI; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; r += 2) {
       const int row = wm * TL::WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const size_t gr = (size_t)(r0 + min(row, n - 1));
-      const float g = B.grow[gr];
-      float part = 0.0f;
+      const size_t gr0 = (size_t)(r0 + min(row, n - 1)), gr1 = (size_t)(r0 + min(row + 1, n - 1));
+      const float g0 = B.grow[gr0], g1 = B.grow[gr1];
+      const size_t grl = odd ? gr1 : gr0;
+      float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
       for (int j = 0; j < TL::NJ; ++j) {
         const int col = wn * TL::WN + 32 * j + (lane & 31);
-        const size_t o = gr * I + c0 + col;
-        const float du = acc[i][j][r];
-        const float av = bf16_to_f32(B.a[o]), bv = bf16_to_f32(B.b[o]), hv = bf16_to_f32(B.h[o]);
-        part = fmaf(du, hv, part);
-        const float dh = g * du;
-        const float sg = sigmoid_f(av);
-        st.put(row, col, dh * bv * sg * (1.0f + av * (1.0f - sg)));
-        acc[i][j][r] = dh * av * sg;
+        const size_t o = grl * I + c0 + (col & ~1);
+        float a0, a1, b0, b1, h0, h1;
+        pair_of(B.a, o, a0, a1);
+        pair_of(B.b, o, b0, b1);
+        pair_of(B.h, o, h0, h1);
+        const float du0 = acc[i][j][r], du1 = acc[i][j][r + 1];
+        part0 = fmaf(du0, h0, part0);
+        part1 = fmaf(du1, h1, part1);
+        const float dh0 = g0 * du0, dh1 = g1 * du1;
+        const float sg0 = sigmoid_f(a0), sg1 = sigmoid_f(a1);
+        st.put(row, col, dh0 * b0 * sg0 * (1.0f + a0 * (1.0f - sg0)));
+        st.put(row + 1, col, dh1 * b1 * sg1 * (1.0f + a1 * (1.0f - sg1)));
+        acc[i][j][r] = dh0 * a0 * sg0;
+        acc[i][j][r + 1] = dh1 * a1 * sg1;
       }
-      // sum over the 32 lanes holding this row's columns (fixed tree)
+      // sums over the 32 lanes holding these rows' columns (fixed tree)
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o);
-      if ((lane & 31) == 0) sred[wn * TL::BM + row] = part;
+      for (int o = 1; o < 32; o <<= 1) {
+        part0 += __shfl_xor(part0, o);
+        part1 += __shfl_xor(part1, o);
+      }
+      if ((lane & 31) == 0) {
+        sred[wn * TL::BM + row] = part0;
+        sred[wn * TL::BM + row + 1] = part1;
+      }
     }
   }
   const size_t I2 = 2 * (size_t)I;
