@@ -299,8 +299,9 @@ MOE_API int moe_quantize_mxfp8_t(const void* src, int64_t batch, int64_t rows, i
  * up-projection tile starting as soon as the ready counter of its rows
  * shows them staged and a down-projection tile as soon as every
  * up-projection tile of its rows has stored H (MoK flash §02: GPU-local
- * counters); the combine follows as a plain launch.  MXFP8 experts run the
- * down projection in a persistent launch of its own by default.
+ * counters); the combine follows as a plain launch.  MXFP8 experts run
+ * routing through the gather, the up projection and the down projection as
+ * three persistent launches by default.
  * MOE_FLAG_PERSISTENT_SINGLE puts the combine in the persistent launch too,
  * MOE_FLAG_PERSISTENT_GEMM_APART gives the down projection its own launch,
  * MOE_FLAG_PERSISTENT_SPLIT gives each phase group its own. */

@@ -879,10 +879,15 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
     // storing them coherently for a reader in the same launch costs more
     // than the launch boundary (measured at the DeepSeek-V3 shape, T = 8192:
     // 6.16 ms in one launch against 5.99 ms), so the down projection gets a
-    // launch of its own
+    // launch of its own; so does the up projection, whose launch then
+    // carries no routing, quantisation or gather code and spills no
+    // registers (40-48 VGPRs with them): 6.02-6.03 against 6.11-6.14 ms
     if ((D->flags & MOE_FLAG_PERSISTENT_GEMM_APART) || TL::kMX) {
-      // routing through the up projection | the down projection | combine
-      int rc = launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st);
+      // routing through the up projection (MXFP8: routing through the
+      // gather | the up projection) | the down projection | combine
+      int rc = TL::kMX ? launch_fused_fwd<Act, TL, 0x0Fu>(D, F, smem, st)
+                       : launch_fused_fwd<Act, TL, 0x1Fu>(D, F, smem, st);
+      if (rc == MOE_OK && TL::kMX) rc = launch_fused_fwd<Act, TL, 0x10u>(D, F, smem, st);
       if (rc == MOE_OK) rc = launch_fused_fwd<Act, TL, 0x20u>(D, F, smem, st);
       if (rc != MOE_OK) return rc;
       hipLaunchKernelGGL(k_combine<Act>, dim3(p.nC), dim3(256), 0, st, F);
