@@ -181,31 +181,53 @@ __device__ void router_partial<bf16_t>(const Fwd& F, int task) {
   const bf16_t* X = (const bf16_t*)F.x;
   const bf16_t* Wr = (const bf16_t*)F.wr;
   const int koff = (lane >> 5) * 8;
-  for (int it = wave; it < 2 * nEB; it += 4) {
-    const int rb = it & 1, eb = it >> 1;
-    const int row = b * kTokBlock + rb * 32 + (lane & 31);
-    const int e = eb * 32 + (lane & 31);
-    const bool rv = row < F.T, ev = e < F.E;
-    const bf16_t* xa = X + (size_t)(rv ? row : 0) * F.d + k0 + koff;
-    const bf16_t* wb = Wr + (size_t)(ev ? e : 0) * F.d + k0 + koff;
-    f32x16_t acc;
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  // wave w: rows 32 (w & 1) .. +31 of the block against expert blocks
+  // REB (w >> 1) + 2 REB q .. +REB-1 (q = 0, 1, ..): the X fragment of a
+  // 64-deep step is loaded once for REB expert blocks, and each pass over
+  // the slice keeps REB accumulators (one pass for E <= 256).  Every
+  // (row, expert) still sums its k in the same order.
+  constexpr int REB = 4;
+  const int rb = wave & 1;
+  const int row = b * kTokBlock + rb * 32 + (lane & 31);
+  const bool rv = row < F.T;
+  const bf16_t* xa = X + (size_t)(rv ? row : 0) * F.d + k0 + koff;
+  for (int eb0 = (wave >> 1) * REB; eb0 < nEB; eb0 += 2 * REB) {
+    const bf16_t* wb[REB];
+    bool ev[REB];
+    f32x16_t acc[REB];
+#pragma unroll
+    for (int q = 0; q < REB; ++q) {
+      const int e = (eb0 + q) * 32 + (lane & 31);
+      ev[q] = e < F.E;
+      wb[q] = Wr + (size_t)(ev[q] ? e : 0) * F.d + k0 + koff;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+    }
     for (int kk = 0; kk < dk; kk += 64) {
-      bf16x8_t av[4], bv[4];
+      bf16x8_t av[4], bv[REB][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        uint4 ta = rv ? *(const uint4*)(xa + kk + 16 * u) : make_uint4(0, 0, 0, 0);
-        uint4 tb = ev ? *(const uint4*)(wb + kk + 16 * u) : make_uint4(0, 0, 0, 0);
-        av[u] = *(bf16x8_t*)&ta;
-        bv[u] = *(bf16x8_t*)&tb;
+        const uint4 ta = rv ? *(const uint4*)(xa + kk + 16 * u) : make_uint4(0, 0, 0, 0);
+        av[u] = *(const bf16x8_t*)&ta;
+#pragma unroll
+        for (int q = 0; q < REB; ++q) {
+          const uint4 tb = ev[q] ? *(const uint4*)(wb[q] + kk + 16 * u) : make_uint4(0, 0, 0, 0);
+          bv[q][u] = *(const bf16x8_t*)&tb;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = mfma32x32x16(av[u], bv[u], acc);
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < REB; ++q) acc[q] = mfma32x32x16(av[u], bv[q][u], acc[q]);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int orow = b * kTokBlock + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (orow < F.T && ev) F.lpart[(size_t)s * F.lstride + (size_t)orow * F.E + e] = acc[r];
+    for (int q = 0; q < REB; ++q) {
+      const int e = (eb0 + q) * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int orow = b * kTokBlock + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (orow < F.T && ev[q]) F.lpart[(size_t)s * F.lstride + (size_t)orow * F.E + e] = acc[q][r];
+      }
     }
   }
 }
