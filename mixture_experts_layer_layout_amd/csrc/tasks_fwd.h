@@ -169,11 +169,11 @@ __device__ __forceinline__ int clamp_row(int r, int R) { return (unsigned)r < (u
 
 // ---------------------------------------------------------------- router
 // logits slice s of token block b: lpart[s][t][e] = sum over k in slice s.
-template <class Act>
-__device__ void router_partial(const Fwd& F, int task);
-
-template <>
-__device__ void router_partial<bf16_t>(const Fwd& F, int task) {
+// PF: the loads of the next 64-deep step are issued before this step's
+// MFMAs (80 more VGPRs; the kernels whose other tasks leave only 256 a lane
+// take the plain loop).
+template <bool PF>
+__device__ void router_partial_bf16(const Fwd& F, int task) {
   const int b = task / F.S, s = task % F.S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int dk = F.d / F.S, k0 = s * dk;
@@ -203,22 +203,40 @@ __device__ void router_partial<bf16_t>(const Fwd& F, int task) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
     }
-    for (int kk = 0; kk < dk; kk += 64) {
-      bf16x8_t av[4], bv[REB][4];
+    bf16x8_t av[2][4], bv[2][REB][4];
+    auto load = [&](int buf, int kk) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint4 ta = rv ? *(const uint4*)(xa + kk + 16 * u) : make_uint4(0, 0, 0, 0);
-        av[u] = *(const bf16x8_t*)&ta;
+        av[buf][u] = *(const bf16x8_t*)&ta;
 #pragma unroll
         for (int q = 0; q < REB; ++q) {
           const uint4 tb = ev[q] ? *(const uint4*)(wb[q] + kk + 16 * u) : make_uint4(0, 0, 0, 0);
-          bv[q][u] = *(const bf16x8_t*)&tb;
+          bv[buf][q][u] = *(const bf16x8_t*)&tb;
         }
       }
+    };
+    auto mma = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int q = 0; q < REB; ++q) acc[q] = mfma32x32x16(av[u], bv[q][u], acc[q]);
+        for (int q = 0; q < REB; ++q) acc[q] = mfma32x32x16(av[buf][u], bv[buf][q][u], acc[q]);
+    };
+    if constexpr (PF) {
+      load(0, 0);
+      int kk = 0;
+      for (; kk + 128 <= dk; kk += 128) {
+        load(1, kk + 64);
+        mma(0);
+        if (kk + 128 < dk) load(0, kk + 128);
+        mma(1);
+      }
+      if (kk < dk) mma(0);
+    } else {
+      for (int kk = 0; kk < dk; kk += 64) {
+        load(0, kk);
+        mma(0);
+      }
     }
 #pragma unroll
     for (int q = 0; q < REB; ++q) {
@@ -232,8 +250,7 @@ __device__ void router_partial<bf16_t>(const Fwd& F, int task) {
   }
 }
 
-template <>
-__device__ void router_partial<float>(const Fwd& F, int task) {
+__device__ void router_partial_f32(const Fwd& F, int task) {
   const int b = task / F.S, s = task % F.S;
   const int dk = F.d / F.S, k0 = s * dk;
   const float* X = (const float*)F.x;
@@ -245,6 +262,14 @@ __device__ void router_partial<float>(const Fwd& F, int task) {
     for (int kk = 0; kk < dk; ++kk) acc = fmaf(X[(size_t)row * F.d + k0 + kk], Wr[(size_t)e * F.d + k0 + kk], acc);
     F.lpart[(size_t)s * F.lstride + (size_t)row * F.E + e] = acc;
   }
+}
+
+template <class Act, bool PF = true>
+__device__ __forceinline__ void router_partial(const Fwd& F, int task) {
+  if constexpr (std::is_same<Act, float>::value)
+    router_partial_f32(F, task);
+  else
+    router_partial_bf16<PF>(F, task);
 }
 
 // Top-k of one token, one wave.  key (LDS) holds the E values ranked: the
