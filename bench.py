@@ -199,7 +199,7 @@ def main():
                     help="skip timing the same step through the separate kernels")
     ap.add_argument("--stage-rows", type=int, default=0)
     ap.add_argument("--flags", type=lambda v: int(v, 0), default=0, help="moe_desc.flags (MOE_FLAG_*)")
-    ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: occupancy limit)")
+    ap.add_argument("--workgroups", type=int, default=0, help="persistent grid size (0: automatic)")
     ap.add_argument("--producer-cus", type=int, default=0,
                     help="CU partition of the fused forward: CUs whose workgroups run only routing, "
                          "layout, gather and combine (0: none)")
