@@ -494,6 +494,8 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   __syncthreads();
   for (int e = threadIdx.x; e < F.E; e += kThreads) {
     int tot = 0;
+    // eight blocks' masks in flight at a time (the loop is latency-bound)
+#pragma unroll 8
     for (int b = 0; b < F.nb; ++b) tot += __popcll(F.bmask[(size_t)b * F.E + e]);
     scnt[e] = tot;
     stile[e] = cdiv(tot, F.BM);
@@ -519,6 +521,7 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
     F.offsets[e] = off;
     F.etile[e] = stile[e];
     int run = off;
+#pragma unroll 8
     for (int b = 0; b < F.nb; ++b) {
       F.bbase[(size_t)b * F.E + e] = run;
       run += __popcll(F.bmask[(size_t)b * F.E + e]);
