@@ -364,8 +364,8 @@ MOE_API int moe_combine(const moe_desc* desc, const void* yp, const float* gate,
  *         for experts without rows);
  *   dgate float [T, k] output, dL/dgate.
  * With desc->fused = 1 the phases (setup, rowprep and pulls, dH, dW2, dXp,
- * dW1/dW3, dX) run as: setup and pulls in one plain launch, dH and dXp in
- * one persistent launch, dW2 and dW1/dW3 in one each, dX a plain launch
+ * dW1/dW3, dX) run as: setup and pulls in one plain launch, dH, dXp, dW2
+ * and dW1/dW3 in a persistent launch each, dX a plain launch
  * (MOE_FLAG_PERSISTENT_SINGLE: one persistent launch for every phase;
  * MOE_FLAG_PERSISTENT_WGRAD_APART: the data gradients in one, the weight
  * gradients in another);

@@ -1025,20 +1025,23 @@ static int backward_impl(const Plan& p, const moe_desc* D, const void* dy, const
     const size_t smem = sm_dw > sm_dh ? sm_dw : sm_dh;
     static_assert(2 * (TileDW::smem_bytes + kWgradStageBytes + 1024) <= 160 * 1024,
                   "two weight-gradient workgroups per CU, with their static LDS");
-    // By default dH and dXp share a persistent launch (dXp tiles wait on
-    // the dH tiles of their rows, [dA | dB] stored coherently), and the
-    // weight gradients get one each: no other phase reads what another
-    // phase of its launch writes, and each launch's registers are those of
-    // its own task kinds.  Every backward task in one launch does not fit
-    // two workgroups' registers per CU (MOE_FLAG_PERSISTENT_SINGLE
-    // runs it anyway).
+    // By default each GEMM phase gets a persistent launch of its own: no
+    // phase reads what another phase of its launch writes, each launch's
+    // registers are those of its own task kinds, and [dA | dB] needs no
+    // coherent stores.  dH and dXp in one launch (dXp tiles waiting on the
+    // dH tiles of their rows) measured 7.05 against 6.99 ms as two at the
+    // DeepSeek-V3 Zipf shape: the pair spills more registers than either
+    // alone.  Every backward task in one launch does not fit two
+    // workgroups' registers per CU (MOE_FLAG_PERSISTENT_SINGLE runs it
+    // anyway).
     if (!(D->flags & (MOE_FLAG_PERSISTENT_SINGLE | MOE_FLAG_PERSISTENT_WGRAD_APART))) {
       // each persistent launch reserves the LDS its own tiles use; setup
       // with the row preparation before them, and the dX gather-sum after
       // them (ordered by the launch boundary, as the forward's combine), run
       // as plain launches
       hipLaunchKernelGGL(k_bwd_prep, dim3(1 + p.nRP), dim3(256), 0, st, B);
-      int rc = launch_fused_bwd<0x14u>(D, B, sm_dh, st);
+      int rc = launch_fused_bwd<0x04u>(D, B, sm_dh, st);
+      if (rc == MOE_OK) rc = launch_fused_bwd<0x10u>(D, B, sm_dh, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x08u>(D, B, sm_dw, st);
       if (rc == MOE_OK) rc = launch_fused_bwd<0x20u>(D, B, sm_dw, st);
       if (rc != MOE_OK) return rc;
