@@ -61,6 +61,24 @@ __device__ __forceinline__ int lds_idx(int row, int chunk) {
   return (row << 6) + ((chunk ^ lds_key<HI>(row)) << 3);
 }
 
+// The same for a stage of KS k values a row: 64 (the layout above) or 32
+// (64-byte rows, four chunks; the key (row >> 2) & 3 puts the 16-byte
+// reads of 8 consecutive rows in 8 distinct groups of four banks: rows
+// 4 apart sit 256 bytes apart, and the key moves rows 4..7 of a group of
+// 8 to the other chunk of a pair).
+template <int KS, bool HI>
+__device__ __forceinline__ int stage_key(int row) {
+  static_assert(KS == 64 || (KS == 32 && !HI), "64-k stages (either key) or 32-k stages (plain key)");
+  if constexpr (KS == 64)
+    return lds_key<HI>(row);
+  else
+    return (row >> 2) & 3;
+}
+template <int KS, bool HI>
+__device__ __forceinline__ int stage_idx(int row, int chunk) {
+  return row * KS + ((chunk ^ stage_key<KS, HI>(row)) << 3);
+}
+
 // Stages whose global loads are in flight while one stage feeds the MFMAs
 // (register buffers per loader).  Measured: 2 gave no gain over 1 on the
 // expert GEMMs, and its 32 extra VGPRs keep the persistent kernels from
@@ -82,6 +100,7 @@ struct Tile {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int MI = WM / 32, NJ = WN / 32;
+  static constexpr int KS = 64;  // k values per stage
   static constexpr int LDS_A = BM * 64, LDS_B = BN * 64;
   static constexpr size_t smem_bytes = 2 * (LDS_A + LDS_B) * sizeof(bf16_t);
   static __device__ __forceinline__ void stage(const bf16_t* As, const bf16_t* Bs, f32x16_t (&acc)[MI][NJ]);
@@ -259,20 +278,21 @@ __device__ __forceinline__ void tile_compute(const bf16_t* As, const bf16_t* Bs,
                                              f32x16_t (&acc)[TL::MI][TL::NJ]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  constexpr int NKS = TL::KS / 16;  // MFMA k-slices per stage
   bf16x8_t a[2][TL::MI], b[2][TL::NJ];
   auto frags = [&](int ks, bf16x8_t(&fa)[TL::MI], bf16x8_t(&fb)[TL::NJ]) {
     const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
-      fa[i] = *(const bf16x8_t*)(As + lds_idx<TL::kKeyHi>(wm * TL::WM + 32 * i + (lane & 31), ch));
+      fa[i] = *(const bf16x8_t*)(As + stage_idx<TL::KS, TL::kKeyHi>(wm * TL::WM + 32 * i + (lane & 31), ch));
 #pragma unroll
     for (int j = 0; j < TL::NJ; ++j)
-      fb[j] = *(const bf16x8_t*)(Bs + lds_idx<TL::kKeyHi>(wn * TL::WN + 32 * j + (lane & 31), ch));
+      fb[j] = *(const bf16x8_t*)(Bs + stage_idx<TL::KS, TL::kKeyHi>(wn * TL::WN + 32 * j + (lane & 31), ch));
   };
   frags(0, a[0], b[0]);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks < 3) frags(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks < NKS - 1) frags(ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
@@ -283,8 +303,8 @@ __device__ __forceinline__ void tile_compute(const bf16_t* As, const bf16_t* Bs,
   constexpr int NR = TL::MI + TL::NJ, NM = TL::MI * TL::NJ;
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks < NKS - 1) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
 }

@@ -75,10 +75,11 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
     p->nN2 = d / 64;
   } else {
     p->BM = D->stage_rows ? D->stage_rows : 128;
-    // column tiles: the bf16 forward with 128-row tiles uses the 256-wide
-    // direct-to-LDS tile, the others 128-wide tiles
+    // column tiles: the bf16 forward uses the 256-wide direct-to-LDS
+    // tiles, MXFP8 128-wide tiles
     if (p->mxfp8 && p->BM != 128) return MOE_ERR_UNSUPPORTED;  // MXFP8 tiles have 128 rows
-    const int bn = (!p->mxfp8 && p->BM <= 128) ? TileD256::BN : TileB128::BN;
+    static_assert(TileD256::BN == TileD256w::BN && TileD256h::BN == TileD256::BN, "one column width");
+    const int bn = !p->mxfp8 ? TileD256::BN : TileB128::BN;
     p->nN1 = I / (bn / 2);
     p->nN2 = d / bn;
   }
@@ -291,11 +292,19 @@ __global__ void __launch_bounds__(256) k_gather(Fwd F) {
   gather_tile<Act, COPY, false>(F, tile, ssrc);
 }
 
-// The default bf16 tile takes its 64-row variant for row tiles of at most
-// 64 rows.
+// The bf16 tiles take their narrower variants for short row tiles: at most
+// 64 rows the 64-row tile, at most 128 rows (of a 256-row stage) the
+// 128-row one.
 template <class TL>
 constexpr bool has_half_tile() {
-  return std::is_same<TL, TileD256>::value;
+  return std::is_same<TL, TileD256>::value || std::is_same<TL, TileD256w>::value;
+}
+template <class TL>
+constexpr size_t fwd_tile_lds() {
+  if constexpr (std::is_same<TL, TileD256w>::value)
+    return TileD256w::smem_bytes > TileD256::smem_bytes ? TileD256w::smem_bytes : TileD256::smem_bytes;
+  else
+    return TL::smem_bytes;
 }
 
 // CO: the tile's output has a reader in the same launch (stored coherently).
@@ -305,11 +314,15 @@ __device__ __forceinline__ void run_g1(const Fwd& F, int tile, int nt, char* sme
     g1_tile_f32<CO>(F, tile, nt, (float*)smem);
   else if constexpr (TL::kMX)
     g1_tile_mx<TL, CO>(F, tile, nt, (bf16_t*)smem);
-  else if constexpr (has_half_tile<TL>())
-    if (fwd_tile(F, tile).n <= TileD256h::BM)
+  else if constexpr (has_half_tile<TL>()) {
+    const int n = fwd_tile(F, tile).n;
+    if (n <= TileD256h::BM)
       g1_tile_bf16<TileD256h, CO>(F, tile, nt, (bf16_t*)smem);
+    else if (TL::BM > TileD256::BM && n <= TileD256::BM)
+      g1_tile_bf16<TileD256, CO>(F, tile, nt, (bf16_t*)smem);
     else
       g1_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
+  }
   else
     g1_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
 }
@@ -319,11 +332,15 @@ __device__ __forceinline__ void run_g2(const Fwd& F, int tile, int nt, char* sme
     g2_tile_f32<CO>(F, tile, nt, (float*)smem);
   else if constexpr (TL::kMX)
     g2_tile_mx<TL, CO>(F, tile, nt, (bf16_t*)smem);
-  else if constexpr (has_half_tile<TL>())
-    if (fwd_tile(F, tile).n <= TileD256h::BM)
+  else if constexpr (has_half_tile<TL>()) {
+    const int n = fwd_tile(F, tile).n;
+    if (n <= TileD256h::BM)
       g2_tile_bf16<TileD256h, CO>(F, tile, nt, (bf16_t*)smem);
+    else if (TL::BM > TileD256::BM && n <= TileD256::BM)
+      g2_tile_bf16<TileD256, CO>(F, tile, nt, (bf16_t*)smem);
     else
       g2_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
+  }
   else
     g2_tile_bf16<TL, CO>(F, tile, nt, (bf16_t*)smem);
 }
@@ -850,10 +867,10 @@ static int forward_impl(const Plan& p, const moe_desc* D, const Fwd& F, hipStrea
   constexpr bool isf = std::is_same<Act, float>::value;
   // the persistent kernel's LDS serves every task: GEMM stages, routing
   // masks (kMaxE u64), the layout scan (2 kMaxE + 16 ints), gather rows
-  size_t smem = isf ? TileF32::smem_bytes : TL::smem_bytes;
+  size_t smem = isf ? TileF32::smem_bytes : fwd_tile_lds<TL>();
   const size_t other[3] = {kTopkSmem, (2 * kMaxE + 16) * 4, 256 * 4};
   for (size_t o : other) smem = smem > o ? smem : o;
-  const size_t gsmem = isf ? TileF32::smem_bytes : TL::smem_bytes;
+  const size_t gsmem = isf ? TileF32::smem_bytes : fwd_tile_lds<TL>();
   hipLaunchKernelGGL(k_zero, dim3(cdiv((int)p.n_ctr, 256)), dim3(256), 0, st, F.s.queue, (int)p.n_ctr);
   if (p.T == 0) {
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, F);
@@ -1233,7 +1250,7 @@ static Fwd forward_args(const Plan& p, const moe_desc* desc, const void* x, cons
 static int forward_run(const Plan& p, const moe_desc* desc, const Fwd& F, hipStream_t st, bool ring = false) {
   if (p.mxfp8) return forward_impl<bf16_t, TileMX128>(p, desc, F, st, ring);
   if (p.f32) return forward_impl<float, TileB128>(p, desc, F, st, ring);
-  if (p.BM == 256) return forward_impl<bf16_t, TileB256>(p, desc, F, st, ring);
+  if (p.BM == 256) return forward_impl<bf16_t, TileD256w>(p, desc, F, st, ring);
   if (p.BM == 64) return forward_impl<bf16_t, TileD256h>(p, desc, F, st, ring);
   return forward_impl<bf16_t, TileD256>(p, desc, F, st, ring);
 }

@@ -43,6 +43,10 @@ typedef TileD<128, 256> TileD256;  // direct-to-LDS ring, 144 KB: one workgroup 
 // expert) run on a 64-row tile of the same width: the same weight columns
 // stream through the ring, with half the matrix-core work on padding.
 typedef TileD<64, 256> TileD256h;
+// 256-row stages: a 256 x 256 tile on a ring of four 32-k slots (half the
+// operand bytes per MFMA of the 128-row tile, for experts with many rows);
+// row tiles of at most 128 or 64 rows take the tiles above.
+typedef TileD<256, 256, 32, 4> TileD256w;
 
 struct Sync {
   int* queue;    // start of the counter region
@@ -622,8 +626,8 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const bf16_t* W1 = (const bf16_t*)F.w1 + (size_t)e * I * d;
   const bf16_t* W3 = (const bf16_t*)F.w3 + (size_t)e * I * d;
   const int c0 = nt * (TL::BN / 2);
-  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BM>, KRows<TL::BM>> LA;
-  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BN>, KRows<TL::BN>> LB;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BM, TL::KS>, KRows<TL::BM>> LA;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BN, TL::KS>, KRows<TL::BN>> LB;
   LA la;
   LB lb;
   // rows past the tile's n repeat its last row (their outputs are dropped)
@@ -642,7 +646,7 @@ __device__ void g1_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   });
   f32x16_t acc[TL::MI][TL::NJ];
   if constexpr (TL::kDMA)
-    tile_mainloop_dma<TL>(d / 64, smem, acc, la, lb);
+    tile_mainloop_dma<TL>(d / TL::KS, smem, acc, la, lb);
   else
     tile_mainloop<TL>(d / 64, smem, acc, la, lb);
   // H (then the saved pre-activations) staged in LDS, stored 16 bytes a lane
@@ -678,15 +682,16 @@ __device__ void g2_tile_bf16(const Fwd& F, int tile, int nt, bf16_t* smem) {
   const bf16_t* W2 = (const bf16_t*)F.w2 + (size_t)e * d * I;
   const bf16_t* H = (const bf16_t*)F.h;
   const int c0 = nt * TL::BN;
-  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BM>, KRows<TL::BM>> LA;
-  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BN>, KRows<TL::BN>> LB;
+  static_assert(Staged<TL::BM, TL::BN>::bytes <= TL::smem_bytes, "output staging fits the tile's LDS");
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BM, TL::KS>, KRows<TL::BM>> LA;
+  typedef std::conditional_t<TL::kDMA, DmaRows<TL::BN, TL::KS>, KRows<TL::BN>> LB;
   LA la;
   LB lb;
   la.init([&](int r) -> const bf16_t* { return H + (size_t)(r0 + min(r, n - 1)) * I; });
   lb.init([&](int nr) -> const bf16_t* { return W2 + (size_t)(c0 + nr) * I; });
   f32x16_t acc[TL::MI][TL::NJ];
   if constexpr (TL::kDMA)
-    tile_mainloop_dma<TL>(I / 64, smem, acc, la, lb);
+    tile_mainloop_dma<TL>(I / TL::KS, smem, acc, la, lb);
   else
     tile_mainloop<TL>(I / 64, smem, acc, la, lb);
   bf16_t* YP = (bf16_t*)F.yp;

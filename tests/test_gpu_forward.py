@@ -71,6 +71,9 @@ SMALL = {
     "dsv3-zipf-small": synth.WORKLOADS["dsv3-fwdbwd-zipf"].shrink(T=500, d=512, E=64, I=256),
     "one-expert": synth.WORKLOADS["mixtral-bf16"].shrink(T=70, d=256, E=1, k=1, I=128),
     "k-equals-E": synth.WORKLOADS["dsv3-bf16"].shrink(T=129, d=256, E=8, k=8, I=128),
+    # about 350 rows per expert: 256-row stages run full 256-row tiles and
+    # ragged tails of either narrower tile
+    "mixtral-long": synth.WORKLOADS["mixtral-bf16"].shrink(T=1400, d=512, I=384),
 }
 
 
