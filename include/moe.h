@@ -87,8 +87,10 @@ typedef struct moe_desc {
   int32_t fused;         /* 1: persistent launches driven by device-side
                             ready counters; 0: one launch per step          */
   int32_t stage_rows;    /* rows per ready counter (the minibatch handed to
-                            the expert GEMM): 0 = auto (128), else 64, 128
-                            or 256 (MXFP8 experts: 0 or 128)               */
+                            the expert GEMM): 0 = auto (bf16 experts: 256
+                            when T k >= 256 E, else 128; MXFP8: 128), else
+                            64, 128 or 256 (MXFP8 experts: 0 or 128); any
+                            value gives the same results                   */
   int32_t n_workgroups;  /* persistent grid size; 0 = auto: as many as
                           * fit on the CUs at once, but no more than the
                           * most tasks any phase of the launch can have

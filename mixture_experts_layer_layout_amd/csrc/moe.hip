@@ -74,7 +74,11 @@ int make_plan(const moe_desc* D, Plan* p, bool fwd_only) {
     p->nN1 = I / 32;
     p->nN2 = d / 64;
   } else {
-    p->BM = D->stage_rows ? D->stage_rows : 128;
+    // auto: 256-row stages (the 256 x 256 tile) once the bf16 experts
+    // average 256 routed rows or more, else 128 (measured: 128 wins at
+    // about 128 rows an expert, 256 from 256 rows up)
+    const bool long_experts = !p->mxfp8 && (int64_t)T * k >= (int64_t)256 * E;
+    p->BM = D->stage_rows ? D->stage_rows : (long_experts ? 256 : 128);
     // column tiles: the bf16 forward uses the 256-wide direct-to-LDS
     // tiles, MXFP8 128-wide tiles
     if (p->mxfp8 && p->BM != 128) return MOE_ERR_UNSUPPORTED;  // MXFP8 tiles have 128 rows

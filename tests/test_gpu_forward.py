@@ -106,6 +106,19 @@ def test_auto_grid_matches_large_grid_bitwise(name):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_stage_rows_same_bits(fused):
+    # 64-, 128- and 256-row stages (and the automatic choice, 256 here: about
+    # 350 rows an expert) run different tiles with the same k order into
+    # each accumulator, so every output bit agrees
+    w = SMALL["mixtral-long"]
+    inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 11).items()}
+    ys = [layer.forward(w, inp, fused=fused, stage_rows=sr)[0] for sr in (0, 64, 128, 256)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0], y)
+
+
 def test_fused_equals_unfused_bitwise():
     w = SMALL["dsv3-zipf-small"]
     inp = {k: (v.cuda() if v is not None else None) for k, v in synth.make_inputs(w, 8).items()}
