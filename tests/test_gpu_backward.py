@@ -28,6 +28,9 @@ SMALL = {
     "one-expert": synth.WORKLOADS["mixtral-bf16"].shrink(T=70, d=256, E=1, k=1, I=256, backward=True),
     "k-equals-E": synth.WORKLOADS["dsv3-bf16"].shrink(T=129, d=256, E=8, k=8, I=256, backward=True),
     "sparse-experts": synth.WORKLOADS["dsv3-bf16"].shrink(T=40, d=256, E=64, k=2, I=256, backward=True),
+    # about 350 rows an expert: the forward takes 256-row stages (the
+    # automatic choice), the backward its own 128-row tiles
+    "mixtral-long": synth.WORKLOADS["mixtral-bf16"].shrink(T=1400, d=512, I=384, backward=True),
 }
 
 
