@@ -108,7 +108,11 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 // strides), and the dispatch's own acquire leaves no copy from earlier
 // launches.  (An agent-scope acquire would invalidate the XCD's whole L2 at
 // every wait, destroying the reuse of the operand rows other workgroups
-// share there.)
+// share there.)  The one exchanged array whose lines have several
+// producers is inv (each token's k slots, written by the gather tasks of
+// the row tiles the token went to); a reader in the same launch (the merge
+// under MOE_FLAG_PERSISTENT_SINGLE) loads it with coherent agent-scope
+// loads instead.
 // The claim and wait logic itself is protocol.h, shared with a host model.
 struct DevOps {
   static __device__ __forceinline__ int load(const int* p) {

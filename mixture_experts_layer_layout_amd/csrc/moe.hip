@@ -509,7 +509,8 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
       else
         signal_add<false>(F.s.g2_done, 1);
     } else if ((MASK & 64u) && ph == 6) {
-      if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act>(merge_of(F), t);
+      // inv comes from this launch's gather tasks when it runs them
+      if (wait_geq(F.s.g2_done, s_nmt * F.nN2, W, &s_flag)) combine_tokens<Act, (MASK & 8u) != 0>(merge_of(F), t);
     }
   }
 }

@@ -28,7 +28,7 @@
 //   dxp        (row tile, d tile), K = 2I over [dA | dB]         [dh of the row tile]
 //   dw13       (expert, band of I, 8 column tiles of d): dW1 and dW3 together
 //                                                                [dh of the expert]
-//   dx         8 tokens: dX and dgate                            [every dxp]
+//   dx         kCombTok tokens: dX and dgate                     [every dxp]
 // Weight-gradient tiles are taken in order of decreasing expert load so the
 // longest tiles start first.
 #pragma once

@@ -759,8 +759,13 @@ __device__ __forceinline__ Merge merge_of(const Fwd& F) { return Merge{F.T, F.d,
 
 // y[t] = sum_j gate[t,j] * yp[inv[t*k+j]], fp32 accumulation in slot order.
 // K = k when known at compile time (every row load of a vector is issued
-// before the first one is used), 0 for any k up to kMaxK.
-template <class Act, int K>
+// before the first one is used), 0 for any k up to kMaxK.  COH: the merge
+// runs in the launch whose gather tasks wrote inv; a 128-byte line of inv
+// holds the slots of 4 tokens (k = 8), written by the gather tasks of
+// several row tiles on any XCD, so an XCD whose L2 took the line in for its
+// own partial write may hold stale bytes of the others: the indices are
+// then read with coherent agent-scope loads.
+template <class Act, int K, bool COH = false>
 __device__ void combine_tokens_k(const Merge& F, int cb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int EPV = 16 / sizeof(Act);  // elements per 16-byte vector
@@ -774,7 +779,8 @@ __device__ void combine_tokens_k(const Merge& F, int cb) {
     float g[NR];
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-      rows[j] = j < k ? clamp_row(F.inv[(size_t)t * k + j], F.R) : 0;
+      const int* ip = F.inv + (size_t)t * k + j;
+      rows[j] = j < k ? clamp_row(COH ? load_relaxed(ip) : *ip, F.R) : 0;
       g[j] = j < k ? F.gate[(size_t)t * k + j] : 0.0f;
     }
     // known k: kCombVec vectors per lane per step, every row load of a step
@@ -838,15 +844,15 @@ __device__ void combine_tokens_k(const Merge& F, int cb) {
   }
 }
 
-template <class Act>
+template <class Act, bool COH = false>
 __device__ void combine_tokens(const Merge& F, int cb) {
   switch (F.k) {
-    case 1: combine_tokens_k<Act, 1>(F, cb); break;
-    case 2: combine_tokens_k<Act, 2>(F, cb); break;
-    case 4: combine_tokens_k<Act, 4>(F, cb); break;
-    case 6: combine_tokens_k<Act, 6>(F, cb); break;
-    case 8: combine_tokens_k<Act, 8>(F, cb); break;
-    default: combine_tokens_k<Act, 0>(F, cb); break;
+    case 1: combine_tokens_k<Act, 1, COH>(F, cb); break;
+    case 2: combine_tokens_k<Act, 2, COH>(F, cb); break;
+    case 4: combine_tokens_k<Act, 4, COH>(F, cb); break;
+    case 6: combine_tokens_k<Act, 6, COH>(F, cb); break;
+    case 8: combine_tokens_k<Act, 8, COH>(F, cb); break;
+    default: combine_tokens_k<Act, 0, COH>(F, cb); break;
   }
 }
 
