@@ -469,7 +469,10 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         signal_add<(MASK & 0x18u) != 0>(F.s.q_done, 1);  // read by gather, g1
       } else {
         router_partial<Act, !TL::kMX>(F, t);
-        signal_add<(MASK & 2u) != 0>(&F.s.r1_cnt[t / F.S], 1);
+        if constexpr ((MASK & 2u) != 0)
+          signal_add_stored(&F.s.r1_cnt[t / F.S], 1);
+        else
+          signal_add<false>(&F.s.r1_cnt[t / F.S], 1);
       }
     } else if ((MASK & 2u) && ph == 1) {
       if (!wait_geq(&F.s.r1_cnt[t / kTopkChunks], F.S, W, &s_flag)) continue;

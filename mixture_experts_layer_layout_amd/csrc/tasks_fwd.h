@@ -248,7 +248,11 @@ __device__ void router_partial_bf16(const Fwd& F, int task) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int orow = b * kTokBlock + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (orow < F.T && ev[q]) F.lpart[(size_t)s * F.lstride + (size_t)orow * F.E + e] = acc[q][r];
+        // stored through the L2 (agent scope): the top-k tasks of this
+        // launch read the slice on any XCD once signal_add_stored counts it
+        if (orow < F.T && ev[q])
+          __hip_atomic_store(F.lpart + (size_t)s * F.lstride + (size_t)orow * F.E + e, acc[q][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -264,7 +268,8 @@ __device__ void router_partial_f32(const Fwd& F, int task) {
     if (row >= F.T) continue;
     float acc = 0.0f;
     for (int kk = 0; kk < dk; ++kk) acc = fmaf(X[(size_t)row * F.d + k0 + kk], Wr[(size_t)e * F.d + k0 + kk], acc);
-    F.lpart[(size_t)s * F.lstride + (size_t)row * F.E + e] = acc;
+    __hip_atomic_store(F.lpart + (size_t)s * F.lstride + (size_t)row * F.E + e, acc, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
