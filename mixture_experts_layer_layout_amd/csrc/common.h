@@ -112,8 +112,9 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
 // producers is inv (each token's k slots, written by the gather tasks of
 // the row tiles the token went to); a reader in the same launch (the merge
 // under MOE_FLAG_PERSISTENT_SINGLE) loads it with coherent agent-scope
-// loads instead.  The router's logit slices are stored coherently and
-// published by signal_add_stored: published by the write-back, the top-k
+// loads instead.  The router's logit slices (and the top-k's indices,
+// gates and mask bytes) are stored coherently and published by
+// signal_add_stored: published by the write-back, the top-k
 // on another XCD now and then read 256 bytes of a slice before the
 // router's values reached it (with a workspace pre-filled with a byte
 // pattern, some builds showed the pattern's logits for 2 or 4 tokens in up

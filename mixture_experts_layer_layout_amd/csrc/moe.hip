@@ -477,7 +477,11 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
     } else if ((MASK & 2u) && ph == 1) {
       if (!wait_geq(&F.s.r1_cnt[t / kTopkChunks], F.S, W, &s_flag)) continue;
       router_topk<true>(F, t, smem);
-      signal_add<(MASK & 0x4Cu) != 0>(F.s.r2_done, 1);  // read by scan, gather, combine
+      // read by scan, gather, combine (stored coherently)
+      if constexpr ((MASK & 0x4Cu) != 0)
+        signal_add_stored(F.s.r2_done, 1);
+      else
+        signal_add<false>(F.s.r2_done, 1);
     } else if ((MASK & 4u) && ph == 2) {
       if (!wait_geq(F.s.r2_done, F.nb * kTopkChunks, W, &s_flag)) continue;
       layout_scan(F, (int*)smem);

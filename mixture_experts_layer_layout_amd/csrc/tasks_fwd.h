@@ -416,8 +416,11 @@ __device__ void router_topk(const Fwd& F, int task, char* smem) {
       wave_topk_gates(row, keyed ? skey : row, E, F.k, F.score, F.renorm, F.n_group, F.topk_group, F.scale,
                       se, sg);
       if (lane < F.k) {
-        F.topk[(size_t)t * F.k + lane] = se;
-        F.gate[(size_t)t * F.k + lane] = sg;
+        // indices, gates and mask bytes are stored through the L2 (agent
+        // scope), as the router's slices: the layout and gather tasks of
+        // this launch read them on any XCD once signal_add_stored counts them
+        __hip_atomic_store(F.topk + (size_t)t * F.k + lane, se, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(F.gate + (size_t)t * F.k + lane, sg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (MASKS) ssel[tt * kMaxK + lane] = se;
       }
     }
@@ -430,7 +433,8 @@ __device__ void router_topk(const Fwd& F, int task, char* smem) {
       for (int tt = 0; tt < nt; ++tt)
         for (int j = 0; j < F.k; ++j)
           if (ssel[tt * kMaxK + j] == e) byte |= 1u << tt;
-      ((uint8_t*)(F.bmask + (size_t)b * E + e))[c] = (uint8_t)byte;
+      __hip_atomic_store((uint8_t*)(F.bmask + (size_t)b * E + e) + c, (uint8_t)byte, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
