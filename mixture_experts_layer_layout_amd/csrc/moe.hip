@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(256) k_build_masks(Fwd F) {
 
 __global__ void __launch_bounds__(256) k_scan(Fwd F) {
   __shared__ int sh[2 * kMaxE + 16];
-  layout_scan(F, sh);
+  layout_scan<false>(F, sh);
 }
 
 template <class Act, bool COPY>
@@ -484,8 +484,11 @@ __global__ void __launch_bounds__(256, tile_occupancy<TL>()) k_fused_fwd(Fwd F) 
         signal_add<false>(F.s.r2_done, 1);
     } else if ((MASK & 4u) && ph == 2) {
       if (!wait_geq(F.s.r2_done, F.nb * kTopkChunks, W, &s_flag)) continue;
-      layout_scan(F, (int*)smem);
-      signal_add<(MASK & 0x78u) != 0>(F.s.scan_done, 1);
+      layout_scan<(MASK & 0x78u) != 0>(F, (int*)smem);
+      if constexpr ((MASK & 0x78u) != 0)
+        signal_add_stored(F.s.scan_done, 1);  // the layout is stored coherently
+      else
+        signal_add<false>(F.s.scan_done, 1);
     } else if ((MASK & 8u) && ph == 3) {
       // MXFP8: a row tile is ready once the codes of x are complete too
       if (TL::kMX && !wait_geq(F.s.q_done, F.nb, W, &s_flag)) continue;

@@ -495,11 +495,24 @@ __device__ int block_exclusive_scan(int* v, int n, int* tmp /* >= 8 ints */) {
   return total;
 }
 
+// An int of the layout: with COH (a persistent launch whose other tasks
+// read the layout on any XCD once signal_add_stored counts it) stored
+// through the L2 at agent scope, else an ordinary store (the standalone
+// layout kernel: the launch boundary publishes it).
+template <bool COH>
+__device__ __forceinline__ void st_layout(int* p, int v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // One workgroup: counts, offsets, bases, tile list.  The masks of a valid
 // routing hold exactly R = T k bits and give at most max_tiles row tiles;
 // anything else (a repeated or out-of-range expert given to moe_layout)
 // records MOE_ERR_INVALID_ROUTE and publishes no row tile, so no later task
 // addresses a row past R.
+template <bool COH>
 __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   int* scnt = sh;
   int* stile = sh + kMaxE;
@@ -512,7 +525,7 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
     for (int b = 0; b < F.nb; ++b) tot += __popcll(F.bmask[(size_t)b * F.E + e]);
     scnt[e] = tot;
     stile[e] = cdiv(tot, F.BM);
-    F.counts[e] = tot;
+    st_layout<COH>(F.counts + e, tot);
   }
   __syncthreads();
   const int R = block_exclusive_scan(scnt, F.E, tmp);
@@ -521,35 +534,35 @@ __device__ void layout_scan(const Fwd& F, int* sh /* >= 2*kMaxE + 16 ints */) {
   if (!valid) {
     if (threadIdx.x == 0) {
       set_status(F.s.status, MOE_ERR_INVALID_ROUTE);
-      *F.s.n_mtiles = 0;
+      st_layout<COH>(F.s.n_mtiles, 0);
     }
     for (int e = threadIdx.x; e <= F.E; e += kThreads) {
-      F.etile[e] = 0;
-      F.offsets[e] = 0;
+      st_layout<COH>(F.etile + e, 0);
+      st_layout<COH>(F.offsets + e, 0);
     }
     return;
   }
   for (int e = threadIdx.x; e < F.E; e += kThreads) {
     const int off = scnt[e];
-    F.offsets[e] = off;
-    F.etile[e] = stile[e];
+    st_layout<COH>(F.offsets + e, off);
+    st_layout<COH>(F.etile + e, stile[e]);
     int run = off;
 #pragma unroll 8
     for (int b = 0; b < F.nb; ++b) {
-      F.bbase[(size_t)b * F.E + e] = run;
+      st_layout<COH>(F.bbase + (size_t)b * F.E + e, run);
       run += __popcll(F.bmask[(size_t)b * F.E + e]);
     }
     const int cnt = run - off;
     for (int mt = 0, id = stile[e]; mt * F.BM < cnt; ++mt, ++id) {
-      F.tile_e[id] = e;
-      F.tile_r0[id] = off + mt * F.BM;
-      F.tile_n[id] = min(F.BM, cnt - mt * F.BM);
+      st_layout<COH>(F.tile_e + id, e);
+      st_layout<COH>(F.tile_r0 + id, off + mt * F.BM);
+      st_layout<COH>(F.tile_n + id, min(F.BM, cnt - mt * F.BM));
     }
   }
   if (threadIdx.x == 0) {
-    F.offsets[F.E] = R;
-    F.etile[F.E] = ntiles;
-    *F.s.n_mtiles = ntiles;
+    st_layout<COH>(F.offsets + F.E, R);
+    st_layout<COH>(F.etile + F.E, ntiles);
+    st_layout<COH>(F.s.n_mtiles, ntiles);
   }
 }
 
