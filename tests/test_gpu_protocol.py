@@ -92,3 +92,35 @@ def test_reused_workspace_over_changing_routings(name, flags):
         assert s1["status"].item() == 0 and s2["status"].item() == 0
         assert torch.equal(y1, y2), seed
         _same(s1, s2, ("topk_idx", "perm", "inv"))
+
+
+@pytest.mark.parametrize("name", sorted(W))
+@pytest.mark.parametrize("flags", [0, api.MOE_FLAG_PERSISTENT_SINGLE])
+def test_prefilled_workspace_gives_the_separate_kernels_bits(name, flags):
+    # Every byte the call reads it has written first: a workspace and saved
+    # buffers pre-filled with byte patterns must give the bits of the
+    # separate kernels, at the automatic grid, at 75 workgroups and at 512.
+    # (With the router's slices published by the L2 write-back, a top-k on
+    # another XCD now and then read them before the router's values: the
+    # pattern's logits for 2 or 4 tokens.)
+    w = W[name]
+    T = w.T
+    for seed in (11, 12):
+        inp = _dev(w, seed)
+        ref, _ = layer.forward(w, inp, fused=False)
+        d = layer.desc_for(w, flags=flags, T=T)
+        weights, keep = layer.weights_of(w, inp)
+        for nwg in (0, 75, 512):
+            d.n_workgroups = nwg
+            for fill in (0x7F, 0x41, 0x00):
+                ws = layer.workspace(d)
+                ws.fill_(fill)
+                sv = layer.alloc_saved(w, "cuda", T=T)
+                for k, v in sv.items():
+                    if v is not None and k != "status":
+                        v.view(torch.uint8).fill_(fill)
+                y = torch.empty_like(ref)
+                api.moe_forward(d, inp["x"], inp["wr"], inp.get("bias"), weights, y, api.make_saved(**sv), ws)
+                torch.cuda.synchronize()
+                assert sv["status"].item() == 0
+                assert torch.equal(y, ref), (seed, nwg, hex(fill))
